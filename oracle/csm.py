@@ -96,11 +96,14 @@ def select_top(score, m):
     return sel
 
 
-def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64"):
+def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64", forced=None):
     """One CSM round over one slice.
 
     K, V : [cap, d] fp64 arrays holding the stored values; N : [cap] integer degrees;
     s : current length.  Rows at and beyond s are ignored and returned unchanged.
+    forced : optional {chunk start: (best_b, selected)} replacing the match and selection
+    decisions of those chunks (used to follow another implementation's decisions where
+    they differ only at a near-tie, so that merging and compaction can still be compared).
     Returns (K', V', N', s', taps) where taps is a list with one dict per chunk
     (start, L, m, best_b, score, selected) and 'src_pos' maps every output row < s'
     to the input row it came from.
@@ -126,6 +129,9 @@ def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64"):
         best_b, score = match(S)
         m = merge_count(r, L)
         sel = select_top(score, m)
+        if forced is not None and start in forced:
+            best_b = np.asarray(forced[start][0], dtype=np.int64)
+            sel = np.asarray(forced[start][1], dtype=bool)
         tap.update(m=m, best_b=best_b, score=score, selected=sel)
         taps.append(tap)
         # Degree-weighted merge: every selected A row folds into its matched B row.

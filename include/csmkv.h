@@ -1,0 +1,172 @@
+/*
+ * csmkv.h -- C ABI of libcsmkv: Chunked Soft Matching (CSM) KV-cache clustering and
+ * log-degree decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the pages
+ *   "Chelsea: Efficient Long-Context LLM Inference via KV Cache Clustering" (xllm-io paper
+ *   review), section 三 技术架构 (核心公式, Algorithm 1, 分块软匹配算法, 定理 6.1), and
+ *   "CentroidKV: Efficient Long-Context LLM Inference via KV Cache Clustering" (gist.science),
+ *   技术摘要 / 方法论 (推理流水线, 分块软匹配 (CSM), 聚合).
+ *
+ * Conventions for every entry point
+ *   - Pointers to cache data, degrees, lengths, queries, outputs and workspace are DEVICE
+ *     pointers owned by the caller.  The library never allocates, frees or keeps them.
+ *   - `stream` is the caller's hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; nothing is read back unless the entry point says so.
+ *   - Arguments are validated on the host before anything is enqueued.  A negative return
+ *     value means nothing was enqueued and no buffer was touched.
+ *   - Cache layout: a "slice" is one (batch, layer, kv-head) sequence.  Slices are ordered
+ *     slice = group * H_kv + kv_head with group = batch_index * layers + layer.
+ *       K, V : [num_slices][cap][d] in `dtype`, token-major, d contiguous
+ *       N    : [num_slices][cap] int32, the degree (tokens a row stands for)
+ *       lens : [num_slices] int32, the current length s of each slice
+ *     K and V must be 16-byte aligned.  Rows at or beyond lens[] are ignored.
+ *   - Device-side errors (a lens[] entry above max_len or cap) are reported through an
+ *     int32 error word in device memory, read with csmkv_read_error().  The affected
+ *     slice is left unchanged (compress, append) or produces zeros (attention).
+ *   - Calls that share a workspace must not overlap in time (use one stream).
+ */
+#ifndef CSMKV_H
+#define CSMKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define CSMKV_API __attribute__((visibility("default")))
+#else
+#define CSMKV_API
+#endif
+
+typedef enum {
+  CSMKV_OK = 0,
+  CSMKV_EINVAL = -1,        /* argument out of range or required pointer NULL */
+  CSMKV_EDTYPE = -2,        /* unknown dtype code */
+  CSMKV_EUNSUPPORTED = -3,  /* shape outside what the kernels are built for */
+  CSMKV_EWORKSPACE = -4,    /* workspace NULL, misaligned or smaller than required */
+  CSMKV_EHIP = -5,          /* a HIP runtime call or kernel launch failed */
+  CSMKV_EDEVICE = -6        /* csmkv_read_error: a kernel flagged a bad lens[] entry */
+} csmkv_status;
+
+typedef enum { CSMKV_BF16 = 0, CSMKV_F32 = 1 } csmkv_dtype;
+
+typedef struct {
+  int64_t num_slices; /* number of (batch, layer, kv-head) slices, >= 0 */
+  int64_t cap;        /* rows allocated per slice, >= 1 */
+  int32_t d;          /* head dimension; the kernels are built for d = 128 */
+  int32_t dtype;      /* csmkv_dtype of K, V (and q) */
+  int32_t max_len;    /* host-known bound on every lens[] entry, 0 <= max_len <= cap;
+                         sizes the launch grids (entries above it are device errors) */
+} csmkv_cache;
+
+/* Human-readable name of a status code (static string). */
+CSMKV_API const char *csmkv_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+CSMKV_API int csmkv_version(void);
+
+/* Bytes of workspace csm_compress / csm_compress_into / csm_compress_debug need for this
+ * cache geometry and these n1, n2, c.  0 if the arguments are invalid. */
+CSMKV_API size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c);
+
+/*
+ * csm_compress -- one CSM round over every slice, in place.
+ *   Chelsea review, section 三, 分块软匹配算法 steps 1-4 and Algorithm 1
+ *   (K, V, N, s = Chelsea(K, V, N, s, n1, n2, r, c)); CentroidKV page, 分块软匹配 (CSM)
+ *   and 聚合.
+ * Per slice of length s (slices with outlier_mask[z] != 0 are not read or written):
+ *   keep rows [0, n1) and the last n2 rows; split the middle [n1, s-n2) into chunks of c
+ *   rows from n1 (the last may be shorter, length L); in each chunk A = even offsets,
+ *   B = odd offsets; every A row takes the B row of highest key cosine similarity (lowest
+ *   B index on ties); the A rows are ranked by that similarity (descending, lower A index
+ *   first on ties) and the first m = floor(r*L/2) merge into their targets:
+ *   k_b <- (N_b k_b + sum N_a k_a) / (N_b + sum N_a), same for v, N_b <- N_b + sum N_a,
+ *   accumulated in fp32 in ascending A order and stored with round-to-nearest-even;
+ *   merged A rows are removed and the slice is compacted in its original order;
+ *   lens[z] becomes s - sum(m).  Similarities are decided in fp32 (bf16 products are
+ *   exact, sums rounded in fp32).
+ * Arguments: n1, n2 >= 0; 2 <= c <= 256; 0 <= r <= 1 (not NaN); outlier_mask is a device
+ *   [num_slices] uint8 array or NULL (no outliers); workspace: device memory of at least
+ *   csm_compress_workspace_bytes() bytes, 256-byte aligned.  Its first int32 is the error
+ *   word of this call.
+ * Returns CSMKV_OK or a negative csmkv_status.
+ */
+CSMKV_API int csm_compress(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+                 int32_t n1, int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csm_compress_into -- the same round, reading one cache and writing another
+ * (out of place).  Outlier slices and the protected rows are copied unchanged.
+ * src and dst must agree on num_slices, d and dtype; dst->cap must hold every output
+ * (a slice whose output would exceed dst->cap is a device error and is not written).
+ * The source buffers are not modified.  Input and output buffers must not overlap.
+ */
+CSMKV_API int csm_compress_into(const void *K_in, const void *V_in, const int32_t *N_in,
+                      const int32_t *lens_in, const csmkv_cache *src,
+                      void *K_out, void *V_out, int32_t *N_out, int32_t *lens_out,
+                      const csmkv_cache *dst,
+                      int32_t n1, int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csm_compress_debug -- csm_compress (in place) that also records its decisions.
+ * Not for timed runs.  Any tap may be NULL.
+ *   best_b   : [num_slices][units][128] int32, per chunk the matched B index of each A
+ *              row (-1 where the row does not exist); units = csm_compress_units().
+ *   selected : same shape, uint8, 1 where the A row was merged.
+ *   src_pos  : [num_slices][cap] int32, for each output row < new lens the input row it
+ *              came from (entries at or beyond the new length are not written).
+ */
+CSMKV_API int csm_compress_debug(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+                       int32_t n1, int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
+                       void *workspace, size_t workspace_bytes, void *stream,
+                       int32_t *best_b, uint8_t *selected, int32_t *src_pos);
+
+/* Chunk units per slice the compress launch uses for this geometry (the leading dimension
+ * of the debug taps, which hold one entry block per unit).  0 if invalid. */
+CSMKV_API int64_t csm_compress_units(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c);
+
+/* Bytes of workspace decode_attn_logn needs.  0 if the arguments are invalid. */
+CSMKV_API size_t decode_attn_logn_workspace_bytes(const csmkv_cache *cache, int32_t H_q, int32_t H_kv);
+
+/*
+ * decode_attn_logn -- grouped-query decode attention over a clustered cache:
+ *   O = Softmax(q K^T / sqrt(d) + log N) V
+ *   (Chelsea review, section 三, 核心公式: attention with cluster degrees; Algorithm 1
+ *   decode output).
+ * q : [groups][H_q][d] in the cache dtype, groups = num_slices / H_kv; query head h of
+ *   group g reads slice g * H_kv + h / (H_q / H_kv).
+ * O : [groups][H_q][d] fp32 (written for every head; an empty slice gives zeros).
+ * Arithmetic in fp32 (exp/log in base 2 with the log2(e) factor folded into the scale).
+ * H_kv >= 1, H_q a multiple of H_kv with H_q / H_kv in {1, 2, 4, 8};
+ * num_slices a multiple of H_kv.  Workspace as for csm_compress (first int32 = error word).
+ */
+CSMKV_API int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t *N,
+                     const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                     float *O, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kv_append -- Algorithm 1 decode update for every slice (Chelsea review, section 三,
+ * Algorithm 1: K = [K, k], V = [V, v], N = [N, 1], s = s + 1).
+ * k_new, v_new : [num_slices][d] in the cache dtype.  A slice whose lens is negative or
+ * already equal to cap is not written and sets *error_word (device int32, may be NULL)
+ * to CSMKV_EDEVICE.  max_len is not used by this call.
+ */
+CSMKV_API int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+              const void *k_new, const void *v_new, int32_t *error_word, void *stream);
+
+/* Synchronise `stream` and return CSMKV_OK if the device error word is 0, CSMKV_EDEVICE if
+ * a kernel set it, or CSMKV_EHIP if the copy failed.  error_word is the first int32 of a
+ * workspace or the word given to kv_append. */
+CSMKV_API int csmkv_read_error(const int32_t *error_word, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSMKV_H */

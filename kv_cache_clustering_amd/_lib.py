@@ -1,0 +1,231 @@
+"""ctypes binding of libcsmkv.so: argument marshalling from torch tensors to the C ABI.
+
+Every computation runs in the library's HIP kernels; this module only checks tensor
+shapes and dtypes, builds the cache descriptor, passes device pointers and the current
+HIP stream, and allocates workspaces with torch when the caller does not pass one.
+Importing it fails loudly when the library has not been built.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsmkv.so")
+
+OK, EINVAL, EDTYPE, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
+BF16, F32 = 0, 1
+
+
+class CsmkvError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_slices", ctypes.c_int64), ("cap", ctypes.c_int64), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("max_len", ctypes.c_int32)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libcsmkv.so is not built ({LIB_PATH}); run "
+                      "`python -c 'import __graft_entry__ as g; g.build()'` first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p, _i32, _i64, _sz, _d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+_desc = ctypes.POINTER(CacheDesc)
+_SIGS = {
+    "csmkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "csmkv_version": (ctypes.c_int, []),
+    "csm_compress_workspace_bytes": (_sz, [_desc, _i32, _i32, _i32]),
+    "csm_compress_units": (_i64, [_desc, _i32, _i32, _i32]),
+    "csm_compress": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _d, _p, _p, _sz, _p]),
+    "csm_compress_into": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p, _desc, _i32, _i32,
+                                         _i32, _d, _p, _p, _sz, _p]),
+    "csm_compress_debug": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _d, _p, _p, _sz,
+                                          _p, _p, _p, _p]),
+    "decode_attn_logn_workspace_bytes": (_sz, [_desc, _i32, _i32]),
+    "decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _sz, _p]),
+    "kv_append": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p]),
+    "csmkv_read_error": (ctypes.c_int, [_p, _p]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def status_string(status):
+    return _lib.csmkv_status_string(int(status)).decode()
+
+
+def version():
+    return _lib.csmkv_version()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"cache dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def cache_desc(K, max_len=None):
+    """Descriptor of a [num_slices, cap, d] cache tensor; max_len defaults to cap."""
+    if K.dim() != 3:
+        raise ValueError("K must be [num_slices, cap, d]")
+    S, cap, d = K.shape
+    return CacheDesc(S, cap, d, _dtype_code(K), cap if max_len is None else int(max_len))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_cache(K, V, N, lens):
+    if not (K.is_cuda and V.is_cuda and N.is_cuda and lens.is_cuda):
+        raise ValueError("cache tensors must be on the GPU")
+    if K.shape != V.shape or K.dtype != V.dtype:
+        raise ValueError("K and V must have the same shape and dtype")
+    if N.shape != K.shape[:2] or N.dtype != torch.int32:
+        raise ValueError("N must be int32 [num_slices, cap]")
+    if lens.shape != K.shape[:1] or lens.dtype != torch.int32:
+        raise ValueError("lens must be int32 [num_slices]")
+    for t in (K, V, N, lens):
+        if not t.is_contiguous():
+            raise ValueError("cache tensors must be contiguous")
+
+
+def _check_mask(mask, S):
+    if mask is None:
+        return
+    if mask.dtype != torch.uint8 or mask.shape != (S,) or not mask.is_cuda or not mask.is_contiguous():
+        raise ValueError("outlier_mask must be a contiguous uint8 GPU tensor [num_slices]")
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or not ws.is_cuda or ws.numel() < nbytes:
+        raise ValueError(f"workspace must be a uint8 GPU tensor of at least {nbytes} bytes")
+    return ws
+
+
+def _raise(rc, what):
+    if rc != OK:
+        raise CsmkvError(rc, what)
+
+
+def csm_workspace_bytes(K, n1, n2, c, max_len=None):
+    return _lib.csm_compress_workspace_bytes(ctypes.byref(cache_desc(K, max_len)), n1, n2, c)
+
+
+def csm_units(K, n1, n2, c, max_len=None):
+    return _lib.csm_compress_units(ctypes.byref(cache_desc(K, max_len)), n1, n2, c)
+
+
+def csm_compress(K, V, N, lens, n1=16, n2=64, c=256, r=0.5, outlier_mask=None, max_len=None,
+                 workspace=None):
+    """One CSM round over every slice, in place.  Returns the workspace used."""
+    _check_cache(K, V, N, lens)
+    _check_mask(outlier_mask, K.shape[0])
+    desc = cache_desc(K, max_len)
+    ws = _workspace(_lib.csm_compress_workspace_bytes(ctypes.byref(desc), n1, n2, c), K.device,
+                    workspace)
+    rc = _lib.csm_compress(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), n1, n2, c,
+                           float(r), _ptr(outlier_mask), _ptr(ws), ws.numel(), _stream(K.device))
+    _raise(rc, "csm_compress")
+    return ws
+
+
+def csm_compress_into(K_in, V_in, N_in, lens_in, K_out, V_out, N_out, lens_out, n1=16, n2=64,
+                      c=256, r=0.5, outlier_mask=None, max_len=None, workspace=None):
+    """One CSM round reading the first cache and writing the second."""
+    _check_cache(K_in, V_in, N_in, lens_in)
+    _check_cache(K_out, V_out, N_out, lens_out)
+    _check_mask(outlier_mask, K_in.shape[0])
+    src = cache_desc(K_in, max_len)
+    dst = cache_desc(K_out, min(K_out.shape[1], src.max_len))
+    ws = _workspace(_lib.csm_compress_workspace_bytes(ctypes.byref(src), n1, n2, c), K_in.device,
+                    workspace)
+    rc = _lib.csm_compress_into(_ptr(K_in), _ptr(V_in), _ptr(N_in), _ptr(lens_in),
+                                ctypes.byref(src), _ptr(K_out), _ptr(V_out), _ptr(N_out),
+                                _ptr(lens_out), ctypes.byref(dst), n1, n2, c, float(r),
+                                _ptr(outlier_mask), _ptr(ws), ws.numel(), _stream(K_in.device))
+    _raise(rc, "csm_compress_into")
+    return ws
+
+
+def csm_compress_debug(K, V, N, lens, n1=16, n2=64, c=256, r=0.5, outlier_mask=None,
+                       max_len=None, workspace=None):
+    """csm_compress in place, returning the decision taps (best_b, selected, src_pos)."""
+    _check_cache(K, V, N, lens)
+    _check_mask(outlier_mask, K.shape[0])
+    desc = cache_desc(K, max_len)
+    units = _lib.csm_compress_units(ctypes.byref(desc), n1, n2, c)
+    S, cap = K.shape[0], K.shape[1]
+    best_b = torch.full((S, max(units, 1), 128), -1, dtype=torch.int32, device=K.device)
+    selected = torch.zeros((S, max(units, 1), 128), dtype=torch.uint8, device=K.device)
+    src_pos = torch.full((S, cap), -1, dtype=torch.int32, device=K.device)
+    ws = _workspace(_lib.csm_compress_workspace_bytes(ctypes.byref(desc), n1, n2, c), K.device,
+                    workspace)
+    rc = _lib.csm_compress_debug(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), n1,
+                                 n2, c, float(r), _ptr(outlier_mask), _ptr(ws), ws.numel(),
+                                 _stream(K.device), _ptr(best_b), _ptr(selected), _ptr(src_pos))
+    _raise(rc, "csm_compress_debug")
+    return best_b, selected, src_pos, ws
+
+
+def decode_workspace_bytes(K, H_q, H_kv, max_len=None):
+    return _lib.decode_attn_logn_workspace_bytes(ctypes.byref(cache_desc(K, max_len)), H_q, H_kv)
+
+
+def decode_attn_logn(q, K, V, N, lens, H_q, H_kv, out=None, max_len=None, workspace=None):
+    """O = softmax(q K^T / sqrt(d) + log N) V for every query head; O is fp32 [groups, H_q, d]."""
+    _check_cache(K, V, N, lens)
+    S, cap, d = K.shape
+    groups = S // H_kv if H_kv > 0 else 0
+    if q.shape != (groups, H_q, d) or q.dtype != K.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
+    if out is None:
+        out = torch.empty((groups, H_q, d), dtype=torch.float32, device=K.device)
+    elif out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [groups, H_q, d]")
+    desc = cache_desc(K, max_len)
+    ws = _workspace(_lib.decode_attn_logn_workspace_bytes(ctypes.byref(desc), H_q, H_kv),
+                    K.device, workspace)
+    rc = _lib.decode_attn_logn(_ptr(q), _ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc),
+                               H_q, H_kv, _ptr(out), _ptr(ws), ws.numel(), _stream(K.device))
+    _raise(rc, "decode_attn_logn")
+    return out
+
+
+def kv_append(K, V, N, lens, k_new, v_new, error_word=None):
+    """Append one token per slice: K[s]=k, V[s]=v, N[s]=1, s+=1."""
+    _check_cache(K, V, N, lens)
+    S, _, d = K.shape
+    for t in (k_new, v_new):
+        if t.shape != (S, d) or t.dtype != K.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"k_new / v_new must be contiguous {K.dtype} GPU tensors [{S}, {d}]")
+    desc = cache_desc(K)
+    rc = _lib.kv_append(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), _ptr(k_new),
+                        _ptr(v_new), _ptr(error_word), _stream(K.device))
+    _raise(rc, "kv_append")
+
+
+def read_error(word):
+    """Synchronise and read a device error word (first int32 of a workspace, or an append word)."""
+    return _lib.csmkv_read_error(_ptr(word), _stream(word.device))
+
+
+# Host-only entry points for argument-validation tests (no GPU work is enqueued on errors).
+raw = _lib

@@ -1,0 +1,514 @@
+// One round of Chunked Soft Matching (CSM) over every slice of a K/V cache.
+//
+// Method: Chelsea review, section 三, 分块软匹配算法 steps 1-4 (chunking with protected sink
+// and recent tokens, alternating A/B partition, soft matching, merge into one centre
+// per cluster with degree n_t) and Algorithm 1 (K, V, N, s rewritten by a round);
+// CentroidKV page, 分块软匹配 (CSM) (cosine similarity, each A token takes its most
+// similar B token, top fraction r of the ranked matches merged) and 聚合 (degree-weighted
+// averaging of K and V; degrees accumulate over rounds).
+//
+// Launch structure (all on the caller's stream):
+//   csm_prep   : resets the error word and the ticket counter, validates every lens[]
+//                entry, records each slice's input and output length, clears the
+//                per-chunk "source consumed" flags.
+//   csm_round  : one 256-thread workgroup per unit; units are (slice, chunk) pairs plus
+//                one "tail" unit per slice that moves the recent rows and writes lens.
+//                Workgroups take a ticket from an atomic counter and map ticket ->
+//                (slice, unit) in slice-major order, so every lower-numbered unit has
+//                already started when a unit runs.
+//
+// In-place compaction: chunk j of a slice writes rows [n1 + j*(c - m), ...), which may
+// overlap the source rows of chunks i <= j.  A chunk loads its whole source (K, V, N)
+// into LDS and registers, waits for its loads to land, and raises its flag; before
+// writing it waits for the flags of the lower chunks whose sources its destination
+// overlaps.  Those chunks hold lower tickets, are already running and raise their flag
+// without waiting on anything, so every wait ends.  Lower chunks never write into a
+// higher chunk's source.
+//
+// Per chunk (c <= 256, d = 128):
+//   keys -> LDS tile (swizzled rows), fp32 norms from the same registers;
+//   S^T = B_keys . A_keys^T on MFMA (bf16: v_mfma_f32_32x32x16_bf16, fp32:
+//   v_mfma_f32_32x32x2_f32), wave w owning A columns [32w, 32w+32) and all B rows;
+//   cosine = dot / (max(|a|,1e-12) * max(|b|,1e-12)) in fp32, arg-max per A column
+//   inside each lane then across the two half-waves (lowest B index on ties);
+//   rank of every A edge by (score desc, index asc) through a 128-way comparison count;
+//   per-target source lists in ascending A order (counting sort);
+//   keep-mask prefix sum (ballot + mbcnt) gives each kept row its output slot;
+//   merged rows = (N_b k_b + sum N_a k_a) / (N_b + sum N_a) in fp32, stored RNE.
+#include <algorithm>
+
+#include "device_common.hpp"
+#include "kernel_args.hpp"
+
+namespace csmkv {
+
+
+__global__ void csm_prep(CsmArgs a) {
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) {
+      *a.err = 0;
+      *a.ticket = 0u;
+    }
+    __syncthreads();
+    for (int64_t z = threadIdx.x; z < a.num_slices; z += blockDim.x) {
+      int s = a.lens_in[z];
+      bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap_in;
+      bool outl = a.mask != nullptr && a.mask[z] != 0;
+      int s_new = s;
+      int M = s - a.n1 - a.n2;
+      if (ok && !outl && M >= 2) {
+        int nch = (M + a.c - 1) / a.c;
+        int last = M - (nch - 1) * a.c;
+        s_new = s - (nch - 1) * a.m_full - merge_count_dev(a.r, last);
+      }
+      if (ok && (int64_t)s_new > a.cap_out) ok = false;
+      a.s_in[z] = ok ? s : -1;
+      a.s_out[z] = s_new;
+      if (!ok) atomicExch(a.err, kDeviceError);
+    }
+  } else {
+    const int64_t total = a.num_slices * (int64_t)a.units;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)(gridDim.x - 1) * blockDim.x)
+      a.flags[i] = 0;
+  }
+}
+
+template <typename T>
+struct Tile {
+  static constexpr int ROWB = kHeadDim * (int)sizeof(T);  // bytes per row
+  static constexpr int SEGS = ROWB / 16;                  // 16-byte segments per row
+  static constexpr int RPI = 256 / SEGS;                  // rows covered by one block-wide load
+  static constexpr int NLD = kMaxChunk / RPI;             // loads per thread for 256 rows
+  static constexpr int EPS = 16 / (int)sizeof(T);         // elements per segment
+};
+
+// Sum of squares of one 16-byte segment (fp32; bf16 squares are exact in fp32).
+__device__ __forceinline__ float seg_sumsq(u32x4 v, __bf16 *) {
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float lo = bf_lo(v[q]), hi = bf_hi(v[q]);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
+__device__ __forceinline__ float seg_sumsq(u32x4 v, float *) {
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x = __uint_as_float(v[q]);
+    s = fmaf(x, x, s);
+  }
+  return s;
+}
+
+// Unpack a segment to fp32 / pack fp32 back to the storage type.
+__device__ __forceinline__ void seg_unpack(u32x4 v, float *o, __bf16 *) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    o[2 * q] = bf_lo(v[q]);
+    o[2 * q + 1] = bf_hi(v[q]);
+  }
+}
+__device__ __forceinline__ void seg_unpack(u32x4 v, float *o, float *) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = __uint_as_float(v[q]);
+}
+__device__ __forceinline__ u32x4 seg_pack(const float *o, __bf16 *) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+  return v;
+}
+__device__ __forceinline__ u32x4 seg_pack(const float *o, float *) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = __float_as_uint(o[q]);
+  return v;
+}
+
+// S^T tile for one wave: acc[tile][i] = <key of B row (tile*32 + row_i), key of A row a>.
+__device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
+                                         __bf16 *) {
+  constexpr int ROWB = Tile<__bf16>::ROWB;
+#pragma unroll
+  for (int kk = 0; kk < kHeadDim / 16; ++kk) {
+    const int seg = 2 * kk + h;
+    u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
+    bf16x8 bop = __builtin_bit_cast(bf16x8, braw);
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) {
+      const int brow = 2 * (tl * 32 + col) + 1;
+      u32x4 araw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(brow, seg, ROWB));
+      bf16x8 aop = __builtin_bit_cast(bf16x8, araw);
+      acc[tl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc[tl], 0, 0, 0);
+    }
+  }
+}
+__device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
+                                         float *) {
+  constexpr int ROWB = Tile<float>::ROWB;
+  // Half-wave h supplies elements 8q + 4h + i at k-step 4q + i: every element is used
+  // once and both operands use the same assignment.
+#pragma unroll 2
+  for (int q = 0; q < kHeadDim / 8; ++q) {
+    const int seg = 2 * q + h;
+    u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) {
+      const int brow = 2 * (tl * 32 + col) + 1;
+      u32x4 araw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(brow, seg, ROWB));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(araw[i]),
+                                                       __uint_as_float(braw[i]), acc[tl], 0, 0, 0);
+    }
+  }
+}
+
+// Copy `nrows` rows (K, V, N) from src to dst in ascending blocks of 256 rows.  Each block
+// is fully read before any of it is written, so dst <= src (a shift to lower rows) is safe
+// in place.
+template <typename T>
+__device__ void copy_rows(const char *Ks, const char *Vs, const int32_t *Ns, char *Kd, char *Vd,
+                          int32_t *Nd, int nrows) {
+  using TL = Tile<T>;
+  const int t = threadIdx.x, sg = t % TL::SEGS, r0 = t / TL::SEGS;
+  for (int blk = 0; blk < nrows; blk += kMaxChunk) {
+    const int nb = min(kMaxChunk, nrows - blk);
+    u32x4 kb[TL::NLD], vb[TL::NLD];
+#pragma unroll
+    for (int i = 0; i < TL::NLD; ++i) {
+      const int r = r0 + TL::RPI * i;
+      if (r < nb) {
+        kb[i] = ld16(Ks + (int64_t)(blk + r) * TL::ROWB + sg * 16);
+        vb[i] = ld16(Vs + (int64_t)(blk + r) * TL::ROWB + sg * 16);
+      }
+    }
+    int32_t nv = t < nb ? Ns[blk + t] : 0;
+    wait_vm_loads();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TL::NLD; ++i) {
+      const int r = r0 + TL::RPI * i;
+      if (r < nb) {
+        st16(Kd + (int64_t)(blk + r) * TL::ROWB + sg * 16, kb[i]);
+        st16(Vd + (int64_t)(blk + r) * TL::ROWB + sg * 16, vb[i]);
+      }
+    }
+    if (t < nb) Nd[blk + t] = nv;
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void wait_flag(const int32_t *f) {
+  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+    __builtin_amdgcn_s_sleep(2);
+}
+
+template <typename T>
+__device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch, bool outl) {
+  using TL = Tile<T>;
+  const int t = threadIdx.x;
+  const int64_t kin = z * a.cap_in * TL::ROWB, kout = z * a.cap_out * TL::ROWB;
+  const char *Ks = a.Kin + kin, *Vs = a.Vin + kin;
+  const int32_t *Ns = a.Nin + z * a.cap_in;
+  char *Kd = a.Kout + kout, *Vd = a.Vout + kout;
+  int32_t *Nd = a.Nout + z * a.cap_out;
+  int32_t *src = a.tap_src ? a.tap_src + z * a.cap_out : nullptr;
+  if (nch == 0) {  // nothing to compress: lens unchanged, copy everything out of place
+    if (!a.in_place) copy_rows<T>(Ks, Vs, Ns, Kd, Vd, Nd, s);
+    if (src)
+      for (int i = t; i < s; i += blockDim.x) src[i] = i;
+    if (t == 0) a.lens_out[z] = s;
+    return;
+  }
+  const int n1 = a.n1, n2 = a.n2, c = a.c;
+  if (!a.in_place) copy_rows<T>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
+  if (a.in_place && !outl && t == 0) {
+    // the recent rows land in [s_new - n2, s_new): wait for chunks whose sources overlap it
+    const int d0 = s_new - n2, d1 = s_new;
+    if (d1 > d0) {
+      const int lo = (d0 - n1) / c, hi = min(nch - 1, (d1 - 1 - n1) / c);
+      for (int i = lo; i <= hi; ++i) wait_flag(a.flags + z * a.units + i);
+    }
+  }
+  __syncthreads();
+  const int64_t so = (int64_t)(s - n2), dof = (int64_t)(s_new - n2);
+  copy_rows<T>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
+               Vd + dof * TL::ROWB, Nd + dof, n2);
+  if (src) {
+    for (int i = t; i < n1; i += blockDim.x) src[i] = i;
+    for (int i = t; i < n2; i += blockDim.x) src[s_new - n2 + i] = s - n2 + i;
+  }
+  if (t == 0) a.lens_out[z] = s_new;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
+  using TL = Tile<T>;
+  constexpr int ROWB = TL::ROWB, SEGS = TL::SEGS, RPI = TL::RPI, NLD = TL::NLD, EPS = TL::EPS;
+  __shared__ __attribute__((aligned(16))) char tile[kMaxChunk * ROWB];
+  __shared__ float s_norm[kMaxChunk];
+  __shared__ int32_t s_n[kMaxChunk];
+  __shared__ int32_t s_outrow[kMaxChunk];
+  __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_pos[128],
+      s_list[128];
+  __shared__ float s_score[128];
+  __shared__ int32_t s_misc[8];
+
+  const int t = threadIdx.x;
+  if (t == 0) s_misc[0] = (int32_t)atomicAdd(a.ticket, 1u);
+  __syncthreads();
+  const uint32_t ticket = (uint32_t)s_misc[0];
+  const int64_t z = ticket / (uint32_t)a.units;
+  const int u = (int)(ticket % (uint32_t)a.units);
+  if (z >= a.num_slices) return;
+  const int s = a.s_in[z];
+  if (s < 0) return;  // invalid length: slice left untouched (error word already set)
+  const bool outl = a.mask != nullptr && a.mask[z] != 0;
+  if (outl && a.in_place) return;
+  const int n1 = a.n1, n2 = a.n2, c = a.c;
+  const int M = s - n1 - n2;
+  const int nch = M >= 2 ? (M + c - 1) / c : 0;
+  const int s_new = a.s_out[z];
+
+  if (u == a.units - 1) {
+    tail_unit<T>(a, z, s, s_new, nch, outl);
+    return;
+  }
+  if (u >= nch) return;
+
+  // ---------------------------------------------------------------- chunk unit
+  const int j = u;
+  const int start = n1 + j * c;
+  const int L = min(c, M - j * c);
+  const bool copy_only = outl;  // outlier slice, out of place: rows move unchanged
+  const int m = copy_only ? 0 : merge_count_dev(a.r, L);
+  const int nA = (L + 1) / 2, nB = L / 2;
+  const int base = copy_only ? start : n1 + j * (c - a.m_full);
+  const int nout = L - m;
+  T *tsel = nullptr;
+
+  const char *Ksrc = a.Kin + (z * a.cap_in + start) * (int64_t)ROWB;
+  const char *Vsrc = a.Vin + (z * a.cap_in + start) * (int64_t)ROWB;
+  const int sg = t % SEGS, r0 = t / SEGS;
+
+  // 1. load the chunk: K -> LDS (+ norms), V -> registers, N -> LDS
+  u32x4 vreg[NLD];
+  {
+    u32x4 kreg[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int r = r0 + RPI * i;
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (r < L) {
+        kreg[i] = ld16(Ksrc + (int64_t)r * ROWB + sg * 16);
+        vreg[i] = ld16(Vsrc + (int64_t)r * ROWB + sg * 16);
+      }
+    }
+    if (t < L) s_n[t] = a.Nin[z * a.cap_in + start + t];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int r = r0 + RPI * i;
+      *reinterpret_cast<u32x4 *>(tile + lds_swz(r, sg, ROWB)) = kreg[i];
+      float ss = row16_sum(seg_sumsq(kreg[i], tsel));
+      if (SEGS == 32) ss += __shfl_xor(ss, 16);
+      if (sg == 0) s_norm[r] = sqrtf(ss);
+    }
+  }
+  wait_vm_loads();
+  __syncthreads();
+  if (a.in_place && t == 0)
+    __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 2. similarity tile on MFMA and arg-max over B for every A column
+  if (!copy_only && nB > 0) {
+    const int w = t >> 6, l = t & 63, h = l >> 5, col = l & 31;
+    const int aidx = 32 * w + col;
+    f32x16 acc[4];
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[tl][q] = 0.f;
+    sim_tile(tile, aidx, col, h, acc, tsel);
+    const float na = fmaxf(s_norm[2 * aidx], 1e-12f);
+    float best = -__builtin_inff();
+    int bidx = 0x7fffffff;
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int bb = tl * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (bb < nB) {
+          const float den = na * fmaxf(s_norm[2 * bb + 1], 1e-12f);
+          const float sc = acc[tl][q] / den;
+          if (sc > best) {
+            best = sc;
+            bidx = bb;
+          }
+        }
+      }
+    }
+    const float ob = __shfl_xor(best, 32);
+    const int oi = __shfl_xor(bidx, 32);
+    if (ob > best || (ob == best && oi < bidx)) {
+      best = ob;
+      bidx = oi;
+    }
+    if (h == 0) {
+      s_best[aidx] = aidx < nA ? bidx : -1;
+      s_score[aidx] = aidx < nA ? best : -__builtin_inff();
+    }
+  } else if (t < 128) {
+    s_best[t] = -1;
+    s_score[t] = -__builtin_inff();
+  }
+  __syncthreads();
+
+  // 3. top-m selection: rank of each A edge by (score desc, index asc)
+  if (t < 128) {
+    int sel = 0;
+    if (t < nA && m > 0 && nB > 0) {
+      const float sc = s_score[t];
+      int rank = 0;
+#pragma unroll 8
+      for (int q = 0; q < 128; ++q) {
+        const float o = s_score[q];
+        rank += (o > sc) || (o == sc && q < t);
+      }
+      sel = rank < m;
+    }
+    s_sel[t] = sel;
+  }
+  __syncthreads();
+
+  // 4. per-target source counts and weights, per-source slot, keep-mask prefix
+  if (t < 128) {
+    const int b = t;
+    int cnt = 0, ws = b < nB ? s_n[2 * b + 1] : 0;
+    for (int q = 0; q < nA; ++q)
+      if (s_sel[q] && s_best[q] == b) {
+        ++cnt;
+        ws += s_n[2 * q];
+      }
+    s_cnt[b] = cnt;
+    s_wsum[b] = ws;
+  } else {
+    const int aa = t - 128;
+    int pos = 0;
+    if (s_sel[aa]) {
+      const int bb = s_best[aa];
+      for (int q = 0; q < aa; ++q) pos += (s_sel[q] && s_best[q] == bb);
+    }
+    s_pos[aa] = pos;
+  }
+  const int keep = (t < L) && ((t & 1) || !s_sel[t >> 1]);
+  const uint64_t bal = __ballot(keep);
+  const int pre = lanes_below(bal);
+  if ((t & 63) == 0) s_misc[1 + (t >> 6)] = __popcll(bal);
+  __syncthreads();
+  if (t < 64) {  // exclusive scan of the 128 counts (2 per lane)
+    const int c0 = s_cnt[2 * t], c1 = s_cnt[2 * t + 1];
+    int incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (t >= o) incl += y;
+    }
+    const int ex = incl - c0 - c1;
+    s_off[2 * t] = ex;
+    s_off[2 * t + 1] = ex + c0;
+  }
+  {
+    int off = 0;
+    for (int w = 0; w < (t >> 6); ++w) off += s_misc[1 + w];
+    if (keep) s_outrow[off + pre] = t;
+  }
+  __syncthreads();
+  if (t < 128 && s_sel[t]) s_list[s_off[s_best[t]] + s_pos[t]] = t;
+  if (a.in_place && t == 0) {
+    // destination rows [base, base + nout) overlap the sources of chunks lo..j
+    const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
+    for (int i = lo; i <= hi; ++i) wait_flag(a.flags + z * a.units + i);
+  }
+  __syncthreads();
+
+  if (a.tap_best != nullptr && t < 128) {
+    const int64_t o = (z * a.units + j) * 128 + t;
+    a.tap_best[o] = (t < nA && !copy_only) ? s_best[t] : -1;
+    a.tap_sel[o] = (uint8_t)s_sel[t];
+  }
+  if (a.tap_src != nullptr && t < nout) a.tap_src[z * a.cap_out + base + t] = start + s_outrow[t];
+
+  // 5. write K (merged rows averaged in fp32), then V through the same LDS tile, then N
+  char *Kdst = a.Kout + (z * a.cap_out + base) * (int64_t)ROWB;
+  char *Vdst = a.Vout + (z * a.cap_out + base) * (int64_t)ROWB;
+  for (int pass = 0; pass < 2; ++pass) {
+    char *dst = pass == 0 ? Kdst : Vdst;
+    if (pass == 1) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        *reinterpret_cast<u32x4 *>(tile + lds_swz(r0 + RPI * i, sg, ROWB)) = vreg[i];
+      __syncthreads();
+    }
+#pragma unroll 4
+    for (int i = 0; i < NLD; ++i) {
+      const int p = r0 + RPI * i;
+      if (p >= nout) break;
+      const int r = s_outrow[p];
+      u32x4 val = *reinterpret_cast<const u32x4 *>(tile + lds_swz(r, sg, ROWB));
+      const int b = r >> 1;
+      if ((r & 1) && s_cnt[b] > 0) {
+        float accv[EPS], tmp[EPS];
+        seg_unpack(val, tmp, tsel);
+        const float nb = (float)s_n[r];
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) accv[e] = nb * tmp[e];
+        const int q0 = s_off[b], q1 = q0 + s_cnt[b];
+        for (int q = q0; q < q1; ++q) {
+          const int ar = 2 * s_list[q];
+          const float w8 = (float)s_n[ar];
+          seg_unpack(*reinterpret_cast<const u32x4 *>(tile + lds_swz(ar, sg, ROWB)), tmp, tsel);
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) accv[e] = fmaf(w8, tmp[e], accv[e]);
+        }
+        const float W = (float)s_wsum[b];
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) accv[e] = accv[e] / W;
+        val = seg_pack(accv, tsel);
+      }
+      st16(dst + (int64_t)p * ROWB + sg * 16, val);
+    }
+  }
+  if (t < nout) {
+    const int r = s_outrow[t];
+    const int b = r >> 1;
+    a.Nout[z * a.cap_out + base + t] = ((r & 1) && s_cnt[b] > 0) ? s_wsum[b] : s_n[r];
+  }
+}
+
+template __global__ void csm_round<__bf16>(CsmArgs);
+template __global__ void csm_round<float>(CsmArgs);
+
+// Host-side launcher used by the C ABI.  Returns 0 or a hipError_t value.
+int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream) {
+  const int64_t total = args.num_slices * (int64_t)args.units;
+  const int prep_blocks = 1 + (int)std::min<int64_t>(1024, (total + 255) / 256);
+  hipLaunchKernelGGL(csm_prep, dim3(prep_blocks), dim3(256), 0, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  if (total == 0) return 0;
+  if (dtype_f32)
+    hipLaunchKernelGGL(csm_round<float>, dim3((uint32_t)total), dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL(csm_round<__bf16>, dim3((uint32_t)total), dim3(256), 0, stream, args);
+  e = hipGetLastError();
+  return (int)e;
+}
+
+}  // namespace csmkv

@@ -1,0 +1,285 @@
+// C ABI of libcsmkv (declared in include/csmkv.h): host-side validation, workspace layout
+// and launches on the caller's stream.  No entry point allocates or frees memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "csmkv.h"
+
+#include "kernel_args.hpp"
+
+namespace {
+
+constexpr int64_t kMaxCap = int64_t(1) << 24;  // degrees and row indices stay exact in fp32 / int32
+constexpr size_t kAlign = 256;
+constexpr int kHeadDim = 128;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == CSMKV_BF16 ? 2 : 4; }
+
+int check_cache(const csmkv_cache *c) {
+  if (c == nullptr) return CSMKV_EINVAL;
+  if (c->dtype != CSMKV_BF16 && c->dtype != CSMKV_F32) return CSMKV_EDTYPE;
+  if (c->num_slices < 0 || c->cap < 1 || c->d < 1) return CSMKV_EINVAL;
+  if (c->max_len < 0 || (int64_t)c->max_len > c->cap) return CSMKV_EINVAL;
+  if (c->d != kHeadDim) return CSMKV_EUNSUPPORTED;
+  if (c->cap > kMaxCap) return CSMKV_EUNSUPPORTED;
+  return CSMKV_OK;
+}
+
+// floor(r * L / 2 + 1e-9) clamped to [0, ceil(L/2)], evaluated in fp64 step by step.
+int merge_count_host(double r, int L) {
+  if (L < 2) return 0;
+  volatile double x = r * (double)L;
+  x = x * 0.5;
+  x = x + 1e-9;
+  int m = (int)std::floor((double)x);
+  int hi = (L + 1) / 2;
+  return m < 0 ? 0 : (m > hi ? hi : m);
+}
+
+int64_t units_per_slice(int32_t max_len, int32_t n1, int32_t n2, int32_t c) {
+  const int64_t M = (int64_t)max_len - n1 - n2;
+  const int64_t nch = M >= 2 ? (M + c - 1) / c : 0;
+  return nch + 1;  // chunks + the tail unit
+}
+
+int check_csm_params(int32_t n1, int32_t n2, int32_t c, double r) {
+  if (n1 < 0 || n2 < 0) return CSMKV_EINVAL;
+  if (c < 2) return CSMKV_EINVAL;
+  if (c > 256) return CSMKV_EUNSUPPORTED;
+  if (!(r >= 0.0 && r <= 1.0)) return CSMKV_EINVAL;  // also rejects NaN
+  return CSMKV_OK;
+}
+
+struct CsmLayout {
+  size_t s_in, s_out, flags, total;
+};
+
+CsmLayout csm_layout(int64_t S, int64_t units) {
+  CsmLayout L;
+  L.s_in = kAlign;
+  L.s_out = L.s_in + align_up((size_t)S * 4);
+  L.flags = L.s_out + align_up((size_t)S * 4);
+  L.total = L.flags + align_up((size_t)(S * units) * 4);
+  return L;
+}
+
+int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const int32_t *lens_in,
+               const csmkv_cache *src, void *K_out, void *V_out, int32_t *N_out,
+               int32_t *lens_out, const csmkv_cache *dst, int32_t n1, int32_t n2, int32_t c,
+               double r, const uint8_t *mask, void *ws, size_t ws_bytes, void *stream,
+               int in_place, int32_t *tap_best, uint8_t *tap_sel, int32_t *tap_src) {
+  int rc = check_cache(src);
+  if (rc) return rc;
+  rc = check_cache(dst);
+  if (rc) return rc;
+  if (src->num_slices != dst->num_slices || src->d != dst->d || src->dtype != dst->dtype)
+    return CSMKV_EINVAL;
+  rc = check_csm_params(n1, n2, c, r);
+  if (rc) return rc;
+  if (!K_in || !V_in || !N_in || !lens_in || !K_out || !V_out || !N_out || !lens_out)
+    return CSMKV_EINVAL;
+  if (!aligned(K_in, 16) || !aligned(V_in, 16) || !aligned(K_out, 16) || !aligned(V_out, 16))
+    return CSMKV_EINVAL;
+  if (tap_sel != nullptr && tap_best == nullptr) return CSMKV_EINVAL;
+  if (tap_best != nullptr && tap_sel == nullptr) return CSMKV_EINVAL;
+  const int64_t S = src->num_slices;
+  const int64_t units = units_per_slice(src->max_len, n1, n2, c);
+  if (S * units > (int64_t)INT32_MAX) return CSMKV_EUNSUPPORTED;
+  const CsmLayout lay = csm_layout(S, units);
+  if (ws == nullptr || !aligned(ws, kAlign) || ws_bytes < lay.total) return CSMKV_EWORKSPACE;
+  char *w = static_cast<char *>(ws);
+  csmkv::CsmArgs a;
+  a.Kin = static_cast<const char *>(K_in);
+  a.Vin = static_cast<const char *>(V_in);
+  a.Nin = N_in;
+  a.Kout = static_cast<char *>(K_out);
+  a.Vout = static_cast<char *>(V_out);
+  a.Nout = N_out;
+  a.lens_out = lens_out;
+  a.lens_in = lens_in;
+  a.mask = mask;
+  a.num_slices = S;
+  a.cap_in = src->cap;
+  a.cap_out = dst->cap;
+  a.max_len = src->max_len;
+  a.n1 = n1;
+  a.n2 = n2;
+  a.c = c;
+  a.m_full = merge_count_host(r, c);
+  a.units = (int32_t)units;
+  a.in_place = in_place;
+  a.r = r;
+  a.err = reinterpret_cast<int32_t *>(w);
+  a.ticket = reinterpret_cast<uint32_t *>(w + 4);
+  a.s_in = reinterpret_cast<int32_t *>(w + lay.s_in);
+  a.s_out = reinterpret_cast<int32_t *>(w + lay.s_out);
+  a.flags = reinterpret_cast<int32_t *>(w + lay.flags);
+  a.tap_best = tap_best;
+  a.tap_sel = tap_sel;
+  a.tap_src = tap_src;
+  if (S == 0) return CSMKV_OK;
+  const int e = csmkv::launch_csm(a, src->dtype == CSMKV_F32, static_cast<hipStream_t>(stream));
+  return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+struct DecLayout {
+  size_t item_off, part, total;
+};
+
+DecLayout dec_layout(const csmkv_cache *c, int G) {
+  DecLayout L;
+  L.item_off = kAlign;
+  L.part = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
+  const int64_t items = csmkv::dec_max_items(c->num_slices, c->max_len);
+  L.total = L.part + align_up((size_t)items * G * (2 + kHeadDim) * 4);
+  return L;
+}
+
+int check_heads(const csmkv_cache *c, int32_t H_q, int32_t H_kv) {
+  if (H_kv < 1 || H_q < 1 || H_q % H_kv != 0) return CSMKV_EINVAL;
+  if (c->num_slices % H_kv != 0) return CSMKV_EINVAL;
+  const int G = H_q / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return CSMKV_EUNSUPPORTED;
+  return CSMKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *csmkv_status_string(int status) {
+  switch (status) {
+    case CSMKV_OK: return "CSMKV_OK";
+    case CSMKV_EINVAL: return "CSMKV_EINVAL: argument out of range or required pointer NULL";
+    case CSMKV_EDTYPE: return "CSMKV_EDTYPE: unknown dtype";
+    case CSMKV_EUNSUPPORTED: return "CSMKV_EUNSUPPORTED: shape outside the built kernels";
+    case CSMKV_EWORKSPACE: return "CSMKV_EWORKSPACE: workspace missing, misaligned or too small";
+    case CSMKV_EHIP: return "CSMKV_EHIP: HIP runtime call or kernel launch failed";
+    case CSMKV_EDEVICE: return "CSMKV_EDEVICE: a kernel flagged an invalid lens[] entry";
+    default: return "unknown csmkv status";
+  }
+}
+
+int csmkv_version(void) { return 100; }
+
+size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
+  if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
+  const int64_t units = units_per_slice(cache->max_len, n1, n2, c);
+  return csm_layout(cache->num_slices, units).total;
+}
+
+int64_t csm_compress_units(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
+  if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
+  return units_per_slice(cache->max_len, n1, n2, c);
+}
+
+int csm_compress(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+                 int32_t n1, int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+  return csm_common(K, V, N, lens, cache, K, V, N, lens, cache, n1, n2, c, r, outlier_mask,
+                    workspace, workspace_bytes, stream, 1, nullptr, nullptr, nullptr);
+}
+
+int csm_compress_debug(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+                       int32_t n1, int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
+                       void *workspace, size_t workspace_bytes, void *stream, int32_t *best_b,
+                       uint8_t *selected, int32_t *src_pos) {
+  return csm_common(K, V, N, lens, cache, K, V, N, lens, cache, n1, n2, c, r, outlier_mask,
+                    workspace, workspace_bytes, stream, 1, best_b, selected, src_pos);
+}
+
+int csm_compress_into(const void *K_in, const void *V_in, const int32_t *N_in,
+                      const int32_t *lens_in, const csmkv_cache *src, void *K_out, void *V_out,
+                      int32_t *N_out, int32_t *lens_out, const csmkv_cache *dst, int32_t n1,
+                      int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (K_in == K_out || V_in == V_out || N_in == N_out || lens_in == lens_out) return CSMKV_EINVAL;
+  return csm_common(K_in, V_in, N_in, lens_in, src, K_out, V_out, N_out, lens_out, dst, n1, n2, c,
+                    r, outlier_mask, workspace, workspace_bytes, stream, 0, nullptr, nullptr,
+                    nullptr);
+}
+
+size_t decode_attn_logn_workspace_bytes(const csmkv_cache *cache, int32_t H_q, int32_t H_kv) {
+  if (check_cache(cache) || check_heads(cache, H_q, H_kv)) return 0;
+  return dec_layout(cache, H_q / H_kv).total;
+}
+
+int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t *N,
+                     const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                     float *O, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  rc = check_heads(cache, H_q, H_kv);
+  if (rc) return rc;
+  if (!q || !K || !V || !N || !lens || !O) return CSMKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16)) return CSMKV_EINVAL;
+  const int G = H_q / H_kv;
+  const DecLayout lay = dec_layout(cache, G);
+  if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < lay.total)
+    return CSMKV_EWORKSPACE;
+  const int64_t items = csmkv::dec_max_items(cache->num_slices, cache->max_len);
+  if (items > (int64_t)INT32_MAX / 2) return CSMKV_EUNSUPPORTED;
+  if (cache->num_slices == 0) return CSMKV_OK;
+  char *w = static_cast<char *>(workspace);
+  csmkv::DecArgs a;
+  a.q = static_cast<const char *>(q);
+  a.K = static_cast<const char *>(K);
+  a.V = static_cast<const char *>(V);
+  a.N = N;
+  a.lens = lens;
+  a.O = O;
+  a.num_slices = cache->num_slices;
+  a.cap = cache->cap;
+  a.max_len = cache->max_len;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cache->d));
+  a.err = reinterpret_cast<int32_t *>(w);
+  a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
+  a.part = reinterpret_cast<float *>(w + lay.part);
+  const int e = csmkv::launch_decode(a, cache->dtype == CSMKV_F32, G, items,
+                                     static_cast<hipStream_t>(stream));
+  return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+              const void *k_new, const void *v_new, int32_t *error_word, void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (!K || !V || !N || !lens || !k_new || !v_new) return CSMKV_EINVAL;
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return CSMKV_EINVAL;
+  if (cache->num_slices * 16 > (int64_t)INT32_MAX * 128) return CSMKV_EUNSUPPORTED;
+  csmkv::AppArgs a;
+  a.K = static_cast<char *>(K);
+  a.V = static_cast<char *>(V);
+  a.N = N;
+  a.lens = lens;
+  a.k_new = static_cast<const char *>(k_new);
+  a.v_new = static_cast<const char *>(v_new);
+  a.err = error_word;
+  a.num_slices = cache->num_slices;
+  a.cap = cache->cap;
+  a.rowb = cache->d * elem_bytes(cache->dtype);
+  const int e = csmkv::launch_append(a, static_cast<hipStream_t>(stream));
+  return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+int csmkv_read_error(const int32_t *error_word, void *stream) {
+  if (error_word == nullptr) return CSMKV_EINVAL;
+  int32_t host = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&host, error_word, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return CSMKV_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return CSMKV_EHIP;
+  return host == 0 ? CSMKV_OK : CSMKV_EDEVICE;
+}
+
+}  // extern "C"

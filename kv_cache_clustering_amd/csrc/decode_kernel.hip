@@ -1,0 +1,338 @@
+// Log-degree decode attention O = Softmax(q K^T / sqrt(d) + log N) V over a clustered
+// cache with grouped-query heads (Chelsea review, section 三, 核心公式: attention with
+// cluster degrees n_t; Algorithm 1 decode output), and the Algorithm 1 append step.
+//
+// Split-K over the sequence, HBM-bound:
+//   dec_prep    : one workgroup validates lens[], gives every slice ceil(len / TSPLIT)
+//                 work items and scans them into item offsets.
+//   dec_split   : persistent workgroups stride over the work items.  A work item is
+//                 TSPLIT tokens of one slice, shared by the G query heads of that KV
+//                 head, so K, V and N are read once per step.  Each wave streams a
+//                 quarter of the item: 16 B per lane per row, rows of 32 tokens per
+//                 sub-block, q.k by packed bf16 dot products, a 16-lane DPP reduction,
+//                 base-2 online softmax (log2 N added, log2 e folded into the scale),
+//                 P.V accumulated in fp32.  Waves merge in LDS; each item writes one
+//                 (max, sum, o[128]) partial per head.
+//   dec_combine : one workgroup per slice merges the item partials by log-sum-exp.
+#include <algorithm>
+
+#include "device_common.hpp"
+#include "kernel_args.hpp"
+
+namespace csmkv {
+
+constexpr int kTSplit = 512;        // tokens per work item
+constexpr int kDecThreads = 256;
+
+
+__global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x;
+  if (t == 0) *a.err = 0;
+  __syncthreads();
+  const int64_t S = a.num_slices;
+  const int64_t per = (S + blockDim.x - 1) / blockDim.x;
+  const int64_t z0 = t * per, z1 = min(S, z0 + per);
+  int local = 0;
+  for (int64_t z = z0; z < z1; ++z) {
+    const int s = a.lens[z];
+    const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
+    if (!ok) atomicExch(a.err, kDeviceError);
+    local += ok ? (s + kTSplit - 1) / kTSplit : 0;
+  }
+  // block exclusive scan of `local`
+  int incl = local;
+  const int lane = t & 63, w = t >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  int run = before + incl - local;
+  for (int64_t z = z0; z < z1; ++z) {
+    a.item_off[z] = run;
+    const int s = a.lens[z];
+    const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
+    run += ok ? (s + kTSplit - 1) / kTSplit : 0;
+  }
+  if (t == (int)blockDim.x - 1) a.item_off[S] = before + incl;
+}
+
+template <typename T>
+struct DecTile {
+  static constexpr int ROWB = kHeadDim * (int)sizeof(T);
+  static constexpr int LPR = ROWB / 16;     // lanes per row
+  static constexpr int RPW = 64 / LPR;      // rows per wave-wide load
+  static constexpr int SUB = 8 * RPW;       // rows per sub-block
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
+};
+
+__device__ __forceinline__ float seg_dot(u32x4 k, const u32x4 &q, __bf16 *) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // copy the element to a scalar first: a bit_cast of the vector element directly was
+    // lowered to the same source register for every i
+    const uint32_t kw = k[i], qw = q[i];
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kw),
+                                        __builtin_bit_cast(bf16x2, qw), s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float seg_dot(u32x4 k, const u32x4 &q, float *) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(k[i]), __uint_as_float(q[i]), s);
+  return s;
+}
+__device__ __forceinline__ void seg_to_f32(u32x4 v, float *o, __bf16 *) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = bf_lo(v[i]);
+    o[2 * i + 1] = bf_hi(v[i]);
+  }
+}
+__device__ __forceinline__ void seg_to_f32(u32x4 v, float *o, float *) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T, int G>
+__global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
+  using DT = DecTile<T>;
+  constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
+  constexpr int PW = 2 + kHeadDim;  // partial width per head
+  __shared__ float s_part[4][G][PW];
+  __shared__ int32_t s_item[2];
+  T *tsel = nullptr;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int sg = l % LPR, rw = l / LPR;
+  const int64_t S = a.num_slices;
+  const int total = a.item_off[S];
+  const float NEG_INF = -__builtin_inff();
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // slice of this item: last z with item_off[z] <= item
+    int64_t lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (a.item_off[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int64_t z = lo;
+    const int s = a.lens[z];
+    const int p = item - a.item_off[z];
+    const int tok0 = p * kTSplit, tok1 = min(s, tok0 + kTSplit);
+    const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
+    // this lane's q segment for each head of the group
+    u32x4 qv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + h) * (int64_t)kHeadDim) * sizeof(T) + sg * 16);
+    const char *Kz = a.K + z * a.cap * ROWB;
+    const char *Vz = a.V + z * a.cap * ROWB;
+    const int32_t *Nz = a.N + z * a.cap;
+    const int wq = (kTSplit / 4);
+    const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
+    float mrun[G], lrun[G], o[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mrun[h] = NEG_INF;
+      lrun[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    }
+    for (int sb = wb; sb < we; sb += SUB) {
+      u32x4 kr[8], vr[8];
+      int32_t nv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = sb + RPW * i + rw;
+        const bool ok = tok < we;
+        kr[i] = ok ? ld16(Kz + (int64_t)tok * ROWB + sg * 16) : u32x4{0u, 0u, 0u, 0u};
+        vr[i] = ok ? ld16(Vz + (int64_t)tok * ROWB + sg * 16) : u32x4{0u, 0u, 0u, 0u};
+        nv[i] = ok ? Nz[tok] : 0;
+      }
+      float zs[8][G];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = sb + RPW * i + rw < we;
+        const float ln = __builtin_amdgcn_logf((float)nv[i]);  // log2
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float d = row16_sum(seg_dot(kr[i], qv[h], tsel));
+          if (LPR == 32) d += __shfl_xor(d, 16);
+          zs[i][h] = ok ? fmaf(d, a.scale_log2, ln) : NEG_INF;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mx = zs[0][h];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, zs[i][h]);
+        if (RPW == 4) mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(mrun[h], mx);
+        const float alpha = fast_exp2(mrun[h] - mn);
+        mrun[h] = mn;
+        lrun[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float vf[EPL];
+        seg_to_f32(vr[i], vf, tsel);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pr = fast_exp2(zs[i][h] - mrun[h]);
+          lrun[h] += pr;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vf[e], o[h][e]);
+        }
+      }
+    }
+    // sum the row groups of the wave (they hold different tokens, same segment)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (RPW == 4) lrun[h] += __shfl_xor(lrun[h], 16);
+      lrun[h] += __shfl_xor(lrun[h], 32);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if (RPW == 4) o[h][e] += __shfl_xor(o[h][e], 16);
+        o[h][e] += __shfl_xor(o[h][e], 32);
+      }
+    }
+    if (rw == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (sg == 0) {
+          s_part[w][h][0] = mrun[h];
+          s_part[w][h][1] = lrun[h];
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s_part[w][h][2 + sg * EPL + e] = o[h][e];
+      }
+    }
+    __syncthreads();
+    float *dst = a.part + (int64_t)item * G * PW;
+    for (int i = t; i < G * PW; i += kDecThreads) {
+      const int h = i / PW, k = i % PW;
+      float M = NEG_INF;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_part[ww][h][0]);
+      float v = 0.f;
+      if (k == 0) {
+        v = M;
+      } else {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float mw = s_part[ww][h][0];
+          if (mw != NEG_INF) v += fast_exp2(mw - M) * s_part[ww][h][k];
+        }
+      }
+      dst[i] = v;
+    }
+    __syncthreads();
+  }
+}
+
+template <int G>
+__global__ void __launch_bounds__(128) dec_combine(DecArgs a) {
+  constexpr int PW = 2 + kHeadDim;
+  const int64_t z = blockIdx.x;
+  const int e = threadIdx.x;
+  const int i0 = a.item_off[z], i1 = a.item_off[z + 1];
+  const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
+  const float NEG_INF = -__builtin_inff();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = NEG_INF, L = 0.f, acc = 0.f;
+    for (int it = i0; it < i1; ++it) {
+      const float *pp = a.part + ((int64_t)it * G + h) * PW;
+      const float m = pp[0];
+      if (m == NEG_INF) continue;
+      const float mn = fmaxf(M, m);
+      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(m - mn);
+      L = L * sa + pp[1] * sb;
+      acc = acc * sa + pp[2 + e] * sb;
+      M = mn;
+    }
+    a.O[(g * a.H_q + kvh * G + h) * (int64_t)kHeadDim + e] = L > 0.f ? acc / L : 0.f;
+  }
+}
+
+template <typename T>
+static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((dec_split<T, 1>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((dec_split<T, 2>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((dec_split<T, 4>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_split<T, 8>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
+  return num_slices * (int64_t)((max_len + kTSplit - 1) / kTSplit);
+}
+
+int launch_decode(const DecArgs &a, int dtype_f32, int G, int64_t max_items, hipStream_t st) {
+  hipLaunchKernelGGL(dec_prep, dim3(1), dim3(1024), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_items, 256 * 8));
+  int rc = dtype_f32 ? launch_dec_t<float>(a, G, grid, st) : launch_dec_t<__bf16>(a, G, grid, st);
+  if (rc) return rc;
+  const dim3 cg((uint32_t)a.num_slices);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(dec_combine<1>, cg, dim3(128), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(dec_combine<2>, cg, dim3(128), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(dec_combine<4>, cg, dim3(128), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(dec_combine<8>, cg, dim3(128), 0, st, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+// ------------------------------------------------------------------ append
+// K[s] = k, V[s] = v, N[s] = 1, s = s + 1 for every slice (Chelsea review, Algorithm 1
+// decode update).  16 lanes of one wave serve one slice (one 16-byte segment each for
+// bf16 rows; two for fp32 rows), so the lens read precedes its update in program order.
+
+
+__global__ void __launch_bounds__(256) kv_append_kernel(AppArgs a) {
+  const int64_t z = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sg = threadIdx.x & 15;
+  if (z >= a.num_slices) return;
+  const int s = a.lens[z];
+  const bool ok = s >= 0 && (int64_t)s < a.cap;
+  if (ok) {
+    for (int off = sg * 16; off < a.rowb; off += 256) {
+      st16(a.K + (z * a.cap + s) * a.rowb + off, ld16(a.k_new + z * a.rowb + off));
+      st16(a.V + (z * a.cap + s) * a.rowb + off, ld16(a.v_new + z * a.rowb + off));
+    }
+  }
+  if (sg == 0) {
+    if (ok) {
+      a.N[z * a.cap + s] = 1;
+      a.lens[z] = s + 1;
+    } else if (a.err != nullptr) {
+      atomicExch(a.err, kDeviceError);
+    }
+  }
+}
+
+int launch_append(const AppArgs &a, hipStream_t st) {
+  const int64_t threads = a.num_slices * 16;
+  if (threads == 0) return 0;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace csmkv

@@ -1,0 +1,60 @@
+// Argument blocks and host launchers shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csmkv {
+
+struct CsmArgs {
+  const char *Kin, *Vin;
+  const int32_t *Nin;
+  char *Kout, *Vout;
+  int32_t *Nout;
+  int32_t *lens_out;
+  const int32_t *lens_in;
+  const uint8_t *mask;
+  int64_t num_slices, cap_in, cap_out;
+  int32_t max_len, n1, n2, c, m_full, units, in_place;
+  double r;
+  // workspace
+  int32_t *err;      // device error word of this call
+  uint32_t *ticket;  // unit ticket counter
+  int32_t *s_in;     // [num_slices] validated input length, -1 = skip the slice
+  int32_t *s_out;    // [num_slices] output length
+  int32_t *flags;    // [num_slices][units] "chunk source consumed"
+  // debug taps (nullable)
+  int32_t *tap_best;
+  uint8_t *tap_sel;
+  int32_t *tap_src;
+};
+
+struct DecArgs {
+  const char *q, *K, *V;
+  const int32_t *N, *lens;
+  float *O;
+  int64_t num_slices, cap;
+  int32_t max_len, H_q, H_kv;
+  float scale_log2;   // log2(e) / sqrt(d)
+  int32_t *err;       // device error word of this call
+  int32_t *item_off;  // [num_slices + 1] first work item of each slice
+  float *part;        // [items][G][2 + d] (max, sum, o) partials
+};
+
+struct AppArgs {
+  char *K, *V;
+  int32_t *N, *lens;
+  const char *k_new, *v_new;
+  int32_t *err;
+  int64_t num_slices, cap;
+  int32_t rowb;
+};
+
+// Each returns 0 or a hipError_t value.
+int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream);
+int launch_decode(const DecArgs &a, int dtype_f32, int G, int64_t max_items, hipStream_t st);
+int launch_append(const AppArgs &a, hipStream_t st);
+// Upper bound on decode work items for a geometry (sizes the partial buffer).
+int64_t dec_max_items(int64_t num_slices, int32_t max_len);
+
+}  // namespace csmkv

@@ -1,0 +1,126 @@
+"""log-N decode attention and append on the GPU (through the C ABI) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+from oracle import attention as oatt
+from tests import parity
+from tests.gpu.conftest import host_cache
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3  # max-abs bound on the attention output
+
+
+def _oracle_all(q, K, V, N, lens, H_q, H_kv):
+    return oatt.decode_attn_logn(parity.to_f64(q), parity.to_f64(K), parity.to_f64(V),
+                                 N.numpy().astype(np.int64), lens.numpy(), H_q, H_kv)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("H_q,H_kv", [(8, 2), (4, 4), (4, 2), (16, 2)])
+def test_ragged_lengths_random_degrees(lib, dev, dtype, H_q, H_kv):
+    groups = 3
+    S = groups * H_kv
+    rng = np.random.default_rng(H_q * 10 + H_kv)
+    choices = [0, 1, 2, 511, 512, 513, 1024, 1500, 2047, 2600]
+    lens = [int(x) for x in rng.choice(choices, size=S)]
+    lens[0] = 2600
+    K, V, N, L = host_cache(S, 2600, lens, dtype=dtype, seed=H_q, degrees=True)
+    N[N > 0] = torch.from_numpy(rng.integers(1, 40, size=int((N > 0).sum())).astype(np.int32))
+    q = torch.randn((groups, H_q, 128), generator=torch.Generator().manual_seed(1)).to(dtype)
+    O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), L.to(dev), H_q, H_kv)
+    ref = _oracle_all(q, K, V, N, L, H_q, H_kv)
+    err = np.abs(O.cpu().double().numpy() - ref)
+    print(dtype, H_q, H_kv, "max abs", err.max(), "max rel", (err / (np.abs(ref) + 1e-3)).max())
+    assert err.max() < TOL
+    assert err.max() < 2e-5 if dtype == torch.float32 else err.max() < 2e-4
+    for z in range(S):                      # empty slices give zeros
+        if lens[z] == 0:
+            g, kvh = divmod(z, H_kv)
+            G = H_q // H_kv
+            assert torch.all(O[g, kvh * G:(kvh + 1) * G] == 0)
+
+
+def test_llama3_64k_budget_cache_sampled(lib, dev):
+    """Attention over a cache compressed to the 20% budget on the GPU (outlier slices stay
+    at 64K); all heads computed, sampled heads compared with the oracle."""
+    from kv_cache_clustering_amd.schedule import Algorithm1
+    w = kvsynth.workload(4)
+    c = kvsynth.make_cache(w, dev, with_appends=False)
+    K, V, N, lens, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]
+    sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps)
+    s_prev = w.ctx
+    for r in sched.prefill_rounds():
+        lib.csm_compress(K, V, N, lens, w.n1, w.n2, w.c, r, mask, max_len=w.ctx)
+    torch.cuda.synchronize()
+    q = kvsynth.make_queries(w, dev, steps=1)[0]
+    O = lib.decode_attn_logn(q, K, V, N, lens, w.H_q, w.H_kv, max_len=w.ctx).cpu().double().numpy()
+    maskh = mask.cpu().numpy()
+    zs = [0, 5, 100, 255] + [int(x) for x in np.nonzero(maskh)[0][:2]]
+    worst = 0.0
+    for z in zs:
+        g, kvh = divmod(z, w.H_kv)
+        s = int(lens[z])
+        assert s == (w.ctx if maskh[z] else sched.s)
+        Kz, Vz = parity.to_f64(K[z, :s].cpu()), parity.to_f64(V[z, :s].cpu())
+        Nz = N[z, :s].cpu().numpy().astype(np.int64)
+        assert int(Nz.sum()) == w.ctx
+        for h in range(w.G):
+            hq = kvh * w.G + h
+            ref = oatt.logn_attention_one(parity.to_f64(q[g, hq].cpu()), Kz, Vz, Nz)
+            worst = max(worst, float(np.abs(O[g, hq] - ref).max()))
+    print("max abs", worst)
+    assert worst < 2e-4
+
+
+def test_single_head_workload_fp32(lib, dev):
+    w = kvsynth.workload(1)
+    c = kvsynth.make_cache(w, "cpu")
+    K, V, N, L = (c[k].to(dev) for k in ("K", "V", "N", "lens"))
+    lib.csm_compress(K, V, N, L, 16, 64, 256, 0.5)
+    q = kvsynth.make_queries(w, "cpu", steps=1)[0]
+    O = lib.decode_attn_logn(q.to(dev), K, V, N, L, 1, 1)
+    ref = _oracle_all(q, K.cpu(), V.cpu(), N.cpu(), L.cpu(), 1, 1)
+    assert int(L[0]) == 1556
+    assert np.abs(O.cpu().double().numpy() - ref).max() < 1e-5
+
+
+def test_append_then_attend(lib, dev):
+    lens = [10, 0, 599, 600]
+    K, V, N, L = host_cache(4, 600, lens, seed=4)
+    Kd, Vd, Nd, Ld = K.to(dev), V.to(dev), N.to(dev), L.to(dev)
+    kn = torch.randn((4, 128)).to(torch.bfloat16)
+    vn = torch.randn((4, 128)).to(torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib.kv_append(Kd, Vd, Nd, Ld, kn.to(dev), vn.to(dev), err)
+    assert lib.read_error(err) == lib.EDEVICE          # slice 3 is full
+    Lh = Ld.cpu().numpy()
+    assert list(Lh) == [11, 1, 600, 600]
+    for z, s in enumerate([10, 0, 599]):
+        assert torch.equal(Kd[z, s].cpu(), kn[z]) and torch.equal(Vd[z, s].cpu(), vn[z])
+        assert int(Nd[z, s]) == 1
+        assert torch.equal(Kd[z, :s].cpu(), K[z, :s])
+    assert torch.equal(Kd[3].cpu(), K[3]) and torch.equal(Nd[3].cpu(), N[3])
+    err.zero_()
+    Ld[2] = 599
+    Ld[3] = 599
+    lib.kv_append(Kd, Vd, Nd, Ld, kn.to(dev), vn.to(dev), err)
+    assert lib.read_error(err) == lib.OK
+    q = torch.randn((1, 4, 128)).to(torch.bfloat16)
+    O = lib.decode_attn_logn(q.to(dev), Kd, Vd, Nd, Ld, 4, 4)
+    ref = _oracle_all(q, Kd.cpu(), Vd.cpu(), Nd.cpu(), Ld.cpu(), 4, 4)
+    assert np.abs(O.cpu().double().numpy() - ref).max() < 2e-4
+
+
+def test_bad_length_gives_zeros_and_error(lib, dev):
+    K, V, N, L = host_cache(2, 700, [700, 700], seed=9)
+    Ld = L.to(dev)
+    Ld[1] = 800
+    q = torch.randn((2, 1, 128)).to(torch.bfloat16)
+    ws = torch.empty(lib.decode_workspace_bytes(K, 1, 1, max_len=700), dtype=torch.uint8, device=dev)
+    O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), Ld, 1, 1, max_len=700,
+                             workspace=ws)
+    assert lib.read_error(ws) == lib.EDEVICE
+    assert torch.all(O[1] == 0) and torch.any(O[0] != 0)

@@ -1,0 +1,124 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared entry point,
+and rejects bad arguments before enqueuing anything (no GPU work is started here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "kv_cache_clustering_amd", "libcsmkv.so")
+HDR = os.path.join(ROOT, "include", "csmkv.h")
+
+
+def _declared():
+    text = open(HDR).read()
+    return re.findall(r"^CSMKV_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libcsmkv.so is not built: run __graft_entry__.build()")
+    from kv_cache_clustering_amd import _lib
+    return _lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 11
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(lib.EXPORTED)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.version() == 100
+    for code in range(-6, 1):
+        assert lib.status_string(code).startswith("CSMKV_")
+    assert "unknown" in lib.status_string(-99)
+
+
+def _desc(lib, S=4, cap=1000, d=128, dtype=0, max_len=1000):
+    return lib.CacheDesc(S, cap, d, dtype, max_len)
+
+
+def test_workspace_sizes(lib):
+    d = _desc(lib)
+    units = lib.raw.csm_compress_units(ctypes.byref(d), 16, 64, 256)
+    assert units == math.ceil((1000 - 80) / 256) + 1
+    ws = lib.raw.csm_compress_workspace_bytes(ctypes.byref(d), 16, 64, 256)
+    assert ws >= 4 * (4 * units) + 2 * 4 * 4 and ws % 256 == 0
+    assert lib.raw.csm_compress_workspace_bytes(ctypes.byref(d), 16, 64, 1) == 0
+    assert lib.raw.csm_compress_workspace_bytes(ctypes.byref(_desc(lib, d=64)), 16, 64, 256) == 0
+    dws = lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(d), 8, 2)
+    assert dws >= 4 * 2 * (2 + 128) * 4 * 2
+    assert lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(d), 6, 4) == 0
+    assert lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(d), 32, 2) == 0  # G = 16
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+
+
+def _compress(lib, desc, n1=16, n2=64, c=256, r=0.5, K=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.raw.csm_compress(K, FAKE, FAKE, FAKE, ctypes.byref(desc), n1, n2, c, r, None, ws,
+                                ws_bytes, None)
+
+
+def test_compress_argument_validation(lib):
+    d = _desc(lib)
+    assert _compress(lib, d, r=1.5) == lib.EINVAL
+    assert _compress(lib, d, r=-0.1) == lib.EINVAL
+    assert _compress(lib, d, r=float("nan")) == lib.EINVAL
+    assert _compress(lib, d, c=1) == lib.EINVAL
+    assert _compress(lib, d, c=257) == lib.EUNSUPPORTED
+    assert _compress(lib, d, n1=-1) == lib.EINVAL
+    assert _compress(lib, d, n2=-3) == lib.EINVAL
+    assert _compress(lib, d, K=None) == lib.EINVAL
+    assert _compress(lib, d, K=ctypes.c_void_p((1 << 20) + 8)) == lib.EINVAL  # misaligned
+    assert _compress(lib, d, ws=None) == lib.EWORKSPACE
+    assert _compress(lib, d, ws_bytes=16) == lib.EWORKSPACE
+    assert _compress(lib, d, ws=ctypes.c_void_p((1 << 20) + 64)) == lib.EWORKSPACE
+    assert _compress(lib, _desc(lib, dtype=7)) == lib.EDTYPE
+    assert _compress(lib, _desc(lib, d=64)) == lib.EUNSUPPORTED
+    assert _compress(lib, _desc(lib, max_len=1001)) == lib.EINVAL
+    assert _compress(lib, _desc(lib, cap=0, max_len=0)) == lib.EINVAL
+    assert _compress(lib, _desc(lib, cap=(1 << 24) + 1, max_len=10)) == lib.EUNSUPPORTED
+    assert lib.raw.csm_compress(FAKE, FAKE, FAKE, FAKE, None, 16, 64, 256, 0.5, None, FAKE,
+                                1 << 30, None) == lib.EINVAL
+
+
+def test_compress_into_rejects_aliasing_and_mismatch(lib):
+    d = _desc(lib)
+    args = (FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, ctypes.c_void_p(2 << 20),
+            ctypes.c_void_p(3 << 20), ctypes.c_void_p(4 << 20), ctypes.byref(d), 16, 64, 256,
+            0.5, None, FAKE, 1 << 30, None)
+    assert lib.raw.csm_compress_into(*args) == lib.EINVAL          # K_in == K_out
+    d2 = _desc(lib, S=5)
+    args2 = (FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), ctypes.c_void_p(5 << 20),
+             ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20), ctypes.c_void_p(4 << 20),
+             ctypes.byref(d2), 16, 64, 256, 0.5, None, FAKE, 1 << 30, None)
+    assert lib.raw.csm_compress_into(*args2) == lib.EINVAL         # slice counts differ
+
+
+def test_debug_taps_must_come_together(lib):
+    d = _desc(lib)
+    rc = lib.raw.csm_compress_debug(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 16, 64, 256, 0.5,
+                                    None, FAKE, 1 << 30, None, FAKE, None, None)
+    assert rc == lib.EINVAL
+
+
+def test_decode_and_append_validation(lib):
+    d = _desc(lib, S=8)
+    dec = lib.raw.decode_attn_logn
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 6, 4, FAKE, FAKE, 1 << 30, None) == lib.EINVAL
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 48, 3, FAKE, FAKE, 1 << 30, None) == lib.EINVAL
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 64, 4, FAKE, FAKE, 1 << 30, None) == lib.EUNSUPPORTED
+    assert dec(None, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 16, 4, FAKE, FAKE, 1 << 30, None) == lib.EINVAL
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 16, 4, FAKE, FAKE, 8, None) == lib.EWORKSPACE
+    app = lib.raw.kv_append
+    assert app(FAKE, FAKE, FAKE, None, ctypes.byref(d), FAKE, FAKE, None, None) == lib.EINVAL
+    assert app(FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc(lib, dtype=3)), FAKE, FAKE, None, None) == lib.EDTYPE
+    assert lib.raw.csmkv_read_error(None, None) == lib.EINVAL

@@ -1,0 +1,280 @@
+"""Benchmark: CSM compression and log-N decode attention at 64K context on one MI355X.
+
+Workload (synthetic, seeded): Llama-3.1-8B-shaped KV cache, 32 layers x 8 KV heads x d=128,
+bf16, batch 1, 65536-token context, 4% of (layer, kv-head) slices flagged outlier, keys
+AR(1) with rho ~ U[0.8, 0.99] per head, values N(0, 1), queries N(0, 1).
+
+One step = one pass of the whole hot path:
+  1. csm_compress_into: one CSM round (r = 0.5, c = 256, n1 = 16, n2 = 64) over the
+     pristine 64K cache, written to a second cache (the prefill -> serving-cache round);
+  2. kv_append: one decode token appended to every slice of the serving cache, which was
+     compressed beforehand (untimed) to the 20% budget by the annealed Algorithm 1 rounds;
+  3. decode_attn_logn: GQA log-N attention for all 32 query heads of all 32 layers.
+Inputs are resident in HBM before timing.  `value` is the CSM round's throughput in
+slice-tokens/s (input tokens of the compressed slices per second of the csm call, timed
+with HIP events on the stream the library launches on); the decode figures are reported
+beside it.  Roofline: algorithmic bytes (what the round must read and write) / duration.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSM compress tokens/s + log-N decode-attn HBM GB/s (% of peak), 64K ctx"
+PEAK_GBPS = 8000.0
+ROW_BYTES = 128 * 2 * 2 + 4  # K + V (bf16, d = 128) + int32 degree
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slices", type=int, default=10)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+def csm_bytes(lens_in, lens_out, mask, n1, out_of_place):
+    """Algorithmic HBM bytes of one round: every compressed slice reads its rows once and
+    writes its kept rows once; out of place, protected rows and outlier slices are copied."""
+    total = 0
+    for s, s2, m in zip(lens_in, lens_out, mask):
+        if m:
+            total += 2 * s * ROW_BYTES if out_of_place else 0
+        elif out_of_place:
+            total += (s + s2) * ROW_BYTES
+        else:
+            total += ((s - n1) + (s2 - n1)) * ROW_BYTES
+    return total
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path "
+              "shards by slice with no exchange, and no multi-GPU run is part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import kvsynth
+    from kv_cache_clustering_amd import _lib as lib
+    from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = kvsynth.workload(4)
+    K, W = args.steps, args.warmup
+    if K + W > w.steps:
+        print(f"steps + warmup must be <= {w.steps} (appended-token capacity)", file=sys.stderr)
+        sys.exit(1)
+
+    t_setup = time.time()
+    c = kvsynth.make_cache(w, dev)
+    K0, V0, N0, L0, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]
+    app_k, app_v = c["app_k"], c["app_v"]
+    q_all = kvsynth.make_queries(w, dev, steps=K + W)
+    S, cap, d = K0.shape
+    maskh = mask.cpu().numpy()
+    # output cache of the timed round
+    Kw, Vw = torch.empty_like(K0), torch.empty_like(V0)
+    Nw, Lw = torch.empty_like(N0), torch.empty_like(L0)
+    # serving cache: compressed to the budget by Algorithm 1's prefill rounds (untimed)
+    Kd, Vd, Nd, Ld = K0.clone(), V0.clone(), N0.clone(), L0.clone()
+    sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
+    ws_c = torch.empty(lib.csm_workspace_bytes(K0, w.n1, w.n2, w.c, max_len=w.ctx),
+                       dtype=torch.uint8, device=dev)
+    for r in sched.prefill_rounds():
+        lib.csm_compress(Kd, Vd, Nd, Ld, w.n1, w.n2, w.c, r, mask, max_len=w.ctx, workspace=ws_c)
+    assert lib.read_error(ws_c) == lib.OK
+    ws_d = torch.empty(lib.decode_workspace_bytes(Kd, w.H_q, w.H_kv), dtype=torch.uint8, device=dev)
+    O = torch.empty((w.groups, w.H_q, d), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    r0 = w.r_init
+    s_out = round_output_length(w.ctx, w.n1, w.n2, w.c, r0)
+    lens_in = [w.ctx] * S
+    lens_out = [w.ctx if m else s_out for m in maskh]
+    csm_alg = csm_bytes(lens_in, lens_out, maskh, w.n1, out_of_place=True)
+    slice_tokens = int(sum(w.ctx for m in maskh if not m))
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+
+    def step(i, evs=None):
+        if evs:
+            evs[0].record(stream)
+        lib.csm_compress_into(K0, V0, N0, L0, Kw, Vw, Nw, Lw, w.n1, w.n2, w.c, r0, mask,
+                              max_len=w.ctx, workspace=ws_c)
+        if evs:
+            evs[1].record(stream)
+        lib.kv_append(Kd, Vd, Nd, Ld, app_k[i], app_v[i], err)
+        if evs:
+            evs[2].record(stream)
+        lib.decode_attn_logn(q_all[i], Kd, Vd, Nd, Ld, w.H_q, w.H_kv, out=O, workspace=ws_d)
+        if evs:
+            evs[3].record(stream)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert lib.read_error(ws_c) == lib.OK and lib.read_error(ws_d) == lib.OK
+    assert lib.read_error(err) == lib.OK
+    ms_per_step = (t1 - t0) * 1e3 / K
+    csm_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    app_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    csm_avg, dec_avg, app_avg = (sum(x) / K for x in (csm_ms, dec_ms, app_ms))
+
+    # decode bytes: every slice's rows once, plus q in and O out
+    lens_d = Ld.cpu().numpy()
+    dec_lens_mid = lens_d - (K // 2)  # lengths grow by one per step; use the mid-run length
+    dec_alg = int(dec_lens_mid.sum()) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
+    assert np.all(Lw.cpu().numpy() == np.array(lens_out))
+
+    csm_gbps = csm_alg / (csm_avg * 1e-3) / 1e9
+    dec_gbps = dec_alg / (dec_avg * 1e-3) / 1e9
+    value = slice_tokens / (csm_avg * 1e-3)
+
+    # auxiliary: the in-place round (input restored untimed before each rep)
+    Ki, Vi, Ni, Li = torch.empty_like(K0), torch.empty_like(V0), torch.empty_like(N0), torch.empty_like(L0)
+    inplace_ms = []
+    for _ in range(3):
+        Ki.copy_(K0); Vi.copy_(V0); Ni.copy_(N0); Li.copy_(L0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.csm_compress(Ki, Vi, Ni, Li, w.n1, w.n2, w.c, r0, mask, max_len=w.ctx, workspace=ws_c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        inplace_ms.append(e0.elapsed_time(e1))
+    assert torch.equal(Li, Lw)
+    inplace_alg = csm_bytes(lens_in, lens_out, maskh, w.n1, out_of_place=False)
+    inplace_avg = sum(inplace_ms) / len(inplace_ms)
+    del Ki, Vi, Ni, Li
+
+    # achievable copy bandwidth on this machine (context for the roofline fraction)
+    nbytes = 4 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    if args.calibrate_copy:
+        g = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        h = torch.empty_like(g)
+        h.copy_(g)
+        torch.cuda.synchronize()
+        del g, h
+    del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, K0, V0, N0, L0, Kd, Vd, Nd, Ld, q_all[W + K - 1], maskh,
+                           args.cpu_slices)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "slice-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": w.H_kv, "q_heads": w.H_q,
+                   "d": d, "batch": w.batch, "ctx": w.ctx, "slices": S,
+                   "outlier_slices": int(maskh.sum()), "c": w.c, "n1": w.n1, "n2": w.n2,
+                   "r": r0, "round_out_len": s_out, "budget": sched.budget,
+                   "decode_len": int(sched.s), "prefill_rounds": len(sched.rounds)},
+        "csm": {"ms": csm_avg, "alg_bytes": csm_alg, "GBps": csm_gbps, "frac": csm_gbps / PEAK_GBPS,
+                "slice_tokens": slice_tokens,
+                "model_tokens_per_s": w.ctx / (csm_avg * 1e-3),
+                "whole_step_slice_tokens_per_s": slice_tokens / (ms_per_step * 1e-3),
+                "in_place_ms": inplace_avg, "in_place_alg_bytes": inplace_alg,
+                "in_place_GBps": inplace_alg / (inplace_avg * 1e-3) / 1e9},
+        "decode_attn": {"us": dec_avg * 1e3, "alg_bytes": dec_alg, "GBps": dec_gbps,
+                        "frac": dec_gbps / PEAK_GBPS, "layers": w.layers},
+        "append_us": app_avg * 1e3,
+        "hbm_copy_GBps": copy_gbps,
+        "roofline": {"bound": "hbm", "kernel": "csm_round<bf16> (csm_compress_into)",
+                     "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": csm_gbps / PEAK_GBPS, "traffic": None},
+        "cpu_baseline": cpu,
+        "setup_s": setup_s,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, K0, V0, N0, L0, Kd, Vd, Nd, Ld, q, maskh, nslices):
+    """The fp64 oracle on the host: one CSM round on a sample of slices (slice-tokens/s) and
+    one full decode step over every slice of the serving cache (us/step)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oatt
+    from oracle import bf16 as obf16
+    from oracle import csm as ocsm
+
+    def f64(t):
+        return obf16.bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+
+    pick = [z for z in range(K0.shape[0]) if not maskh[z]]
+    rng = np.random.default_rng(0)
+    pick = sorted(rng.choice(pick, size=min(nslices, len(pick)), replace=False).tolist())
+    inputs = [(f64(K0[z, :w.ctx]), f64(V0[z, :w.ctx]), N0[z, :w.ctx].cpu().numpy().astype(np.int64))
+              for z in pick]
+    lens = Ld.cpu().numpy()
+    dec_in = [(f64(Kd[z, :lens[z]]), f64(Vd[z, :lens[z]]), Nd[z, :lens[z]].cpu().numpy().astype(np.int64))
+              for z in range(Kd.shape[0])]
+    qh = f64(q)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for (k, v, n) in inputs:
+            ocsm.csm_round_slice(k, v, n, w.ctx, w.n1, w.n2, w.c, w.r_init, "bf16", "f64")
+        t_csm = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for z, (k, v, n) in enumerate(dec_in):
+            g, kvh = divmod(z, w.H_kv)
+            for h in range(w.G):
+                oatt.logn_attention_one(qh[g, kvh * w.G + h], k, v, n)
+        t_dec = time.perf_counter() - t0
+    return {"value": len(inputs) * w.ctx / t_csm, "unit": "slice-tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"CSM round on {len(inputs)} of {int((maskh == 0).sum())} compressible "
+                      f"64K slices (fp64 numpy, 1 thread); decode: one full step over all "
+                      f"{Kd.shape[0]} slices",
+            "csm_s": t_csm, "decode_us_per_step": t_dec * 1e6,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

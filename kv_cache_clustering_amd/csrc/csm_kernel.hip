@@ -31,10 +31,14 @@
 //   v_mfma_f32_32x32x2_f32), wave w owning A columns [32w, 32w+32) and all B rows;
 //   cosine = dot / (max(|a|,1e-12) * max(|b|,1e-12)) in fp32, arg-max per A column
 //   inside each lane then across the two half-waves (lowest B index on ties);
-//   rank of every A edge by (score desc, index asc) through a 128-way comparison count;
-//   per-target source lists in ascending A order (counting sort);
+//   rank of every A edge by (score desc, index asc) through a 128-way comparison count
+//   split over all four waves;
+//   per-target source lists in ascending A order: same-target lanes found with seven
+//   ballots over the target index bits, slots by mbcnt, counts scanned across targets;
 //   keep-mask prefix sum (ballot + mbcnt) gives each kept row its output slot;
-//   merged rows = (N_b k_b + sum N_a k_a) / (N_b + sum N_a) in fp32, stored RNE.
+//   rows that are not merge targets are copied in one pass; merge targets, compacted into
+//   a list, are computed as (N_b k_b + sum N_a k_a) * (1 / (N_b + sum N_a)) in fp32 and
+//   stored RNE (v_cvt_pk_bf16_f32); stores are non-temporal (the output is not re-read).
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -119,7 +123,10 @@ __device__ __forceinline__ void seg_unpack(u32x4 v, float *o, float *) {
 __device__ __forceinline__ u32x4 seg_pack(const float *o, __bf16 *) {
   u32x4 v;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(o[2 * q], o[2 * q + 1]);
+  for (int q = 0; q < 4; ++q) {  // v_cvt_pk_bf16_f32: round to nearest even
+    const bf16x2 h = {(__bf16)o[2 * q], (__bf16)o[2 * q + 1]};
+    v[q] = __builtin_bit_cast(uint32_t, h);
+  }
   return v;
 }
 __device__ __forceinline__ u32x4 seg_pack(const float *o, float *) {
@@ -247,16 +254,17 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
+__device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   using TL = Tile<T>;
   constexpr int ROWB = TL::ROWB, SEGS = TL::SEGS, RPI = TL::RPI, NLD = TL::NLD, EPS = TL::EPS;
   __shared__ __attribute__((aligned(16))) char tile[kMaxChunk * ROWB];
   __shared__ float s_norm[kMaxChunk];
   __shared__ int32_t s_n[kMaxChunk];
   __shared__ int32_t s_outrow[kMaxChunk];
-  __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_pos[128],
-      s_list[128];
-  __shared__ float s_score[128];
+  __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_list[128];
+  __shared__ int32_t s_cnt0[128], s_cnt1[128], s_rank[2][128];
+  __shared__ int32_t s_mrg[4][64], s_mcnt[4];
+  __shared__ __attribute__((aligned(16))) float s_score[128];
   __shared__ int32_t s_misc[8];
 
   const int t = threadIdx.x;
@@ -369,50 +377,61 @@ __global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
   }
   __syncthreads();
 
-  // 3. top-m selection: rank of each A edge by (score desc, index asc)
-  if (t < 128) {
-    int sel = 0;
-    if (t < nA && m > 0 && nB > 0) {
-      const float sc = s_score[t];
-      int rank = 0;
-#pragma unroll 8
-      for (int q = 0; q < 128; ++q) {
-        const float o = s_score[q];
-        rank += (o > sc) || (o == sc && q < t);
-      }
-      sel = rank < m;
+  // 3. top-m selection: rank of each A edge by (score desc, index asc).  Every thread
+  //    counts the higher-ranked edges among one half of the 128 candidates.
+  {
+    const int aa = t & 127, half = t >> 7;
+    const float sc = s_score[aa];
+    int cnt = 0;
+#pragma unroll 4
+    for (int q = half * 64; q < half * 64 + 64; q += 4) {
+      const float4 o = *reinterpret_cast<const float4 *>(&s_score[q]);
+      cnt += (o.x > sc) | ((o.x == sc) & (q < aa));
+      cnt += (o.y > sc) | ((o.y == sc) & (q + 1 < aa));
+      cnt += (o.z > sc) | ((o.z == sc) & (q + 2 < aa));
+      cnt += (o.w > sc) | ((o.w == sc) & (q + 3 < aa));
     }
-    s_sel[t] = sel;
+    s_rank[half][aa] = cnt;
+  }
+  __syncthreads();
+  if (t < 128) {
+    s_sel[t] = (t < nA && m > 0 && nB > 0) ? (s_rank[0][t] + s_rank[1][t] < m) : 0;
+    s_cnt0[t] = 0;
+    s_cnt1[t] = 0;
+    s_wsum[t] = t < nB ? s_n[2 * t + 1] : 0;
   }
   __syncthreads();
 
-  // 4. per-target source counts and weights, per-source slot, keep-mask prefix
+  // 4. source lists.  Waves 0 and 1 hold A rows 0..63 and 64..127; lanes with the same
+  //    target are found with seven ballots over the bits of the target index, which gives
+  //    each source its slot among the same-target sources of its wave (ascending A).
+  int my_pos = 0, my_b = -1;
   if (t < 128) {
-    const int b = t;
-    int cnt = 0, ws = b < nB ? s_n[2 * b + 1] : 0;
-    for (int q = 0; q < nA; ++q)
-      if (s_sel[q] && s_best[q] == b) {
-        ++cnt;
-        ws += s_n[2 * q];
-      }
-    s_cnt[b] = cnt;
-    s_wsum[b] = ws;
-  } else {
-    const int aa = t - 128;
-    int pos = 0;
-    if (s_sel[aa]) {
-      const int bb = s_best[aa];
-      for (int q = 0; q < aa; ++q) pos += (s_sel[q] && s_best[q] == bb);
+    const int aa = t;
+    const bool sa = s_sel[aa] != 0;
+    const int b = sa ? s_best[aa] : 0;
+    uint64_t eq = __ballot(sa);
+#pragma unroll
+    for (int bit = 0; bit < 7; ++bit) {
+      const uint64_t mb = __ballot(sa && ((b >> bit) & 1));
+      eq &= ((b >> bit) & 1) ? mb : ~mb;
     }
-    s_pos[aa] = pos;
+    if (sa) {
+      my_b = b;
+      my_pos = lanes_below(eq);
+      if (my_pos == 0) {
+        if (t < 64) s_cnt0[b] = __popcll(eq); else s_cnt1[b] = __popcll(eq);
+      }
+      atomicAdd(&s_wsum[b], s_n[2 * aa]);
+    }
   }
   const int keep = (t < L) && ((t & 1) || !s_sel[t >> 1]);
   const uint64_t bal = __ballot(keep);
   const int pre = lanes_below(bal);
   if ((t & 63) == 0) s_misc[1 + (t >> 6)] = __popcll(bal);
   __syncthreads();
-  if (t < 64) {  // exclusive scan of the 128 counts (2 per lane)
-    const int c0 = s_cnt[2 * t], c1 = s_cnt[2 * t + 1];
+  if (t < 64) {  // per-target counts and their exclusive scan (2 targets per lane)
+    const int c0 = s_cnt0[2 * t] + s_cnt1[2 * t], c1 = s_cnt0[2 * t + 1] + s_cnt1[2 * t + 1];
     int incl = c0 + c1;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -422,6 +441,8 @@ __global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
     const int ex = incl - c0 - c1;
     s_off[2 * t] = ex;
     s_off[2 * t + 1] = ex + c0;
+    s_cnt[2 * t] = c0;
+    s_cnt[2 * t + 1] = c1;
   }
   {
     int off = 0;
@@ -429,7 +450,17 @@ __global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
     if (keep) s_outrow[off + pre] = t;
   }
   __syncthreads();
-  if (t < 128 && s_sel[t]) s_list[s_off[s_best[t]] + s_pos[t]] = t;
+  if (my_b >= 0) s_list[s_off[my_b] + (t >= 64 ? s_cnt0[my_b] : 0) + my_pos] = t;
+  {  // output slots that hold a merged target, compacted per wave
+    bool mg = false;
+    if (t < nout) {
+      const int r = s_outrow[t];
+      mg = (r & 1) && s_cnt[r >> 1] > 0;
+    }
+    const uint64_t mb = __ballot(mg);
+    if (mg) s_mrg[t >> 6][lanes_below(mb)] = t;
+    if ((t & 63) == 0) s_mcnt[t >> 6] = __popcll(mb);
+  }
   if (a.in_place && t == 0) {
     // destination rows [base, base + nout) overlap the sources of chunks lo..j
     const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
@@ -447,6 +478,8 @@ __global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
   // 5. write K (merged rows averaged in fp32), then V through the same LDS tile, then N
   char *Kdst = a.Kout + (z * a.cap_out + base) * (int64_t)ROWB;
   char *Vdst = a.Vout + (z * a.cap_out + base) * (int64_t)ROWB;
+  const int m0 = s_mcnt[0], m1 = s_mcnt[1], m2 = s_mcnt[2], m3 = s_mcnt[3];
+  const int nmerged = m0 + m1 + m2 + m3;
   for (int pass = 0; pass < 2; ++pass) {
     char *dst = pass == 0 ? Kdst : Vdst;
     if (pass == 1) {
@@ -456,33 +489,40 @@ __global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
         *reinterpret_cast<u32x4 *>(tile + lds_swz(r0 + RPI * i, sg, ROWB)) = vreg[i];
       __syncthreads();
     }
+    // rows that are not merge targets move unchanged
 #pragma unroll 4
     for (int i = 0; i < NLD; ++i) {
       const int p = r0 + RPI * i;
       if (p >= nout) break;
       const int r = s_outrow[p];
-      u32x4 val = *reinterpret_cast<const u32x4 *>(tile + lds_swz(r, sg, ROWB));
+      if ((r & 1) && s_cnt[r >> 1] > 0) continue;
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(tile + lds_swz(r, sg, ROWB)),
+                                  reinterpret_cast<u32x4 *>(dst + (int64_t)p * ROWB + sg * 16));
+    }
+    // merge targets: (N_b x_b + sum N_a x_a) * (1 / W), fp32, sources in ascending A order
+    for (int idx = r0; idx < nmerged; idx += RPI) {
+      const int wv = idx < m0 ? 0 : idx < m0 + m1 ? 1 : idx < m0 + m1 + m2 ? 2 : 3;
+      const int p = s_mrg[wv][idx - (wv > 0 ? m0 : 0) - (wv > 1 ? m1 : 0) - (wv > 2 ? m2 : 0)];
+      const int r = s_outrow[p];
       const int b = r >> 1;
-      if ((r & 1) && s_cnt[b] > 0) {
-        float accv[EPS], tmp[EPS];
-        seg_unpack(val, tmp, tsel);
-        const float nb = (float)s_n[r];
+      float accv[EPS], tmp[EPS];
+      seg_unpack(*reinterpret_cast<const u32x4 *>(tile + lds_swz(r, sg, ROWB)), tmp, tsel);
+      const float nb = (float)s_n[r];
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) accv[e] = nb * tmp[e];
-        const int q0 = s_off[b], q1 = q0 + s_cnt[b];
-        for (int q = q0; q < q1; ++q) {
-          const int ar = 2 * s_list[q];
-          const float w8 = (float)s_n[ar];
-          seg_unpack(*reinterpret_cast<const u32x4 *>(tile + lds_swz(ar, sg, ROWB)), tmp, tsel);
+      for (int e = 0; e < EPS; ++e) accv[e] = nb * tmp[e];
+      const int q0 = s_off[b], q1 = q0 + s_cnt[b];
+      for (int q = q0; q < q1; ++q) {
+        const int ar = 2 * s_list[q];
+        const float wa = (float)s_n[ar];
+        seg_unpack(*reinterpret_cast<const u32x4 *>(tile + lds_swz(ar, sg, ROWB)), tmp, tsel);
 #pragma unroll
-          for (int e = 0; e < EPS; ++e) accv[e] = fmaf(w8, tmp[e], accv[e]);
-        }
-        const float W = (float)s_wsum[b];
-#pragma unroll
-        for (int e = 0; e < EPS; ++e) accv[e] = accv[e] / W;
-        val = seg_pack(accv, tsel);
+        for (int e = 0; e < EPS; ++e) accv[e] = fmaf(wa, tmp[e], accv[e]);
       }
-      st16(dst + (int64_t)p * ROWB + sg * 16, val);
+      const float inv = 1.0f / (float)s_wsum[b];
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) accv[e] *= inv;
+      __builtin_nontemporal_store(seg_pack(accv, tsel),
+                                  reinterpret_cast<u32x4 *>(dst + (int64_t)p * ROWB + sg * 16));
     }
   }
   if (t < nout) {
@@ -492,8 +532,10 @@ __global__ void __launch_bounds__(256) csm_round(CsmArgs a) {
   }
 }
 
-template __global__ void csm_round<__bf16>(CsmArgs);
-template __global__ void csm_round<float>(CsmArgs);
+// bf16: 72 KB of LDS per workgroup, two workgroups (two waves per SIMD) per CU.
+__global__ void __launch_bounds__(256, 2) csm_round_bf16(CsmArgs a) { csm_round_body<__bf16>(a); }
+// fp32: the 128 KB key tile allows one workgroup per CU.
+__global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) { csm_round_body<float>(a); }
 
 // Host-side launcher used by the C ABI.  Returns 0 or a hipError_t value.
 int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream) {
@@ -504,9 +546,9 @@ int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream) {
   if (e != hipSuccess) return (int)e;
   if (total == 0) return 0;
   if (dtype_f32)
-    hipLaunchKernelGGL(csm_round<float>, dim3((uint32_t)total), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(csm_round_f32, dim3((uint32_t)total), dim3(256), 0, stream, args);
   else
-    hipLaunchKernelGGL(csm_round<__bf16>, dim3((uint32_t)total), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(csm_round_bf16, dim3((uint32_t)total), dim3(256), 0, stream, args);
   e = hipGetLastError();
   return (int)e;
 }

@@ -138,7 +138,7 @@ DecLayout dec_layout(const csmkv_cache *c, int G) {
   L.item_off = kAlign;
   L.part = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
   const int64_t items = csmkv::dec_max_items(c->num_slices, c->max_len);
-  L.total = L.part + align_up((size_t)items * G * (2 + kHeadDim) * 4);
+  L.total = L.part + align_up((size_t)items * G * (4 + kHeadDim) * 4);
   return L;
 }
 

@@ -12,8 +12,9 @@
 //                 sub-block, q.k by packed bf16 dot products, a 16-lane DPP reduction,
 //                 base-2 online softmax (log2 N added, log2 e folded into the scale),
 //                 P.V accumulated in fp32.  Waves merge in LDS; each item writes one
-//                 (max, sum, o[128]) partial per head.
-//   dec_combine : one workgroup per slice merges the item partials by log-sum-exp.
+//                 (max, sum, 0, 0, o[128]) partial per head.
+//   dec_combine : one workgroup per slice merges the item partials by log-sum-exp
+//                 (max first, then rescaled sums over item groups in parallel).
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -22,6 +23,7 @@
 namespace csmkv {
 
 constexpr int kTSplit = 512;        // tokens per work item
+constexpr int kPartWidth = 4 + kHeadDim;  // floats per (item, head) partial: 16-byte rows
 constexpr int kDecThreads = 256;
 
 
@@ -107,7 +109,7 @@ template <typename T, int G>
 __global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
   using DT = DecTile<T>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
-  constexpr int PW = 2 + kHeadDim;  // partial width per head
+  constexpr int PW = kPartWidth;  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][G][PW];
   __shared__ int32_t s_item[2];
   T *tsel = nullptr;
@@ -215,7 +217,7 @@ __global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
           s_part[w][h][1] = lrun[h];
         }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_part[w][h][2 + sg * EPL + e] = o[h][e];
+        for (int e = 0; e < EPL; ++e) s_part[w][h][4 + sg * EPL + e] = o[h][e];
       }
     }
     __syncthreads();
@@ -228,6 +230,8 @@ __global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
       float v = 0.f;
       if (k == 0) {
         v = M;
+      } else if (k == 2 || k == 3) {
+        v = 0.f;
       } else {
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
@@ -241,28 +245,56 @@ __global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
   }
 }
 
+// One workgroup per slice.  For each head: block-wide max of the item maxima, then 8 item
+// groups of 32 lanes (4 output elements per lane) accumulate the rescaled partials with
+// independent loads, and the groups are summed through LDS.
 template <int G>
-__global__ void __launch_bounds__(128) dec_combine(DecArgs a) {
-  constexpr int PW = 2 + kHeadDim;
+__global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
+  constexpr int PW = kPartWidth;
+  __shared__ float s_red[8];
+  __shared__ float s_acc[8][kHeadDim];
+  __shared__ float s_l[8];
   const int64_t z = blockIdx.x;
-  const int e = threadIdx.x;
+  const int t = threadIdx.x, grp = t >> 5, e4 = (t & 31) * 4;
   const int i0 = a.item_off[z], i1 = a.item_off[z + 1];
   const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
   const float NEG_INF = -__builtin_inff();
-#pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = NEG_INF, L = 0.f, acc = 0.f;
-    for (int it = i0; it < i1; ++it) {
+    float M = NEG_INF;
+    for (int it = i0 + t; it < i1; it += 256) M = fmaxf(M, a.part[((int64_t)it * G + h) * PW]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if ((t & 63) == 0) s_red[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
+    for (int it = i0 + grp; it < i1; it += 8) {
       const float *pp = a.part + ((int64_t)it * G + h) * PW;
       const float m = pp[0];
-      if (m == NEG_INF) continue;
-      const float mn = fmaxf(M, m);
-      const float sa = __builtin_amdgcn_exp2f(M - mn), sb = __builtin_amdgcn_exp2f(m - mn);
-      L = L * sa + pp[1] * sb;
-      acc = acc * sa + pp[2 + e] * sb;
-      M = mn;
+      const float wgt = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      const float4 o = *reinterpret_cast<const float4 *>(pp + 4 + e4);
+      L = fmaf(wgt, pp[1], L);
+      acc0 = fmaf(wgt, o.x, acc0);
+      acc1 = fmaf(wgt, o.y, acc1);
+      acc2 = fmaf(wgt, o.z, acc2);
+      acc3 = fmaf(wgt, o.w, acc3);
     }
-    a.O[(g * a.H_q + kvh * G + h) * (int64_t)kHeadDim + e] = L > 0.f ? acc / L : 0.f;
+    s_acc[grp][e4] = acc0;
+    s_acc[grp][e4 + 1] = acc1;
+    s_acc[grp][e4 + 2] = acc2;
+    s_acc[grp][e4 + 3] = acc3;
+    if ((t & 31) == 0) s_l[grp] = L;
+    __syncthreads();
+    if (t < kHeadDim) {
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        num += s_acc[q][t];
+        den += s_l[q];
+      }
+      a.O[(g * a.H_q + kvh * G + h) * (int64_t)kHeadDim + t] = den > 0.f ? num / den : 0.f;
+    }
+    __syncthreads();
   }
 }
 
@@ -291,10 +323,10 @@ int launch_decode(const DecArgs &a, int dtype_f32, int G, int64_t max_items, hip
   if (rc) return rc;
   const dim3 cg((uint32_t)a.num_slices);
   switch (G) {
-    case 1: hipLaunchKernelGGL(dec_combine<1>, cg, dim3(128), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(dec_combine<2>, cg, dim3(128), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(dec_combine<4>, cg, dim3(128), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(dec_combine<8>, cg, dim3(128), 0, st, a); break;
+    case 1: hipLaunchKernelGGL(dec_combine<1>, cg, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(dec_combine<2>, cg, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(dec_combine<4>, cg, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(dec_combine<8>, cg, dim3(256), 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

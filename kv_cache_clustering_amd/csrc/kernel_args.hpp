@@ -38,7 +38,7 @@ struct DecArgs {
   float scale_log2;   // log2(e) / sqrt(d)
   int32_t *err;       // device error word of this call
   int32_t *item_off;  // [num_slices + 1] first work item of each slice
-  float *part;        // [items][G][2 + d] (max, sum, o) partials
+  float *part;        // [items][G][4 + d] (max, sum, 0, 0, o) partials
 };
 
 struct AppArgs {

@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "CSM compress tokens/s + log-N decode-attn HBM GB/s (% of peak), 64K ctx"
 PEAK_GBPS = 8000.0
 ROW_BYTES = 128 * 2 * 2 + 4  # K + V (bf16, d = 128) + int32 degree
+CSM_SOURCES = ["csm_kernel.hip", "device_common.hpp", "kernel_args.hpp"]
+DEC_SOURCES = ["decode_kernel.hip", "device_common.hpp", "kernel_args.hpp"]
 
 
 def parse():
@@ -41,6 +43,25 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     return ap.parse_args()
+
+
+COUNTER_RECORD = os.path.join(ROOT, "profiles", "csm_decode_64k_hbm_counters.md")
+CSRC = os.path.join(ROOT, "kv_cache_clustering_amd", "csrc")
+
+
+def recorded_traffic(key, sources):
+    """HBM bytes per launch from the recorded FETCH_SIZE / WRITE_SIZE passes (copy-calibrated),
+    or None when the record is missing or the kernel sources changed since it was taken."""
+    import hashlib
+    try:
+        text = open(COUNTER_RECORD).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])[key]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
 def csm_bytes(lens_in, lens_out, mask, n1, out_of_place):
@@ -221,12 +242,14 @@ def main():
                 "in_place_ms": inplace_avg, "in_place_alg_bytes": inplace_alg,
                 "in_place_GBps": inplace_alg / (inplace_avg * 1e-3) / 1e9},
         "decode_attn": {"us": dec_avg * 1e3, "alg_bytes": dec_alg, "GBps": dec_gbps,
-                        "frac": dec_gbps / PEAK_GBPS, "layers": w.layers},
+                        "frac": dec_gbps / PEAK_GBPS, "layers": w.layers,
+                        "traffic": recorded_traffic("dec_split_bf16_g4", DEC_SOURCES)},
         "append_us": app_avg * 1e3,
         "hbm_copy_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": "csm_round<bf16> (csm_compress_into)",
                      "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": csm_gbps / PEAK_GBPS, "traffic": None},
+                     "frac": csm_gbps / PEAK_GBPS,
+                     "traffic": recorded_traffic("csm_round_bf16", CSM_SOURCES)},
         "cpu_baseline": cpu,
         "setup_s": setup_s,
     }

@@ -8,8 +8,9 @@
 //   dec_split   : persistent workgroups stride over the work items.  A work item is
 //                 TSPLIT tokens of one slice, shared by the G query heads of that KV
 //                 head, so K, V and N are read once per step.  Each wave streams a
-//                 quarter of the item: 16 B per lane per row, rows of 32 tokens per
-//                 sub-block, q.k by packed bf16 dot products, a 16-lane DPP reduction,
+//                 quarter of the item: 16 B per lane per row, sub-blocks of 16 tokens
+//                 (bf16) with the next sub-block's loads in flight while the current
+//                 one is computed, q.k by packed bf16 dot products, a 16-lane DPP reduction,
 //                 base-2 online softmax (log2 N added, log2 e folded into the scale),
 //                 P.V accumulated in fp32.  Waves merge in LDS; each item writes one
 //                 (max, sum, 0, 0, o[128]) partial per head.
@@ -22,7 +23,7 @@
 
 namespace csmkv {
 
-constexpr int kTSplit = 512;        // tokens per work item
+constexpr int kTSplit = 1024;       // tokens per work item
 constexpr int kPartWidth = 4 + kHeadDim;  // floats per (item, head) partial: 16-byte rows
 constexpr int kDecThreads = 256;
 
@@ -69,7 +70,8 @@ struct DecTile {
   static constexpr int ROWB = kHeadDim * (int)sizeof(T);
   static constexpr int LPR = ROWB / 16;     // lanes per row
   static constexpr int RPW = 64 / LPR;      // rows per wave-wide load
-  static constexpr int SUB = 8 * RPW;       // rows per sub-block
+  static constexpr int NR = 4;              // wave loads per sub-block
+  static constexpr int SUB = NR * RPW;      // rows per sub-block
   static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
 };
 
@@ -105,14 +107,86 @@ __device__ __forceinline__ void seg_to_f32(u32x4 v, float *o, float *) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One sub-block of a wave's token range held in registers: NR wave loads of K and V rows
+// (16 B per lane per row) and the degrees of the lane's rows.
+struct DecStage {
+  u32x4 k[4], v[4];
+  int32_t n[4];
+};
+
+template <typename T>
+__device__ __forceinline__ void dec_load(DecStage &st, const char *Kz, const char *Vz,
+                                         const int32_t *Nz, int sb, int we, int rw, int sg) {
+  using DT = DecTile<T>;
+#pragma unroll
+  for (int i = 0; i < DT::NR; ++i) {
+    const int tok = sb + DT::RPW * i + rw;
+    const bool ok = tok < we;
+    st.k[i] = ok ? __builtin_nontemporal_load(
+                       reinterpret_cast<const u32x4 *>(Kz + (int64_t)tok * DT::ROWB + sg * 16))
+                 : u32x4{0u, 0u, 0u, 0u};
+    st.v[i] = ok ? __builtin_nontemporal_load(
+                       reinterpret_cast<const u32x4 *>(Vz + (int64_t)tok * DT::ROWB + sg * 16))
+                 : u32x4{0u, 0u, 0u, 0u};
+    st.n[i] = ok ? Nz[tok] : 0;
+  }
+}
+
+// Online-softmax update of (mrun, lrun, o) with one sub-block, base 2.
 template <typename T, int G>
-__global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
+__device__ __forceinline__ void dec_compute(const DecStage &st, int sb, int we, int rw,
+                                            const u32x4 *qv, float scale_log2, float *mrun,
+                                            float *lrun, float (*o)[DecTile<T>::EPL]) {
+  using DT = DecTile<T>;
+  constexpr int EPL = DT::EPL;
+  T *tsel = nullptr;
+  const float NEG_INF = -__builtin_inff();
+  float zs[DT::NR][G];
+#pragma unroll
+  for (int i = 0; i < DT::NR; ++i) {
+    const bool ok = sb + DT::RPW * i + rw < we;
+    const float ln = __builtin_amdgcn_logf((float)st.n[i]);  // log2
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = row16_sum(seg_dot(st.k[i], qv[h], tsel));
+      if (DT::LPR == 32) d += __shfl_xor(d, 16);
+      zs[i][h] = ok ? fmaf(d, scale_log2, ln) : NEG_INF;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = zs[0][h];
+#pragma unroll
+    for (int i = 1; i < DT::NR; ++i) mx = fmaxf(mx, zs[i][h]);
+    if (DT::RPW == 4) mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(mrun[h], mx);
+    const float alpha = fast_exp2(mrun[h] - mn);
+    mrun[h] = mn;
+    lrun[h] *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+  }
+#pragma unroll
+  for (int i = 0; i < DT::NR; ++i) {
+    float vf[EPL];
+    seg_to_f32(st.v[i], vf, tsel);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = fast_exp2(zs[i][h] - mrun[h]);
+      lrun[h] += pr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vf[e], o[h][e]);
+    }
+  }
+}
+
+template <typename T, int G>
+__global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
   using DT = DecTile<T>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
   constexpr int PW = kPartWidth;  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][G][PW];
-  __shared__ int32_t s_item[2];
-  T *tsel = nullptr;
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int sg = l % LPR, rw = l / LPR;
   const int64_t S = a.num_slices;
@@ -130,16 +204,19 @@ __global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
     const int p = item - a.item_off[z];
     const int tok0 = p * kTSplit, tok1 = min(s, tok0 + kTSplit);
     const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
+    const char *Kz = a.K + z * a.cap * ROWB;
+    const char *Vz = a.V + z * a.cap * ROWB;
+    const int32_t *Nz = a.N + z * a.cap;
+    const int wq = kTSplit / 4;
+    const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
+    // two register stages: the next sub-block loads while the current one is computed
+    DecStage A, B;
+    if (wb < we) dec_load<T>(A, Kz, Vz, Nz, wb, we, rw, sg);
     // this lane's q segment for each head of the group
     u32x4 qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h)
       qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + h) * (int64_t)kHeadDim) * sizeof(T) + sg * 16);
-    const char *Kz = a.K + z * a.cap * ROWB;
-    const char *Vz = a.V + z * a.cap * ROWB;
-    const int32_t *Nz = a.N + z * a.cap;
-    const int wq = (kTSplit / 4);
-    const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
     float mrun[G], lrun[G], o[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -148,55 +225,13 @@ __global__ void __launch_bounds__(kDecThreads) dec_split(DecArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
     }
-    for (int sb = wb; sb < we; sb += SUB) {
-      u32x4 kr[8], vr[8];
-      int32_t nv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = sb + RPW * i + rw;
-        const bool ok = tok < we;
-        kr[i] = ok ? ld16(Kz + (int64_t)tok * ROWB + sg * 16) : u32x4{0u, 0u, 0u, 0u};
-        vr[i] = ok ? ld16(Vz + (int64_t)tok * ROWB + sg * 16) : u32x4{0u, 0u, 0u, 0u};
-        nv[i] = ok ? Nz[tok] : 0;
-      }
-      float zs[8][G];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool ok = sb + RPW * i + rw < we;
-        const float ln = __builtin_amdgcn_logf((float)nv[i]);  // log2
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float d = row16_sum(seg_dot(kr[i], qv[h], tsel));
-          if (LPR == 32) d += __shfl_xor(d, 16);
-          zs[i][h] = ok ? fmaf(d, a.scale_log2, ln) : NEG_INF;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mx = zs[0][h];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, zs[i][h]);
-        if (RPW == 4) mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(mrun[h], mx);
-        const float alpha = fast_exp2(mrun[h] - mn);
-        mrun[h] = mn;
-        lrun[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float vf[EPL];
-        seg_to_f32(vr[i], vf, tsel);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pr = fast_exp2(zs[i][h] - mrun[h]);
-          lrun[h] += pr;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vf[e], o[h][e]);
-        }
-      }
+    for (int sb = wb; sb < we; sb += 2 * SUB) {
+      const int sb1 = sb + SUB;
+      if (sb1 < we) dec_load<T>(B, Kz, Vz, Nz, sb1, we, rw, sg);
+      dec_compute<T, G>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
+      if (sb1 >= we) break;
+      if (sb1 + SUB < we) dec_load<T>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
+      dec_compute<T, G>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
     }
     // sum the row groups of the wave (they hold different tokens, same segment)
 #pragma unroll

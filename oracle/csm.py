@@ -26,8 +26,9 @@ Readings taken where the pages are silent (each also listed in the design doc):
   * Outlier (masked) slices are left untouched.
 
 Decision precision: ``precision='f64'`` scores in fp64 (the definition); ``'f32'``
-scores in binary32 (dot products, norms, the product of norms and the division each
-rounded to fp32), which is the precision a GPU kernel decides in.
+scores in binary32 (dot products and norms rounded to fp32, then the dot product scaled
+by the two rounded reciprocal norms), which is the precision and form a GPU kernel
+decides in.
 
 Pins (tests/oracle/): Theorem 6.1 brute force for the partition; argmax / ranking
 properties on every chunk; r = 0 identity; sum of N conserved; first moments
@@ -69,7 +70,13 @@ def partition(L):
 
 
 def cosine_matrix(Ka, Kb, precision="f64"):
-    """S[i, j] = <a_i, b_j> / (max(|a_i|, eps) * max(|b_j|, eps)) in the given precision."""
+    """Cosine similarity S[i, j] of rows a_i and b_j, norms floored at eps.
+
+    'f64': <a_i, b_j> / (max(|a_i|, eps) * max(|b_j|, eps)), the definition.
+    'f32': binary32 throughout, evaluated as (<a_i, b_j> * (1 / max(|b_j|, eps))) *
+    (1 / max(|a_i|, eps)) with each reciprocal rounded once: the form the GPU kernel
+    decides with, so that both sides take the same decision up to summation order.
+    """
     dt = {"f64": np.float64, "f32": np.float32}[precision]
     a = np.asarray(Ka).astype(dt)
     b = np.asarray(Kb).astype(dt)
@@ -77,8 +84,12 @@ def cosine_matrix(Ka, Kb, precision="f64"):
     na = np.sqrt(np.sum(a * a, axis=1, dtype=dt))
     nb = np.sqrt(np.sum(b * b, axis=1, dtype=dt))
     floor = dt(NORM_FLOOR)
-    den = np.maximum(na, floor)[:, None] * np.maximum(nb, floor)[None, :]
-    return (dots / den).astype(dt)
+    if precision == "f64":
+        den = np.maximum(na, floor)[:, None] * np.maximum(nb, floor)[None, :]
+        return dots / den
+    inv_a = dt(1) / np.maximum(na, floor)
+    inv_b = dt(1) / np.maximum(nb, floor)
+    return ((dots * inv_b[None, :]) * inv_a[:, None]).astype(dt)
 
 
 def match(S):

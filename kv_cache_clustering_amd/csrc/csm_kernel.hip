@@ -29,18 +29,20 @@
 //   keys -> LDS tile (swizzled rows), fp32 norms from the same registers;
 //   S^T = B_keys . A_keys^T on MFMA (bf16: v_mfma_f32_32x32x16_bf16, fp32:
 //   v_mfma_f32_32x32x2_f32), wave w owning A columns [32w, 32w+32) and all B rows;
-//   cosine = dot / (max(|a|,1e-12) * max(|b|,1e-12)) in fp32, arg-max per A column
-//   inside each lane then across the two half-waves (lowest B index on ties);
+//   cosine = (dot * fl(1/max(|b|,1e-12))) * fl(1/max(|a|,1e-12)) in fp32 (reciprocal norms
+//   computed once per row at load time), branch-free arg-max per A column inside each
+//   lane then across the two half-waves (lowest B index on ties);
 //   rank of every A edge by (score desc, index asc) through a 128-way comparison count
 //   split over all four waves;
 //   per-target source lists in ascending A order: same-target lanes found with seven
 //   ballots over the target index bits, slots by mbcnt, counts scanned across targets;
 //   keep-mask prefix sum (ballot + mbcnt) gives each kept row its output slot;
 //   rows that are not merge targets are copied in one pass; merge targets, compacted into
-//   a list, are computed as (N_b k_b + sum N_a k_a) * (1 / (N_b + sum N_a)) in fp32 and
+//   a list, are computed as (N_b k_b + sum N_a k_a) * rcp(N_b + sum N_a) in fp32 and
 //   stored RNE (v_cvt_pk_bf16_f32); stores are non-temporal (the output is not re-read).
 #include <algorithm>
 
+#include "csm_common.hpp"
 #include "device_common.hpp"
 #include "kernel_args.hpp"
 
@@ -76,143 +78,6 @@ __global__ void csm_prep(CsmArgs a) {
          i += (int64_t)(gridDim.x - 1) * blockDim.x)
       a.flags[i] = 0;
   }
-}
-
-template <typename T>
-struct Tile {
-  static constexpr int ROWB = kHeadDim * (int)sizeof(T);  // bytes per row
-  static constexpr int SEGS = ROWB / 16;                  // 16-byte segments per row
-  static constexpr int RPI = 256 / SEGS;                  // rows covered by one block-wide load
-  static constexpr int NLD = kMaxChunk / RPI;             // loads per thread for 256 rows
-  static constexpr int EPS = 16 / (int)sizeof(T);         // elements per segment
-};
-
-// Sum of squares of one 16-byte segment (fp32; bf16 squares are exact in fp32).
-__device__ __forceinline__ float seg_sumsq(u32x4 v, __bf16 *) {
-  float s = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float lo = bf_lo(v[q]), hi = bf_hi(v[q]);
-    s = fmaf(lo, lo, s);
-    s = fmaf(hi, hi, s);
-  }
-  return s;
-}
-__device__ __forceinline__ float seg_sumsq(u32x4 v, float *) {
-  float s = 0.f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float x = __uint_as_float(v[q]);
-    s = fmaf(x, x, s);
-  }
-  return s;
-}
-
-// Unpack a segment to fp32 / pack fp32 back to the storage type.
-__device__ __forceinline__ void seg_unpack(u32x4 v, float *o, __bf16 *) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    o[2 * q] = bf_lo(v[q]);
-    o[2 * q + 1] = bf_hi(v[q]);
-  }
-}
-__device__ __forceinline__ void seg_unpack(u32x4 v, float *o, float *) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = __uint_as_float(v[q]);
-}
-__device__ __forceinline__ u32x4 seg_pack(const float *o, __bf16 *) {
-  u32x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {  // v_cvt_pk_bf16_f32: round to nearest even
-    const bf16x2 h = {(__bf16)o[2 * q], (__bf16)o[2 * q + 1]};
-    v[q] = __builtin_bit_cast(uint32_t, h);
-  }
-  return v;
-}
-__device__ __forceinline__ u32x4 seg_pack(const float *o, float *) {
-  u32x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = __float_as_uint(o[q]);
-  return v;
-}
-
-// S^T tile for one wave: acc[tile][i] = <key of B row (tile*32 + row_i), key of A row a>.
-__device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
-                                         __bf16 *) {
-  constexpr int ROWB = Tile<__bf16>::ROWB;
-#pragma unroll
-  for (int kk = 0; kk < kHeadDim / 16; ++kk) {
-    const int seg = 2 * kk + h;
-    u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
-    bf16x8 bop = __builtin_bit_cast(bf16x8, braw);
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      const int brow = 2 * (tl * 32 + col) + 1;
-      u32x4 araw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(brow, seg, ROWB));
-      bf16x8 aop = __builtin_bit_cast(bf16x8, araw);
-      acc[tl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc[tl], 0, 0, 0);
-    }
-  }
-}
-__device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
-                                         float *) {
-  constexpr int ROWB = Tile<float>::ROWB;
-  // Half-wave h supplies elements 8q + 4h + i at k-step 4q + i: every element is used
-  // once and both operands use the same assignment.
-#pragma unroll 2
-  for (int q = 0; q < kHeadDim / 8; ++q) {
-    const int seg = 2 * q + h;
-    u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
-#pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
-      const int brow = 2 * (tl * 32 + col) + 1;
-      u32x4 araw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(brow, seg, ROWB));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[tl] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(araw[i]),
-                                                       __uint_as_float(braw[i]), acc[tl], 0, 0, 0);
-    }
-  }
-}
-
-// Copy `nrows` rows (K, V, N) from src to dst in ascending blocks of 256 rows.  Each block
-// is fully read before any of it is written, so dst <= src (a shift to lower rows) is safe
-// in place.
-template <typename T>
-__device__ void copy_rows(const char *Ks, const char *Vs, const int32_t *Ns, char *Kd, char *Vd,
-                          int32_t *Nd, int nrows) {
-  using TL = Tile<T>;
-  const int t = threadIdx.x, sg = t % TL::SEGS, r0 = t / TL::SEGS;
-  for (int blk = 0; blk < nrows; blk += kMaxChunk) {
-    const int nb = min(kMaxChunk, nrows - blk);
-    u32x4 kb[TL::NLD], vb[TL::NLD];
-#pragma unroll
-    for (int i = 0; i < TL::NLD; ++i) {
-      const int r = r0 + TL::RPI * i;
-      if (r < nb) {
-        kb[i] = ld16(Ks + (int64_t)(blk + r) * TL::ROWB + sg * 16);
-        vb[i] = ld16(Vs + (int64_t)(blk + r) * TL::ROWB + sg * 16);
-      }
-    }
-    int32_t nv = t < nb ? Ns[blk + t] : 0;
-    wait_vm_loads();
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TL::NLD; ++i) {
-      const int r = r0 + TL::RPI * i;
-      if (r < nb) {
-        st16(Kd + (int64_t)(blk + r) * TL::ROWB + sg * 16, kb[i]);
-        st16(Vd + (int64_t)(blk + r) * TL::ROWB + sg * 16, vb[i]);
-      }
-    }
-    if (t < nb) Nd[blk + t] = nv;
-    __syncthreads();
-  }
-}
-
-__device__ __forceinline__ void wait_flag(const int32_t *f) {
-  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
-    __builtin_amdgcn_s_sleep(2);
 }
 
 template <typename T>
@@ -258,7 +123,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   using TL = Tile<T>;
   constexpr int ROWB = TL::ROWB, SEGS = TL::SEGS, RPI = TL::RPI, NLD = TL::NLD, EPS = TL::EPS;
   __shared__ __attribute__((aligned(16))) char tile[kMaxChunk * ROWB];
-  __shared__ float s_norm[kMaxChunk];
+  __shared__ __attribute__((aligned(16))) float s_invA[128], s_invB[128];  // 1 / max(|k|, eps)
   __shared__ int32_t s_n[kMaxChunk];
   __shared__ int32_t s_outrow[kMaxChunk];
   __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_list[128];
@@ -304,34 +169,41 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   const char *Vsrc = a.Vin + (z * a.cap_in + start) * (int64_t)ROWB;
   const int sg = t % SEGS, r0 = t / SEGS;
 
-  // 1. load the chunk: K -> LDS (+ norms), V -> registers, N -> LDS
+  // 1. load the chunk: keys first, then degrees, then values.  The load counter retires in
+  //    order, so the key tile (+ norms) is written as soon as the keys land while the
+  //    values are still in flight; they are only needed for the output.
   u32x4 vreg[NLD];
   {
     u32x4 kreg[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = r0 + RPI * i;
-      kreg[i] = u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (r < L) {
-        kreg[i] = ld16(Ksrc + (int64_t)r * ROWB + sg * 16);
-        vreg[i] = ld16(Vsrc + (int64_t)r * ROWB + sg * 16);
-      }
+      kreg[i] = r < L ? __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4 *>(Ksrc + (int64_t)r * ROWB + sg * 16))
+                      : u32x4{0u, 0u, 0u, 0u};
     }
-    if (t < L) s_n[t] = a.Nin[z * a.cap_in + start + t];
+    const int32_t nval = t < L ? a.Nin[z * a.cap_in + start + t] : 0;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int r = r0 + RPI * i;
+      vreg[i] = r < L ? __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x4 *>(Vsrc + (int64_t)r * ROWB + sg * 16))
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = r0 + RPI * i;
       *reinterpret_cast<u32x4 *>(tile + lds_swz(r, sg, ROWB)) = kreg[i];
       float ss = row16_sum(seg_sumsq(kreg[i], tsel));
       if (SEGS == 32) ss += __shfl_xor(ss, 16);
-      if (sg == 0) s_norm[r] = sqrtf(ss);
+      if (sg == 0) {
+        const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+        if (r & 1) s_invB[r >> 1] = inv; else s_invA[r >> 1] = inv;
+      }
     }
+    if (t < L) s_n[t] = nval;
   }
-  wait_vm_loads();
   __syncthreads();
-  if (a.in_place && t == 0)
-    __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 2. similarity tile on MFMA and arg-max over B for every A column
   if (!copy_only && nB > 0) {
@@ -342,22 +214,25 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     for (int tl = 0; tl < 4; ++tl)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tl][q] = 0.f;
-    sim_tile(tile, aidx, col, h, acc, tsel);
-    const float na = fmaxf(s_norm[2 * aidx], 1e-12f);
+    sim_tile<4>(tile, aidx, col, h, acc, tsel);
+    // cosine = (dot * (1/|b|)) * (1/|a|); lowest B index wins a tie (ascending order, strict >)
+    const float ia = s_invA[aidx];
     float best = -__builtin_inff();
     int bidx = 0x7fffffff;
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int bb = tl * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-        if (bb < nB) {
-          const float den = na * fmaxf(s_norm[2 * bb + 1], 1e-12f);
-          const float sc = acc[tl][q] / den;
-          if (sc > best) {
-            best = sc;
-            bidx = bb;
-          }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int b0 = tl * 32 + 8 * g4 + 4 * h;
+        const float4 ib = *reinterpret_cast<const float4 *>(&s_invB[b0]);
+        const float ibv[4] = {ib.x, ib.y, ib.z, ib.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sc = (acc[tl][4 * g4 + i] * ibv[i]) * ia;
+          sc = (b0 + i < nB) ? sc : -__builtin_inff();
+          const bool up = sc > best;
+          best = up ? sc : best;
+          bidx = up ? b0 + i : bidx;
         }
       }
     }
@@ -375,7 +250,11 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     s_best[t] = -1;
     s_score[t] = -__builtin_inff();
   }
+  // in place: every load of this chunk has landed before its "source consumed" flag rises
+  if (a.in_place) wait_vm_loads();
   __syncthreads();
+  if (a.in_place && t == 0)
+    __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 3. top-m selection: rank of each A edge by (score desc, index asc).  Every thread
   //    counts the higher-ranked edges among one half of the 128 candidates.
@@ -518,7 +397,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
 #pragma unroll
         for (int e = 0; e < EPS; ++e) accv[e] = fmaf(wa, tmp[e], accv[e]);
       }
-      const float inv = 1.0f / (float)s_wsum[b];
+      const float inv = __builtin_amdgcn_rcpf((float)s_wsum[b]);  // v_rcp_f32, 1 ulp
 #pragma unroll
       for (int e = 0; e < EPS; ++e) accv[e] *= inv;
       __builtin_nontemporal_store(seg_pack(accv, tsel),

@@ -118,6 +118,14 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   if (t == 0) a.lens_out[z] = s_new;
 }
 
+// Unique 64-bit key ordering A edges by descending score, then ascending index: the score's
+// bits mapped to an order-preserving unsigned integer (-0 folded into +0), then 255 - a.
+__device__ __forceinline__ uint64_t rank_key(float score, int aidx) {
+  const uint32_t u = __float_as_uint(score + 0.0f);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 8) | (uint64_t)(255 - aidx);
+}
+
 template <typename T>
 __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   using TL = Tile<T>;
@@ -129,7 +137,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_list[128];
   __shared__ int32_t s_cnt0[128], s_cnt1[128], s_rank[2][128];
   __shared__ int32_t s_mrg[4][64], s_mcnt[4];
-  __shared__ __attribute__((aligned(16))) float s_score[128];
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[128];  // rank keys, 0 = no edge
   __shared__ int32_t s_misc[8];
 
   const int t = threadIdx.x;
@@ -244,11 +252,11 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     }
     if (h == 0) {
       s_best[aidx] = aidx < nA ? bidx : -1;
-      s_score[aidx] = aidx < nA ? best : -__builtin_inff();
+      s_key[aidx] = aidx < nA ? rank_key(best, aidx) : 0ull;
     }
   } else if (t < 128) {
     s_best[t] = -1;
-    s_score[t] = -__builtin_inff();
+    s_key[t] = 0ull;
   }
   // in place: every load of this chunk has landed before its "source consumed" flag rises
   if (a.in_place) wait_vm_loads();
@@ -256,19 +264,16 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   if (a.in_place && t == 0)
     __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // 3. top-m selection: rank of each A edge by (score desc, index asc).  Every thread
-  //    counts the higher-ranked edges among one half of the 128 candidates.
+  // 3. top-m selection: rank of each A edge by (score desc, index asc), i.e. the number of
+  //    larger unique keys.  Every thread counts over one half of the 128 candidates.
   {
     const int aa = t & 127, half = t >> 7;
-    const float sc = s_score[aa];
+    const uint64_t my = s_key[aa];
     int cnt = 0;
-#pragma unroll 4
-    for (int q = half * 64; q < half * 64 + 64; q += 4) {
-      const float4 o = *reinterpret_cast<const float4 *>(&s_score[q]);
-      cnt += (o.x > sc) | ((o.x == sc) & (q < aa));
-      cnt += (o.y > sc) | ((o.y == sc) & (q + 1 < aa));
-      cnt += (o.z > sc) | ((o.z == sc) & (q + 2 < aa));
-      cnt += (o.w > sc) | ((o.w == sc) & (q + 3 < aa));
+#pragma unroll 8
+    for (int q = half * 64; q < half * 64 + 64; q += 2) {
+      const uint64_t k0 = s_key[q], k1 = s_key[q + 1];
+      cnt += (k0 > my) + (k1 > my);
     }
     s_rank[half][aa] = cnt;
   }

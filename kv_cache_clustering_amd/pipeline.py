@@ -1,0 +1,99 @@
+"""Algorithm 1 runtime: a clustered K/V cache driven through prefill rounds and decode steps.
+
+Chelsea review, section 三, Algorithm 1: after prefill, cluster while s >= B + g (budget
+B = R * (n + Gamma)); each decode step appends k, v with degree 1, attends with
+O = Softmax(q K^T / sqrt(d) + log N) V, and clusters when s >= B + g.  CentroidKV page,
+渐进式调度: r is annealed over rounds.
+
+Every length is known on the host in closed form (schedule.Algorithm1), so driving the
+device needs no read-back: the whole loop is a sequence of asynchronous library calls on
+the current stream.  All sequences of a batch share one prefill length and therefore one
+schedule; slices flagged outlier are never clustered and keep growing.
+"""
+
+import torch
+
+from . import _lib as lib
+from .schedule import Algorithm1
+
+
+class ClusteredKVCache:
+    """K, V: [S, cap, d] (S = batch * layers * H_kv); N: [S, cap] int32; lens: [S] int32.
+
+    The tensors are used in place.  `n` is the common prefill length of every slice.
+    """
+
+    def __init__(self, K, V, N, lens, *, H_q, H_kv, n, R, Gamma, g=32, n1=16, n2=64, c=256,
+                 r_init=0.5, delta=0.05, r_min=0.1, outlier_mask=None, observer=None):
+        """observer: optional object with before_round(cache, r) and
+        after_round(cache, r, best_b, selected, src_pos); rounds then record their decisions
+        (csm_compress_debug, same kernel)."""
+        self.K, self.V, self.N, self.lens = K, V, N, lens
+        self.observer = observer
+        self.H_q, self.H_kv = H_q, H_kv
+        self.n1, self.n2, self.c = n1, n2, c
+        self.mask = outlier_mask
+        self.has_outliers = outlier_mask is not None and bool(outlier_mask.any())
+        self.sched = Algorithm1(n=n, R=R, Gamma=Gamma, g=g, n1=n1, n2=n2, c=c, r_init=r_init,
+                                delta=delta, r_min=r_min)
+        self.step_index = 0
+        self.outlier_len = n
+        dev = K.device
+        cap = K.shape[1]
+        self.ws_csm = torch.empty(lib.csm_workspace_bytes(K, n1, n2, c, max_len=cap),
+                                  dtype=torch.uint8, device=dev)
+        self.ws_dec = torch.empty(lib.decode_workspace_bytes(K, H_q, H_kv, max_len=cap),
+                                  dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        groups = K.shape[0] // H_kv
+        self.out = torch.empty((groups, H_q, K.shape[2]), dtype=torch.float32, device=dev)
+
+    @property
+    def max_len(self):
+        """Host-known bound on every slice length."""
+        return max(self.sched.s, self.outlier_len if self.has_outliers else 0)
+
+    def _round(self, r, s_before):
+        """One clustering round; s_before (host-known length before it) bounds the launch."""
+        max_len = max(s_before, self.outlier_len if self.has_outliers else 0)
+        if self.observer is None:
+            lib.csm_compress(self.K, self.V, self.N, self.lens, self.n1, self.n2, self.c, r,
+                             self.mask, max_len=max_len, workspace=self.ws_csm)
+            return
+        self.observer.before_round(self, r)
+        taps = lib.csm_compress_debug(self.K, self.V, self.N, self.lens, self.n1, self.n2, self.c,
+                                      r, self.mask, max_len=max_len, workspace=self.ws_csm)
+        self.observer.after_round(self, r, *taps[:3])
+
+    def prefill(self):
+        """Cluster until the cache is under budget; returns the r of every round run."""
+        rs = []
+        while self.sched.over_budget():
+            s_before = self.sched.s
+            r = self.sched.next_round(0)
+            self._round(r, s_before)
+            rs.append(r)
+        return rs
+
+    def decode_step(self, q, k_new, v_new, out=None):
+        """Append, attend, then cluster if the trigger fires.  Returns (O, r or None)."""
+        self.step_index += 1
+        lib.kv_append(self.K, self.V, self.N, self.lens, k_new, v_new, self.err)
+        self.sched.append()
+        self.outlier_len += 1
+        O = lib.decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
+                                 out=self.out if out is None else out, max_len=self.max_len,
+                                 workspace=self.ws_dec)
+        r = None
+        if self.sched.over_budget():
+            s_before = self.sched.s
+            r = self.sched.next_round(self.step_index)
+            self._round(r, s_before)
+        return O, r
+
+    def check_errors(self):
+        """Synchronise and raise if a kernel flagged a bad length."""
+        for word in (self.ws_csm, self.ws_dec, self.err):
+            rc = lib.read_error(word)
+            if rc != lib.OK:
+                raise lib.CsmkvError(rc, "device")

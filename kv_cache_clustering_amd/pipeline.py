@@ -91,6 +91,46 @@ class ClusteredKVCache:
             self._round(r, s_before)
         return O, r
 
+    def capture_decode(self):
+        """Capture one decode step's append + attention into a HIP graph.
+
+        The launch bounds are fixed at the cache capacity (the kernels read the actual
+        lengths on the device), so one graph serves every step.  Step inputs are read from
+        the static buffers q_in, k_in, v_in; the output lands in self.out.  Clustering
+        rounds stay outside the graph (they are rare and their r changes).
+        """
+        S, cap, d = self.K.shape
+        dev = self.K.device
+        groups = S // self.H_kv
+        self.q_in = torch.zeros((groups, self.H_q, d), dtype=self.K.dtype, device=dev)
+        self.k_in = torch.zeros((S, d), dtype=self.K.dtype, device=dev)
+        self.v_in = torch.zeros((S, d), dtype=self.K.dtype, device=dev)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            lib.kv_append(self.K, self.V, self.N, self.lens, self.k_in, self.v_in, self.err)
+            lib.decode_attn_logn(self.q_in, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
+                                 out=self.out, max_len=cap, workspace=self.ws_dec)
+        self.graph = graph
+
+    def decode_step_graph(self, q=None, k_new=None, v_new=None):
+        """decode_step through the captured graph.  Inputs, when given, are copied into the
+        static buffers first.  Returns (O, r or None)."""
+        if q is not None:
+            self.q_in.copy_(q)
+            self.k_in.copy_(k_new)
+            self.v_in.copy_(v_new)
+        self.step_index += 1
+        self.graph.replay()
+        self.sched.append()
+        self.outlier_len += 1
+        r = None
+        if self.sched.over_budget():
+            s_before = self.sched.s
+            r = self.sched.next_round(self.step_index)
+            self._round(r, s_before)
+        return self.out, r
+
     def check_errors(self):
         """Synchronise and raise if a kernel flagged a bad length."""
         for word in (self.ws_csm, self.ws_dec, self.err):

@@ -192,6 +192,32 @@ def main():
     inplace_avg = sum(inplace_ms) / len(inplace_ms)
     del Ki, Vi, Ni, Li
 
+    # decode loop wall time per step: eager calls vs one HIP graph replay per step
+    loop_steps = min(100, w.steps - K - W - 1)
+    base = W + K
+    t0 = time.perf_counter()
+    for i in range(loop_steps):
+        lib.kv_append(Kd, Vd, Nd, Ld, app_k[base + i], app_v[base + i], err)
+        lib.decode_attn_logn(q_all[i % (K + W)], Kd, Vd, Nd, Ld, w.H_q, w.H_kv, out=O,
+                             max_len=cap, workspace=ws_d)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / loop_steps
+    q_in, k_in, v_in = q_all[0].clone(), app_k[0].clone(), app_v[0].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.kv_append(Kd, Vd, Nd, Ld, k_in, v_in, err)
+        lib.decode_attn_logn(q_in, Kd, Vd, Nd, Ld, w.H_q, w.H_kv, out=O, max_len=cap,
+                             workspace=ws_d)
+    graph.replay()  # one appended token
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gsteps = min(loop_steps, w.steps - K - W - loop_steps - 2)
+    for _ in range(gsteps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / max(1, gsteps)
+    assert lib.read_error(err) == lib.OK and lib.read_error(ws_d) == lib.OK
+
     # achievable copy bandwidth on this machine (context for the roofline fraction)
     nbytes = 4 << 30
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -245,6 +271,8 @@ def main():
                         "frac": dec_gbps / PEAK_GBPS, "layers": w.layers,
                         "traffic": recorded_traffic("dec_split_bf16_g4", DEC_SOURCES)},
         "append_us": app_avg * 1e3,
+        "decode_loop_wall_us_per_step": {"eager": eager_us, "hip_graph": graph_us,
+                                         "steps": loop_steps, "includes": "append + attention, 32 layers"},
         "hbm_copy_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": "csm_round<bf16> (csm_compress_into)",
                      "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",

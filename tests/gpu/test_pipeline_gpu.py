@@ -76,3 +76,38 @@ def test_algorithm1_loop_32k_batch4(lib, dev):
     assert np.all(Nsum == w.ctx + w.steps - 1)
     parity.check_report(obs.rep)
     assert worst < 2e-4
+
+
+def test_mha_32k_batch8_full_size(lib, dev):
+    """Llama-2-7B-32K MHA shape at batch 8: 8192 slices, ~137 GB of bf16 K/V resident in HBM.
+    Prefill rounds to the 25% budget in lockstep on sampled slices, then two decode steps."""
+    from kv_cache_clustering_amd.pipeline import ClusteredKVCache
+    w = kvsynth.workload(5, steps=3, cap_extra=3)
+    c = kvsynth.make_cache(w, dev, batch_slices=256)
+    assert c["K"].numel() * 2 * 2 > 130e9
+    q_all = kvsynth.make_queries(w, dev)
+    obs = Lockstep(sample=[0, 4097, w.slices - 1])
+    cache = ClusteredKVCache(c["K"], c["V"], c["N"], c["lens"], H_q=w.H_q, H_kv=w.H_kv, n=w.ctx,
+                             R=w.R, Gamma=128, g=w.g, observer=obs)
+    rs = cache.prefill()
+    assert len(rs) == 8 and cache.sched.s == 7947        # the hand-derived prefill trajectory
+    worst = 0.0
+    for i in range(1, 3):
+        O, r = cache.decode_step(q_all[i], c["app_k"][i - 1], c["app_v"][i - 1])
+        assert r is None
+        Oh = O.cpu().double().numpy()
+        for z in obs.sample:
+            g, kvh = divmod(z, w.H_kv)
+            s = int(cache.lens[z])
+            ref = oatt.logn_attention_one(parity.to_f64(q_all[i, g, kvh].cpu()),
+                                          parity.to_f64(cache.K[z, :s].cpu()),
+                                          parity.to_f64(cache.V[z, :s].cpu()),
+                                          cache.N[z, :s].cpu().numpy().astype(np.int64))
+            worst = max(worst, float(np.abs(Oh[g, kvh] - ref).max()))
+    cache.check_errors()
+    print(obs.rep, "decode max abs", worst)
+    assert np.all(cache.lens.cpu().numpy() == 7949)
+    parity.check_report(obs.rep)
+    assert worst < 2e-4
+    del cache, c, q_all
+    torch.cuda.empty_cache()

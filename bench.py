@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-slices", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--workloads", default="1,2,3,5",
+                    help="other synthetic workloads to measure and report (comma list, '' for none)")
     return ap.parse_args()
 
 
@@ -243,6 +245,13 @@ def main():
         cpu = cpu_baseline(w, K0, V0, N0, L0, Kd, Vd, Nd, Ld, q_all[W + K - 1], maskh,
                            args.cpu_slices)
 
+    others = []
+    wl = [int(x) for x in args.workloads.split(",") if x.strip()]
+    if wl:
+        del K0, V0, N0, Kw, Vw, Nw, Kd, Vd, Nd, app_k, app_v, c
+        torch.cuda.empty_cache()
+        for cid in wl:
+            others.append(measure_workload(cid))
     out = {
         "metric": METRIC,
         "value": value,
@@ -279,9 +288,83 @@ def main():
                      "frac": csm_gbps / PEAK_GBPS,
                      "traffic": recorded_traffic("csm_round_bf16", CSM_SOURCES)},
         "cpu_baseline": cpu,
+        "workloads": others,
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_workload(cid):
+    """One synthetic workload: every prefill round in place (HIP events per round), then
+    decode steps (append + attention) over the compressed cache.  Figures are algorithmic
+    bytes / event time."""
+    import numpy as np
+    import torch
+
+    import kvsynth
+    from kv_cache_clustering_amd import _lib as lib
+    from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
+
+    w = kvsynth.workload(cid)
+    dev = torch.device("cuda:0")
+    c = kvsynth.make_cache(w, dev, batch_slices=256)
+    K, V, N, L, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]
+    maskh = mask.cpu().numpy()
+    S, cap, d = K.shape
+    row = 2 * d * K.element_size() + 4
+    ws = torch.empty(lib.csm_workspace_bytes(K, w.n1, w.n2, w.c, max_len=w.ctx), dtype=torch.uint8,
+                     device=dev)
+    if w.R is None:
+        rs = [w.r_init]
+    else:
+        sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
+        rs = sched.prefill_rounds()
+    stream = torch.cuda.current_stream(dev)
+    rounds = []
+    s = w.ctx
+    n_comp = int((maskh == 0).sum())
+    for r in rs:
+        s2 = round_output_length(s, w.n1, w.n2, w.c, r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.csm_compress(K, V, N, L, w.n1, w.n2, w.c, r, mask if maskh.any() else None,
+                         max_len=max(s, w.ctx if maskh.any() else 0), workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        alg = n_comp * ((s - w.n1) + (s2 - w.n1)) * row
+        rounds.append({"r": round(r, 4), "s_in": s, "s_out": s2, "ms": ms, "GBps": alg / ms / 1e6,
+                       "slice_tokens_per_s": n_comp * s / (ms * 1e-3)})
+        s = s2
+    assert lib.read_error(ws) == lib.OK
+    assert int(L[int(np.argmin(maskh))]) == s
+    out = {"workload": w.name, "slices": S, "dtype": w.dtype, "ctx": w.ctx, "round0": rounds[0],
+           "prefill": {"rounds": len(rounds), "len": s, "ms": sum(x["ms"] for x in rounds),
+                       "GBps": sum(n_comp * ((x["s_in"] - w.n1) + (x["s_out"] - w.n1)) * row
+                                   for x in rounds) / sum(x["ms"] for x in rounds) / 1e6}}
+    ws_d = torch.empty(lib.decode_workspace_bytes(K, w.H_q, w.H_kv), dtype=torch.uint8, device=dev)
+    q = kvsynth.make_queries(w, dev, steps=min(w.steps, 8))
+    O = torch.empty((w.groups, w.H_q, d), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    nsteps = q.shape[0]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+    for i in range(nsteps):
+        if w.append:
+            lib.kv_append(K, V, N, L, c["app_k"][i], c["app_v"][i], err)
+        evs[i][0].record(stream)
+        lib.decode_attn_logn(q[i], K, V, N, L, w.H_q, w.H_kv, out=O, workspace=ws_d)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    assert lib.read_error(ws_d) == lib.OK and lib.read_error(err) == lib.OK
+    times = [a.elapsed_time(b) for a, b in evs[1:]] or [evs[0][0].elapsed_time(evs[0][1])]
+    us = sum(times) / len(times) * 1e3
+    dec_alg = int(L.sum()) * row + w.groups * w.H_q * d * (K.element_size() + 4)
+    out["decode"] = {"us": us, "GBps": dec_alg / (us * 1e-6) / 1e9,
+                     "frac": dec_alg / (us * 1e-6) / 1e9 / PEAK_GBPS, "steps_timed": len(times)}
+    out["round0"]["frac"] = out["round0"]["GBps"] / PEAK_GBPS
+    del c, K, V, N, L, q, ws, ws_d
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, K0, V0, N0, L0, Kd, Vd, Nd, Ld, q, maskh, nslices):

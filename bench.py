@@ -22,6 +22,7 @@ import math
 import os
 import sys
 import time
+from statistics import median
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -29,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "CSM compress tokens/s + log-N decode-attn HBM GB/s (% of peak), 64K ctx"
 PEAK_GBPS = 8000.0
 ROW_BYTES = 128 * 2 * 2 + 4  # K + V (bf16, d = 128) + int32 degree
-CSM_SOURCES = ["csm_kernel.hip", "device_common.hpp", "kernel_args.hpp"]
+CSM_SOURCES = ["csm_kernel.hip", "csm_common.hpp", "device_common.hpp", "kernel_args.hpp"]
 DEC_SOURCES = ["decode_kernel.hip", "device_common.hpp", "kernel_args.hpp"]
 
 
@@ -167,6 +168,7 @@ def main():
     app_ms = [e[1].elapsed_time(e[2]) for e in ev]
     dec_ms = [e[2].elapsed_time(e[3]) for e in ev]
     csm_avg, dec_avg, app_avg = (sum(x) / K for x in (csm_ms, dec_ms, app_ms))
+    csm_med, dec_med = median(csm_ms), median(dec_ms)
 
     # decode bytes: every slice's rows once, plus q in and O out
     lens_d = Ld.cpu().numpy()
@@ -178,11 +180,42 @@ def main():
     dec_gbps = dec_alg / (dec_avg * 1e-3) / 1e9
     value = slice_tokens / (csm_avg * 1e-3)
 
-    # auxiliary: the in-place round (input restored untimed before each rep)
+    # decode as a model runs it: one call per layer (that layer's slices, its query heads)
+    hk = w.H_kv
+    layer_views = []
+    for layer in range(w.layers):
+        sl = slice(layer * hk, (layer + 1) * hk)
+        layer_views.append((Kd[sl], Vd[sl], Nd[sl], Ld[sl], O[layer:layer + 1]))
+    ws_l = torch.empty(lib.decode_workspace_bytes(layer_views[0][0], w.H_q, w.H_kv, max_len=w.ctx),
+                       dtype=torch.uint8, device=dev)
+    q_last = q_all[W + K - 1]
+
+    def layer_calls():
+        for layer, (Kl, Vl, Nl, Ll, Ol) in enumerate(layer_views):
+            lib.decode_attn_logn(q_last[layer:layer + 1], Kl, Vl, Nl, Ll, w.H_q, w.H_kv, out=Ol,
+                                 max_len=w.ctx, workspace=ws_l)
+
+    layer_calls()
+    torch.cuda.synchronize()
+    layer_ms = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer_calls()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        layer_ms.append(e0.elapsed_time(e1))
+    assert lib.read_error(ws_l) == lib.OK
+    dec_alg_now = int(Ld.cpu().numpy().sum()) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
+
+    # auxiliary: the in-place round.  Before each rep the input is restored and the 256 MB
+    # last-level cache (MALL) is flushed by writing a 512 MB buffer, both untimed.
     Ki, Vi, Ni, Li = torch.empty_like(K0), torch.empty_like(V0), torch.empty_like(N0), torch.empty_like(L0)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     inplace_ms = []
-    for _ in range(3):
+    for rep in range(5):
         Ki.copy_(K0); Vi.copy_(V0); Ni.copy_(N0); Li.copy_(L0)
+        flush.fill_(rep & 0xFF)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         lib.csm_compress(Ki, Vi, Ni, Li, w.n1, w.n2, w.c, r0, mask, max_len=w.ctx, workspace=ws_c)
@@ -192,7 +225,7 @@ def main():
     assert torch.equal(Li, Lw)
     inplace_alg = csm_bytes(lens_in, lens_out, maskh, w.n1, out_of_place=False)
     inplace_avg = sum(inplace_ms) / len(inplace_ms)
-    del Ki, Vi, Ni, Li
+    del Ki, Vi, Ni, Li, flush
 
     # decode loop wall time per step: eager calls vs one HIP graph replay per step
     loop_steps = min(100, w.steps - K - W - 1)
@@ -270,14 +303,21 @@ def main():
                    "outlier_slices": int(maskh.sum()), "c": w.c, "n1": w.n1, "n2": w.n2,
                    "r": r0, "round_out_len": s_out, "budget": sched.budget,
                    "decode_len": int(sched.s), "prefill_rounds": len(sched.rounds)},
-        "csm": {"ms": csm_avg, "alg_bytes": csm_alg, "GBps": csm_gbps, "frac": csm_gbps / PEAK_GBPS,
+        "csm": {"ms": csm_avg, "median_ms": csm_med, "min_ms": min(csm_ms),
+                "alg_bytes": csm_alg, "GBps": csm_gbps, "frac": csm_gbps / PEAK_GBPS,
                 "slice_tokens": slice_tokens,
                 "model_tokens_per_s": w.ctx / (csm_avg * 1e-3),
                 "whole_step_slice_tokens_per_s": slice_tokens / (ms_per_step * 1e-3),
-                "in_place_ms": inplace_avg, "in_place_alg_bytes": inplace_alg,
+                "in_place_ms": inplace_avg, "in_place_median_ms": median(inplace_ms),
+                "in_place_min_ms": min(inplace_ms), "in_place_alg_bytes": inplace_alg,
                 "in_place_GBps": inplace_alg / (inplace_avg * 1e-3) / 1e9},
-        "decode_attn": {"us": dec_avg * 1e3, "alg_bytes": dec_alg, "GBps": dec_gbps,
+        "decode_attn": {"us": dec_avg * 1e3, "median_us": dec_med * 1e3,
+                        "min_us": min(dec_ms) * 1e3, "alg_bytes": dec_alg, "GBps": dec_gbps,
                         "frac": dec_gbps / PEAK_GBPS, "layers": w.layers,
+                        "per_layer_calls": {
+                            "calls": w.layers, "median_us": median(layer_ms) * 1e3,
+                            "min_us": min(layer_ms) * 1e3, "alg_bytes": dec_alg_now,
+                            "GBps": dec_alg_now / (median(layer_ms) * 1e-3) / 1e9},
                         "traffic": recorded_traffic("dec_split_bf16_g4", DEC_SOURCES)},
         "append_us": app_avg * 1e3,
         "decode_loop_wall_us_per_step": {"eager": eager_us, "hip_graph": graph_us,

@@ -130,14 +130,15 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
 }
 
 struct DecLayout {
-  size_t item_off, part, total;
+  size_t item_off, item_zp, part, total;
 };
 
 DecLayout dec_layout(const csmkv_cache *c, int G) {
   DecLayout L;
-  L.item_off = kAlign;
-  L.part = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
   const int64_t items = csmkv::dec_max_items(c->num_slices, c->max_len);
+  L.item_off = kAlign;
+  L.item_zp = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
+  L.part = L.item_zp + align_up((size_t)items * 16);
   L.total = L.part + align_up((size_t)items * G * (4 + kHeadDim) * 4);
   return L;
 }
@@ -240,9 +241,11 @@ int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t 
   a.max_len = cache->max_len;
   a.H_q = H_q;
   a.H_kv = H_kv;
+  a.tsplit = csmkv::dec_split_tokens(cache->num_slices, cache->max_len);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cache->d));
   a.err = reinterpret_cast<int32_t *>(w);
   a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
+  a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
   a.part = reinterpret_cast<float *>(w + lay.part);
   const int e = csmkv::launch_decode(a, cache->dtype == CSMKV_F32, G, items,
                                      static_cast<hipStream_t>(stream));

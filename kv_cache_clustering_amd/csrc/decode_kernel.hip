@@ -3,10 +3,13 @@
 // cluster degrees n_t; Algorithm 1 decode output), and the Algorithm 1 append step.
 //
 // Split-K over the sequence, HBM-bound:
-//   dec_prep    : one workgroup validates lens[], gives every slice ceil(len / TSPLIT)
-//                 work items and scans them into item offsets.
+//   dec_prep    : one workgroup validates lens[], gives every slice ceil(len / tsplit)
+//                 work items and scans them into item offsets.  tsplit (512 or 1024
+//                 tokens) is chosen on the host from the slice count and the length bound so
+//                 that a call has about 2048 items: a call over one layer's few slices still
+//                 spreads over every CU, a call over many slices keeps items long.
 //   dec_split   : persistent workgroups stride over the work items.  A work item is
-//                 TSPLIT tokens of one slice, shared by the G query heads of that KV
+//                 tsplit tokens of one slice, shared by the G query heads of that KV
 //                 head, so K, V and N are read once per step.  Each wave streams a
 //                 quarter of the item: 16 B per lane per row, sub-blocks of 16 tokens
 //                 (bf16) with the next sub-block's loads in flight while the current
@@ -23,7 +26,8 @@
 
 namespace csmkv {
 
-constexpr int kTSplit = 1024;       // tokens per work item
+constexpr int kTSplitMin = 512, kTSplitMax = 1024;  // tokens per work item
+constexpr int64_t kItemTarget = 2048;               // work items a call aims for
 constexpr int kPartWidth = 4 + kHeadDim;  // floats per (item, head) partial: 16-byte rows
 constexpr int kDecThreads = 256;
 
@@ -41,7 +45,7 @@ __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
     const int s = a.lens[z];
     const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
     if (!ok) atomicExch(a.err, kDeviceError);
-    local += ok ? (s + kTSplit - 1) / kTSplit : 0;
+    local += ok ? (s + a.tsplit - 1) / a.tsplit : 0;
   }
   // block exclusive scan of `local`
   int incl = local;
@@ -60,17 +64,21 @@ __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
     a.item_off[z] = run;
     const int s = a.lens[z];
     const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
-    run += ok ? (s + kTSplit - 1) / kTSplit : 0;
+    const int cnt = ok ? (s + a.tsplit - 1) / a.tsplit : 0;
+    for (int p = 0; p < cnt; ++p)  // (slice, first token, end token): one load in dec_split
+      *reinterpret_cast<int4 *>(a.item_zp + 4 * (int64_t)(run + p)) =
+          make_int4((int)z, p * a.tsplit, min(s, (p + 1) * a.tsplit), 0);
+    run += cnt;
   }
   if (t == (int)blockDim.x - 1) a.item_off[S] = before + incl;
 }
 
-template <typename T>
+template <typename T, int G>
 struct DecTile {
   static constexpr int ROWB = kHeadDim * (int)sizeof(T);
   static constexpr int LPR = ROWB / 16;     // lanes per row
   static constexpr int RPW = 64 / LPR;      // rows per wave-wide load
-  static constexpr int NR = 4;              // wave loads per sub-block
+  static constexpr int NR = G >= 8 ? 2 : 4;  // wave loads per sub-block (8 heads: fewer, no spills)
   static constexpr int SUB = NR * RPW;      // rows per sub-block
   static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
 };
@@ -109,15 +117,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // One sub-block of a wave's token range held in registers: NR wave loads of K and V rows
 // (16 B per lane per row) and the degrees of the lane's rows.
+template <int NR>
 struct DecStage {
-  u32x4 k[4], v[4];
-  int32_t n[4];
+  u32x4 k[NR], v[NR];
+  int32_t n[NR];
 };
 
-template <typename T>
-__device__ __forceinline__ void dec_load(DecStage &st, const char *Kz, const char *Vz,
+template <typename T, int G>
+__device__ __forceinline__ void dec_load(DecStage<DecTile<T, G>::NR> &st, const char *Kz, const char *Vz,
                                          const int32_t *Nz, int sb, int we, int rw, int sg) {
-  using DT = DecTile<T>;
+  using DT = DecTile<T, G>;
 #pragma unroll
   for (int i = 0; i < DT::NR; ++i) {
     const int tok = sb + DT::RPW * i + rw;
@@ -134,10 +143,10 @@ __device__ __forceinline__ void dec_load(DecStage &st, const char *Kz, const cha
 
 // Online-softmax update of (mrun, lrun, o) with one sub-block, base 2.
 template <typename T, int G>
-__device__ __forceinline__ void dec_compute(const DecStage &st, int sb, int we, int rw,
+__device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G>::NR> &st, int sb, int we, int rw,
                                             const u32x4 *qv, float scale_log2, float *mrun,
-                                            float *lrun, float (*o)[DecTile<T>::EPL]) {
-  using DT = DecTile<T>;
+                                            float *lrun, float (*o)[DecTile<T, G>::EPL]) {
+  using DT = DecTile<T, G>;
   constexpr int EPL = DT::EPL;
   T *tsel = nullptr;
   const float NEG_INF = -__builtin_inff();
@@ -183,7 +192,7 @@ __device__ __forceinline__ void dec_compute(const DecStage &st, int sb, int we, 
 
 template <typename T, int G>
 __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
-  using DT = DecTile<T>;
+  using DT = DecTile<T, G>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
   constexpr int PW = kPartWidth;  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][G][PW];
@@ -193,25 +202,18 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
   const int total = a.item_off[S];
   const float NEG_INF = -__builtin_inff();
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // slice of this item: last z with item_off[z] <= item
-    int64_t lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (a.item_off[mid] <= item) lo = mid; else hi = mid - 1;
-    }
-    const int64_t z = lo;
-    const int s = a.lens[z];
-    const int p = item - a.item_off[z];
-    const int tok0 = p * kTSplit, tok1 = min(s, tok0 + kTSplit);
+    const int4 it4 = *reinterpret_cast<const int4 *>(a.item_zp + 4 * (int64_t)item);
+    const int64_t z = it4.x;
+    const int tok0 = it4.y, tok1 = it4.z;
     const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
     const char *Kz = a.K + z * a.cap * ROWB;
     const char *Vz = a.V + z * a.cap * ROWB;
     const int32_t *Nz = a.N + z * a.cap;
-    const int wq = kTSplit / 4;
+    const int wq = a.tsplit / 4;
     const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
     // two register stages: the next sub-block loads while the current one is computed
-    DecStage A, B;
-    if (wb < we) dec_load<T>(A, Kz, Vz, Nz, wb, we, rw, sg);
+    DecStage<DT::NR> A, B;
+    if (wb < we) dec_load<T, G>(A, Kz, Vz, Nz, wb, we, rw, sg);
     // this lane's q segment for each head of the group
     u32x4 qv[G];
 #pragma unroll
@@ -227,10 +229,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     }
     for (int sb = wb; sb < we; sb += 2 * SUB) {
       const int sb1 = sb + SUB;
-      if (sb1 < we) dec_load<T>(B, Kz, Vz, Nz, sb1, we, rw, sg);
+      if (sb1 < we) dec_load<T, G>(B, Kz, Vz, Nz, sb1, we, rw, sg);
       dec_compute<T, G>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
       if (sb1 >= we) break;
-      if (sb1 + SUB < we) dec_load<T>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
+      if (sb1 + SUB < we) dec_load<T, G>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
       dec_compute<T, G>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
     }
     // sum the row groups of the wave (they hold different tokens, same segment)
@@ -280,56 +282,77 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
   }
 }
 
-// One workgroup per slice.  For each head: block-wide max of the item maxima, then 8 item
-// groups of 32 lanes (4 output elements per lane) accumulate the rescaled partials with
-// independent loads, and the groups are summed through LDS.
+// One workgroup per slice, every head at once.  1. per-head maximum of the item maxima
+// (strided loads, wave reductions over the lanes of one head, four waves through LDS);
+// 2. each thread takes 4 output elements of one head and one of 8/G item groups and sums the
+// rescaled partials, four independent items per step; 3. the item groups are summed through
+// LDS and divided.
 template <int G>
 __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
   constexpr int PW = kPartWidth;
-  __shared__ float s_red[8];
-  __shared__ float s_acc[8][kHeadDim];
-  __shared__ float s_l[8];
+  constexpr int COLS = 32 * G;    // 4-element columns over the G heads
+  constexpr int IG = 256 / COLS;  // item groups
+  __shared__ float s_mx[4][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[IG][G][kHeadDim];
+  __shared__ float s_l[IG][G];
   const int64_t z = blockIdx.x;
-  const int t = threadIdx.x, grp = t >> 5, e4 = (t & 31) * 4;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int i0 = a.item_off[z], i1 = a.item_off[z + 1];
   const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
   const float NEG_INF = -__builtin_inff();
-  for (int h = 0; h < G; ++h) {
-    float M = NEG_INF;
-    for (int it = i0 + t; it < i1; it += 256) M = fmaxf(M, a.part[((int64_t)it * G + h) * PW]);
+  {
+    const int h = t % G;
+    float m = NEG_INF;
+    for (int it = i0 + t / G; it < i1; it += 256 / G)
+      m = fmaxf(m, a.part[((int64_t)it * G + h) * PW]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if ((t & 63) == 0) s_red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
-    for (int it = i0 + grp; it < i1; it += 8) {
-      const float *pp = a.part + ((int64_t)it * G + h) * PW;
-      const float m = pp[0];
-      const float wgt = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      const float4 o = *reinterpret_cast<const float4 *>(pp + 4 + e4);
-      L = fmaf(wgt, pp[1], L);
-      acc0 = fmaf(wgt, o.x, acc0);
-      acc1 = fmaf(wgt, o.y, acc1);
-      acc2 = fmaf(wgt, o.z, acc2);
-      acc3 = fmaf(wgt, o.w, acc3);
-    }
-    s_acc[grp][e4] = acc0;
-    s_acc[grp][e4 + 1] = acc1;
-    s_acc[grp][e4 + 2] = acc2;
-    s_acc[grp][e4 + 3] = acc3;
-    if ((t & 31) == 0) s_l[grp] = L;
-    __syncthreads();
-    if (t < kHeadDim) {
-      float num = 0.f, den = 0.f;
+    for (int o = G; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (l < G) s_mx[w][l] = m;
+  }
+  __syncthreads();
+  const int col = t % COLS, grp = t / COLS, h = col / 32, e4 = (col % 32) * 4;
+  const float M = fmaxf(fmaxf(s_mx[0][h], s_mx[1][h]), fmaxf(s_mx[2][h], s_mx[3][h]));
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
+  auto add = [&](float m, float lsum, float4 o) {
+    const float wgt = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    L = fmaf(wgt, lsum, L);
+    acc0 = fmaf(wgt, o.x, acc0);
+    acc1 = fmaf(wgt, o.y, acc1);
+    acc2 = fmaf(wgt, o.z, acc2);
+    acc3 = fmaf(wgt, o.w, acc3);
+  };
+  int it = i0 + grp;
+  for (; it + 3 * IG < i1; it += 4 * IG) {
+    float m[4], ls[4];
+    float4 o[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        num += s_acc[q][t];
-        den += s_l[q];
-      }
-      a.O[(g * a.H_q + kvh * G + h) * (int64_t)kHeadDim + t] = den > 0.f ? num / den : 0.f;
+    for (int k = 0; k < 4; ++k) {
+      const float *pp = a.part + ((int64_t)(it + k * IG) * G + h) * PW;
+      const float4 head = *reinterpret_cast<const float4 *>(pp);
+      m[k] = head.x;
+      ls[k] = head.y;
+      o[k] = *reinterpret_cast<const float4 *>(pp + 4 + e4);
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add(m[k], ls[k], o[k]);
+  }
+  for (; it < i1; it += IG) {
+    const float *pp = a.part + ((int64_t)it * G + h) * PW;
+    const float4 head = *reinterpret_cast<const float4 *>(pp);
+    add(head.x, head.y, *reinterpret_cast<const float4 *>(pp + 4 + e4));
+  }
+  *reinterpret_cast<float4 *>(&s_acc[grp][h][e4]) = make_float4(acc0, acc1, acc2, acc3);
+  if (e4 == 0) s_l[grp][h] = L;
+  __syncthreads();
+  for (int i = t; i < G * kHeadDim; i += 256) {
+    const int hh = i / kHeadDim, d = i % kHeadDim;
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int q = 0; q < IG; ++q) {
+      num += s_acc[q][hh][d];
+      den += s_l[q][hh];
+    }
+    a.O[(g * a.H_q + kvh * G + hh) * (int64_t)kHeadDim + d] = den > 0.f ? num / den : 0.f;
   }
 }
 
@@ -345,8 +368,16 @@ static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
+int32_t dec_split_tokens(int64_t num_slices, int32_t max_len) {
+  const int64_t want = num_slices * (int64_t)max_len / kItemTarget;
+  int32_t ts = kTSplitMin;
+  while (ts < kTSplitMax && ts < want) ts *= 2;
+  return ts;
+}
+
 int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
-  return num_slices * (int64_t)((max_len + kTSplit - 1) / kTSplit);
+  const int32_t ts = dec_split_tokens(num_slices, max_len);
+  return num_slices * (int64_t)((max_len + ts - 1) / ts);
 }
 
 int launch_decode(const DecArgs &a, int dtype_f32, int G, int64_t max_items, hipStream_t st) {

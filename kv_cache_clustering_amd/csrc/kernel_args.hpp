@@ -35,9 +35,11 @@ struct DecArgs {
   float *O;
   int64_t num_slices, cap;
   int32_t max_len, H_q, H_kv;
+  int32_t tsplit;     // tokens per work item (dec_split_tokens of num_slices, max_len)
   float scale_log2;   // log2(e) / sqrt(d)
   int32_t *err;       // device error word of this call
   int32_t *item_off;  // [num_slices + 1] first work item of each slice
+  int32_t *item_zp;   // [items][4] (slice, first token, end token, 0) of every work item
   float *part;        // [items][G][4 + d] (max, sum, 0, 0, o) partials
 };
 
@@ -54,7 +56,9 @@ struct AppArgs {
 int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream);
 int launch_decode(const DecArgs &a, int dtype_f32, int G, int64_t max_items, hipStream_t st);
 int launch_append(const AppArgs &a, hipStream_t st);
-// Upper bound on decode work items for a geometry (sizes the partial buffer).
+// Tokens per decode work item for a geometry, and the upper bound on work items (sizes the
+// partial buffer).  Both depend only on the slice count and the host-known length bound.
+int32_t dec_split_tokens(int64_t num_slices, int32_t max_len);
 int64_t dec_max_items(int64_t num_slices, int32_t max_len);
 
 }  // namespace csmkv

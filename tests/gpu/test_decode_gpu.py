@@ -43,6 +43,82 @@ def test_ragged_lengths_random_degrees(lib, dev, dtype, H_q, H_kv):
             assert torch.all(O[g, kvh * G:(kvh + 1) * G] == 0)
 
 
+def _split_tokens(S, max_len):
+    """The work-item size rule stated in the decode kernel: 512 tokens when that gives at most
+    about 2048 items over the length bound, else 1024."""
+    want = S * max_len // 2048
+    ts = 512
+    while ts < 1024 and ts < want:
+        ts *= 2
+    return ts
+
+
+@pytest.mark.parametrize("ts,S,cap", [(512, 16, 1544), (512, 400, 1544), (1024, 400, 3080)])
+def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
+    """Each work-item size, with lengths on both sides of item boundaries; the cache is built
+    on the device and one slice of every distinct length is checked against the oracle."""
+    assert _split_tokens(S, cap) == ts
+    H_q, H_kv = 8, 2
+    G = H_q // H_kv
+    gen = torch.Generator(device=dev).manual_seed(ts)
+    K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.randint(1, 30, (S, cap), generator=gen, device=dev, dtype=torch.int32)
+    choices = [0, 1, ts - 1, ts, ts + 1, 2 * ts, 2 * ts + 1, 3 * ts - 1, 3 * ts, cap]
+    rng = np.random.default_rng(ts)
+    lens = rng.choice(choices, size=S)
+    lens[:len(choices)] = choices
+    L = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    q = torch.randn((S // H_kv, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
+    O = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, max_len=cap).cpu().double().numpy()
+    worst = 0.0
+    for z in range(len(choices)):
+        g, kvh = divmod(z, H_kv)
+        s = int(lens[z])
+        Kz, Vz = parity.to_f64(K[z, :s].cpu()), parity.to_f64(V[z, :s].cpu())
+        Nz = N[z, :s].cpu().numpy().astype(np.int64)
+        for h in range(G):
+            hq = kvh * G + h
+            if s == 0:
+                assert np.all(O[g, hq] == 0)
+                continue
+            ref = oatt.logn_attention_one(parity.to_f64(q[g, hq].cpu()), Kz, Vz, Nz)
+            worst = max(worst, float(np.abs(O[g, hq] - ref).max()))
+    print("tsplit", ts, "max abs", worst)
+    assert worst < 2e-4
+
+
+def test_per_layer_calls_match_one_call(lib, dev):
+    """Decode over each layer's slices (a view of the cache, a smaller work-item size) against
+    one call over every layer: both within the oracle tolerance of each other, sampled heads
+    checked against the oracle."""
+    layers, H_kv, H_q, cap = 6, 8, 32, 3000
+    S = layers * H_kv
+    G = H_q // H_kv
+    gen = torch.Generator(device=dev).manual_seed(7)
+    K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.randint(1, 9, (S, cap), generator=gen, device=dev, dtype=torch.int32)
+    L = torch.randint(1, cap + 1, (S,), generator=gen, device=dev, dtype=torch.int32)
+    q = torch.randn((layers, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
+    O_all = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, max_len=cap)
+    O_l = torch.empty_like(O_all)
+    for l in range(layers):
+        sl = slice(l * H_kv, (l + 1) * H_kv)
+        lib.decode_attn_logn(q[l:l + 1], K[sl], V[sl], N[sl], L[sl], H_q, H_kv,
+                             out=O_l[l:l + 1], max_len=cap)
+    assert float((O_all - O_l).abs().max()) < 2e-5
+    Lh = L.cpu().numpy()
+    for z in (0, 13, S - 1):
+        g, kvh = divmod(z, H_kv)
+        s = int(Lh[z])
+        Kz, Vz = parity.to_f64(K[z, :s].cpu()), parity.to_f64(V[z, :s].cpu())
+        Nz = N[z, :s].cpu().numpy().astype(np.int64)
+        for h in range(G):
+            ref = oatt.logn_attention_one(parity.to_f64(q[g, kvh * G + h].cpu()), Kz, Vz, Nz)
+            assert float(np.abs(O_l[g, kvh * G + h].cpu().double().numpy() - ref).max()) < 2e-4
+
+
 def test_llama3_64k_budget_cache_sampled(lib, dev):
     """Attention over a cache compressed to the 20% budget on the GPU (outlier slices stay
     at 64K); all heads computed, sampled heads compared with the oracle."""

@@ -228,7 +228,7 @@ def main():
     del Ki, Vi, Ni, Li, flush
 
     # decode loop wall time per step: eager calls vs one HIP graph replay per step
-    loop_steps = min(100, w.steps - K - W - 1)
+    loop_steps = min(50, w.steps - K - W - 1)
     base = W + K
     t0 = time.perf_counter()
     for i in range(loop_steps):
@@ -252,6 +252,41 @@ def main():
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - t0) * 1e6 / max(1, gsteps)
     assert lib.read_error(err) == lib.OK and lib.read_error(ws_d) == lib.OK
+
+    # the same steps with Algorithm 1's trigger decided on the device: 25 steps (append,
+    # attention, triggered round) per graph; rounds fire whenever a slice reaches B + g
+    tsteps = min(100, w.steps - K - W - loop_steps - gsteps - 2) // 25 * 25
+    trig_us, trig_rounds = None, None
+    if tsteps > 0:
+        thr_v = math.ceil(sched.budget + sched.g)
+        thr = torch.full((S,), thr_v, dtype=torch.int32, device=dev)
+        ridx = torch.full((S,), len(sched.rounds), dtype=torch.int32, device=dev)
+        s_now = int(Ld[int(np.argmin(maskh))].item())
+        bound = min(cap, max(thr_v, s_now) + tsteps)
+        ws_t = torch.empty(lib.csm_workspace_bytes(Kd, w.n1, w.n2, w.c, max_len=bound),
+                           dtype=torch.uint8, device=dev)
+        tq = q_all[0].clone()
+        tk = torch.stack([app_k[base + loop_steps + gsteps + 1 + i] for i in range(25)])
+        tv = torch.stack([app_v[base + loop_steps + gsteps + 1 + i] for i in range(25)])
+        torch.cuda.synchronize()
+        tgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tgraph):
+            for i in range(25):
+                lib.kv_append(Kd, Vd, Nd, Ld, tk[i], tv[i], err)
+                lib.decode_attn_logn(tq, Kd, Vd, Nd, Ld, w.H_q, w.H_kv, out=O, max_len=cap,
+                                     workspace=ws_d)
+                lib.csm_compress_triggered(Kd, Vd, Nd, Ld, thr, ridx, w.n1, w.n2, w.c, w.r_init,
+                                           0.05, 0.1, mask, max_len=bound, workspace=ws_t)
+        torch.cuda.synchronize()
+        per_replay = []
+        for _ in range(tsteps // 25):
+            t0 = time.perf_counter()
+            tgraph.replay()
+            torch.cuda.synchronize()
+            per_replay.append((time.perf_counter() - t0) * 1e6 / 25)
+        trig_us = {"mean": sum(per_replay) / len(per_replay), "per_replay": per_replay}
+        assert lib.read_error(ws_t) == lib.OK and lib.read_error(err) == lib.OK
+        trig_rounds = int(ridx[int(np.argmin(maskh))].item()) - len(sched.rounds)
 
     # achievable copy bandwidth on this machine (context for the roofline fraction)
     nbytes = 4 << 30
@@ -321,7 +356,10 @@ def main():
                         "traffic": recorded_traffic("dec_split_bf16_g4", DEC_SOURCES)},
         "append_us": app_avg * 1e3,
         "decode_loop_wall_us_per_step": {"eager": eager_us, "hip_graph": graph_us,
-                                         "steps": loop_steps, "includes": "append + attention, 32 layers"},
+                                         "steps": loop_steps, "includes": "append + attention, 32 layers",
+                                         "hip_graph_device_trigger": trig_us,
+                                         "device_trigger_steps": tsteps,
+                                         "device_trigger_rounds_fired": trig_rounds},
         "hbm_copy_GBps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": "csm_round<bf16> (csm_compress_into)",
                      "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",

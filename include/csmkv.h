@@ -69,7 +69,8 @@ CSMKV_API const char *csmkv_status_string(int status);
 /* ABI version of this header (major * 100 + minor). */
 CSMKV_API int csmkv_version(void);
 
-/* Bytes of workspace csm_compress / csm_compress_into / csm_compress_debug need for this
+/* Bytes of workspace csm_compress / csm_compress_into / csm_compress_debug /
+ * csm_compress_triggered need for this
  * cache geometry and these n1, n2, c.  0 if the arguments are invalid. */
 CSMKV_API size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c);
 
@@ -126,6 +127,32 @@ CSMKV_API int csm_compress_debug(void *K, void *V, int32_t *N, int32_t *lens, co
                        int32_t n1, int32_t n2, int32_t c, double r, const uint8_t *outlier_mask,
                        void *workspace, size_t workspace_bytes, void *stream,
                        int32_t *best_b, uint8_t *selected, int32_t *src_pos);
+
+/*
+ * csm_compress_triggered -- csm_compress (in place) with Algorithm 1's trigger and r
+ * schedule decided on the device, so that decode steps and their rounds can be enqueued
+ * (or captured in a graph) without reading lengths back.
+ *   Chelsea review, section 三, Algorithm 1: after an append, cluster when s >= B + g;
+ *   CentroidKV page, 渐进式调度: r annealed linearly over the rounds.
+ * Per slice z: the round runs only when outlier_mask[z] == 0 and lens[z] >= threshold[z]
+ *   (give ceil(B + g): for an integer length, s >= B + g exactly when s >= ceil(B + g));
+ *   it then uses r = max(r_init - j * r_delta, r_min), with j = round_index[z] and the
+ *   product and difference each rounded once in fp64, and increments round_index[z].
+ *   A slice that does not run (or is in error) is left as it is, round_index included.
+ *   The round itself is csm_compress's.
+ * Arguments: threshold [num_slices] int32 and round_index [num_slices] int32 are device
+ *   arrays owned by the caller (round_index is updated in place: it is the schedule state,
+ *   start it at the number of rounds already run, e.g. 0 or the prefill round count);
+ *   0 <= r_min <= r_init <= 1, r_delta >= 0, none NaN; cache->max_len bounds the length of
+ *   every slice that runs (a running slice above it is a device error and is left as it is;
+ *   slices that do not run are only checked against cap); the rest as csm_compress.
+ * Returns CSMKV_OK or a negative csmkv_status.
+ */
+CSMKV_API int csm_compress_triggered(void *K, void *V, int32_t *N, int32_t *lens,
+                           const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c,
+                           const int32_t *threshold, int32_t *round_index, double r_init,
+                           double r_delta, double r_min, const uint8_t *outlier_mask,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Chunk units per slice the compress launch uses for this geometry (the leading dimension
  * of the debug taps, which hold one entry block per unit).  0 if invalid. */

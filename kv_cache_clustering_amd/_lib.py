@@ -46,6 +46,8 @@ _SIGS = {
                                          _i32, _d, _p, _p, _sz, _p]),
     "csm_compress_debug": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _d, _p, _p, _sz,
                                           _p, _p, _p, _p]),
+    "csm_compress_triggered": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _p, _p, _d,
+                                              _d, _d, _p, _p, _sz, _p]),
     "decode_attn_logn_workspace_bytes": (_sz, [_desc, _i32, _i32]),
     "decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _sz, _p]),
     "kv_append": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p]),
@@ -144,6 +146,29 @@ def csm_compress(K, V, N, lens, n1=16, n2=64, c=256, r=0.5, outlier_mask=None, m
     rc = _lib.csm_compress(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), n1, n2, c,
                            float(r), _ptr(outlier_mask), _ptr(ws), ws.numel(), _stream(K.device))
     _raise(rc, "csm_compress")
+    return ws
+
+
+def csm_compress_triggered(K, V, N, lens, threshold, round_index, n1=16, n2=64, c=256,
+                           r_init=0.5, r_delta=0.05, r_min=0.1, outlier_mask=None, max_len=None,
+                           workspace=None):
+    """csm_compress in place where each slice runs only when lens >= threshold, with
+    r = max(r_init - j * r_delta, r_min) from its round counter j (incremented on the device).
+    threshold, round_index: int32 GPU tensors [num_slices].  Returns the workspace used."""
+    _check_cache(K, V, N, lens)
+    _check_mask(outlier_mask, K.shape[0])
+    for t, name in ((threshold, "threshold"), (round_index, "round_index")):
+        if (t is None or t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous()
+                or t.shape != (K.shape[0],)):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor [{K.shape[0]}]")
+    desc = cache_desc(K, max_len)
+    ws = _workspace(_lib.csm_compress_workspace_bytes(ctypes.byref(desc), n1, n2, c), K.device,
+                    workspace)
+    rc = _lib.csm_compress_triggered(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), n1,
+                                     n2, c, _ptr(threshold), _ptr(round_index), float(r_init),
+                                     float(r_delta), float(r_min), _ptr(outlier_mask), _ptr(ws),
+                                     ws.numel(), _stream(K.device))
+    _raise(rc, "csm_compress_triggered")
     return ws
 
 

@@ -8,20 +8,23 @@
 // averaging of K and V; degrees accumulate over rounds).
 //
 // Launch structure (all on the caller's stream):
-//   csm_prep   : resets the error word and the ticket counter, validates every lens[]
-//                entry, records each slice's input and output length, clears the
-//                per-chunk "source consumed" flags.
+//   csm_prep   : resets the error word, validates every lens[] entry, decides which
+//                slices run (all, or those at their trigger threshold) and with which r,
+//                records each slice's input and output length, resets the per-slice
+//                ticket counters and clears the per-chunk "source consumed" flags.
 //   csm_round  : one 256-thread workgroup per unit; units are (slice, chunk) pairs plus
 //                one "tail" unit per slice that moves the recent rows and writes lens.
-//                Workgroups take a ticket from an atomic counter and map ticket ->
-//                (slice, unit) in slice-major order, so every lower-numbered unit has
-//                already started when a unit runs.
+//                A workgroup's slice comes from its block index (a slice that does not
+//                run exits at once, touching no counter); its unit within the slice is a
+//                ticket from that slice's atomic counter, so every lower-numbered unit of
+//                the slice has already started when a unit runs.
 //
 // In-place compaction: chunk j of a slice writes rows [n1 + j*(c - m), ...), which may
 // overlap the source rows of chunks i <= j.  A chunk loads its whole source (K, V, N)
 // into LDS and registers, waits for its loads to land, and raises its flag; before
 // writing it waits for the flags of the lower chunks whose sources its destination
-// overlaps.  Those chunks hold lower tickets, are already running and raise their flag
+// overlaps.  Those chunks hold lower tickets of the same slice, are already running and
+// raise their flag
 // without waiting on anything, so every wait ends.  Lower chunks never write into a
 // higher chunk's source.
 //
@@ -51,25 +54,33 @@ namespace csmkv {
 
 __global__ void csm_prep(CsmArgs a) {
   if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) {
-      *a.err = 0;
-      *a.ticket = 0u;
-    }
+    if (threadIdx.x == 0) *a.err = 0;
     __syncthreads();
     for (int64_t z = threadIdx.x; z < a.num_slices; z += blockDim.x) {
-      int s = a.lens_in[z];
-      bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap_in;
-      bool outl = a.mask != nullptr && a.mask[z] != 0;
+      const int s = a.lens_in[z];
+      const bool outl = a.mask != nullptr && a.mask[z] != 0;
+      bool ok = s >= 0 && (int64_t)s <= a.cap_in;
+      // Algorithm 1 trigger (when thresholds are given): cluster when s >= B + g
+      const bool run = a.thr == nullptr || (ok && !outl && s >= a.thr[z]);
+      if (run && s > a.max_len) ok = false;  // the launch covers max_len rows
+      double r = a.r;
+      if (a.thr != nullptr && run && ok) {  // r annealed over this slice's rounds
+        const int j = a.round_idx[z];
+        r = fmax(__dsub_rn(a.r_init, __dmul_rn((double)j, a.r_delta)), a.r_min);
+        a.round_idx[z] = j + 1;
+      }
       int s_new = s;
-      int M = s - a.n1 - a.n2;
-      if (ok && !outl && M >= 2) {
-        int nch = (M + a.c - 1) / a.c;
-        int last = M - (nch - 1) * a.c;
-        s_new = s - (nch - 1) * a.m_full - merge_count_dev(a.r, last);
+      const int M = s - a.n1 - a.n2;
+      if (ok && run && !outl && M >= 2) {
+        const int nch = (M + a.c - 1) / a.c;
+        const int last = M - (nch - 1) * a.c;
+        s_new = s - (nch - 1) * merge_count_dev(r, a.c) - merge_count_dev(r, last);
       }
       if (ok && (int64_t)s_new > a.cap_out) ok = false;
       a.s_in[z] = ok ? s : -1;
       a.s_out[z] = s_new;
+      a.s_r[z] = run ? r : -1.0;
+      a.ticket[z] = 0u;
       if (!ok) atomicExch(a.err, kDeviceError);
     }
   } else {
@@ -141,17 +152,18 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   __shared__ int32_t s_misc[8];
 
   const int t = threadIdx.x;
-  if (t == 0) s_misc[0] = (int32_t)atomicAdd(a.ticket, 1u);
-  __syncthreads();
-  const uint32_t ticket = (uint32_t)s_misc[0];
-  const int64_t z = ticket / (uint32_t)a.units;
-  const int u = (int)(ticket % (uint32_t)a.units);
-  if (z >= a.num_slices) return;
+  const int64_t z = blockIdx.x / (uint32_t)a.units;
   const int s = a.s_in[z];
   if (s < 0) return;  // invalid length: slice left untouched (error word already set)
+  const double r = a.s_r[z];
+  if (r < 0.0) return;  // trigger not met: slice left as it is
   const bool outl = a.mask != nullptr && a.mask[z] != 0;
   if (outl && a.in_place) return;
+  if (t == 0) s_misc[0] = (int32_t)atomicAdd(a.ticket + z, 1u);
+  __syncthreads();
+  const int u = s_misc[0];
   const int n1 = a.n1, n2 = a.n2, c = a.c;
+  const int m_full = merge_count_dev(r, c);
   const int M = s - n1 - n2;
   const int nch = M >= 2 ? (M + c - 1) / c : 0;
   const int s_new = a.s_out[z];
@@ -167,9 +179,9 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   const int start = n1 + j * c;
   const int L = min(c, M - j * c);
   const bool copy_only = outl;  // outlier slice, out of place: rows move unchanged
-  const int m = copy_only ? 0 : merge_count_dev(a.r, L);
+  const int m = copy_only ? 0 : merge_count_dev(r, L);
   const int nA = (L + 1) / 2, nB = L / 2;
-  const int base = copy_only ? start : n1 + j * (c - a.m_full);
+  const int base = copy_only ? start : n1 + j * (c - m_full);
   const int nout = L - m;
   T *tsel = nullptr;
 

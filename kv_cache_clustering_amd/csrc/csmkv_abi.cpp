@@ -32,17 +32,6 @@ int check_cache(const csmkv_cache *c) {
   return CSMKV_OK;
 }
 
-// floor(r * L / 2 + 1e-9) clamped to [0, ceil(L/2)], evaluated in fp64 step by step.
-int merge_count_host(double r, int L) {
-  if (L < 2) return 0;
-  volatile double x = r * (double)L;
-  x = x * 0.5;
-  x = x + 1e-9;
-  int m = (int)std::floor((double)x);
-  int hi = (L + 1) / 2;
-  return m < 0 ? 0 : (m > hi ? hi : m);
-}
-
 int64_t units_per_slice(int32_t max_len, int32_t n1, int32_t n2, int32_t c) {
   const int64_t M = (int64_t)max_len - n1 - n2;
   const int64_t nch = M >= 2 ? (M + c - 1) / c : 0;
@@ -58,14 +47,16 @@ int check_csm_params(int32_t n1, int32_t n2, int32_t c, double r) {
 }
 
 struct CsmLayout {
-  size_t s_in, s_out, flags, total;
+  size_t ticket, s_in, s_out, s_r, flags, total;
 };
 
 CsmLayout csm_layout(int64_t S, int64_t units) {
   CsmLayout L;
-  L.s_in = kAlign;
+  L.ticket = kAlign;
+  L.s_in = L.ticket + align_up((size_t)S * 4);
   L.s_out = L.s_in + align_up((size_t)S * 4);
-  L.flags = L.s_out + align_up((size_t)S * 4);
+  L.s_r = L.s_out + align_up((size_t)S * 4);
+  L.flags = L.s_r + align_up((size_t)S * 8);
   L.total = L.flags + align_up((size_t)(S * units) * 4);
   return L;
 }
@@ -74,7 +65,9 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
                const csmkv_cache *src, void *K_out, void *V_out, int32_t *N_out,
                int32_t *lens_out, const csmkv_cache *dst, int32_t n1, int32_t n2, int32_t c,
                double r, const uint8_t *mask, void *ws, size_t ws_bytes, void *stream,
-               int in_place, int32_t *tap_best, uint8_t *tap_sel, int32_t *tap_src) {
+               int in_place, int32_t *tap_best, uint8_t *tap_sel, int32_t *tap_src,
+               const int32_t *thr = nullptr, int32_t *round_idx = nullptr, double r_init = 0.0,
+               double r_delta = 0.0, double r_min = 0.0) {
   int rc = check_cache(src);
   if (rc) return rc;
   rc = check_cache(dst);
@@ -112,14 +105,19 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
   a.n1 = n1;
   a.n2 = n2;
   a.c = c;
-  a.m_full = merge_count_host(r, c);
   a.units = (int32_t)units;
   a.in_place = in_place;
   a.r = r;
+  a.thr = thr;
+  a.round_idx = round_idx;
+  a.r_init = r_init;
+  a.r_delta = r_delta;
+  a.r_min = r_min;
   a.err = reinterpret_cast<int32_t *>(w);
-  a.ticket = reinterpret_cast<uint32_t *>(w + 4);
+  a.ticket = reinterpret_cast<uint32_t *>(w + lay.ticket);
   a.s_in = reinterpret_cast<int32_t *>(w + lay.s_in);
   a.s_out = reinterpret_cast<int32_t *>(w + lay.s_out);
+  a.s_r = reinterpret_cast<double *>(w + lay.s_r);
   a.flags = reinterpret_cast<int32_t *>(w + lay.flags);
   a.tap_best = tap_best;
   a.tap_sel = tap_sel;
@@ -168,12 +166,25 @@ const char *csmkv_status_string(int status) {
   }
 }
 
-int csmkv_version(void) { return 100; }
+int csmkv_version(void) { return 101; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
   if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
   const int64_t units = units_per_slice(cache->max_len, n1, n2, c);
   return csm_layout(cache->num_slices, units).total;
+}
+
+int csm_compress_triggered(void *K, void *V, int32_t *N, int32_t *lens,
+                           const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c,
+                           const int32_t *threshold, int32_t *round_index, double r_init,
+                           double r_delta, double r_min, const uint8_t *outlier_mask,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  if (threshold == nullptr || round_index == nullptr) return CSMKV_EINVAL;
+  if (!(r_delta >= 0.0) || !(r_min >= 0.0 && r_min <= 1.0) || !(r_init >= r_min && r_init <= 1.0))
+    return CSMKV_EINVAL;  // also rejects NaN; every annealed r then lies in [r_min, r_init]
+  return csm_common(K, V, N, lens, cache, K, V, N, lens, cache, n1, n2, c, r_init, outlier_mask,
+                    workspace, workspace_bytes, stream, 1, nullptr, nullptr, nullptr, threshold,
+                    round_index, r_init, r_delta, r_min);
 }
 
 int64_t csm_compress_units(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {

@@ -15,13 +15,18 @@ struct CsmArgs {
   const int32_t *lens_in;
   const uint8_t *mask;
   int64_t num_slices, cap_in, cap_out;
-  int32_t max_len, n1, n2, c, m_full, units, in_place;
+  int32_t max_len, n1, n2, c, units, in_place;
   double r;
+  // device-side trigger (nullable thr: every slice runs with r)
+  const int32_t *thr;   // [num_slices] a slice runs when its length >= thr[z]
+  int32_t *round_idx;   // [num_slices] rounds run so far; r = max(r_init - j * r_delta, r_min)
+  double r_init, r_delta, r_min;
   // workspace
   int32_t *err;      // device error word of this call
-  uint32_t *ticket;  // unit ticket counter
+  uint32_t *ticket;  // [num_slices] unit ticket counters
   int32_t *s_in;     // [num_slices] validated input length, -1 = skip the slice
   int32_t *s_out;    // [num_slices] output length
+  double *s_r;       // [num_slices] this round's r, < 0 = slice not clustered this call
   int32_t *flags;    // [num_slices][units] "chunk source consumed"
   // debug taps (nullable)
   int32_t *tap_best;

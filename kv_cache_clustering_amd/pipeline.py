@@ -7,7 +7,9 @@ O = Softmax(q K^T / sqrt(d) + log N) V, and clusters when s >= B + g.  CentroidK
 
 Every length is known on the host in closed form (schedule.Algorithm1), so driving the
 device needs no read-back: the whole loop is a sequence of asynchronous library calls on
-the current stream.  All sequences of a batch share one prefill length and therefore one
+the current stream.  With the device-side trigger (csm_compress_triggered) the round of a
+step is decided on the device from each slice's length and round counter, so many steps can
+also be captured in one HIP graph (capture_loop / run_loop).  All sequences of a batch share one prefill length and therefore one
 schedule; slices flagged outlier are never clustered and keep growing.
 """
 
@@ -130,6 +132,99 @@ class ClusteredKVCache:
             r = self.sched.next_round(self.step_index)
             self._round(r, s_before)
         return self.out, r
+
+    # ------------------------------------------------------------ device-side trigger
+    def _device_schedule(self):
+        """Per-slice trigger threshold ceil(B + g) and round counter (the device's copy of the
+        schedule state), created on first use from the host bookkeeping."""
+        if getattr(self, "thr", None) is None:
+            import math
+            S = self.K.shape[0]
+            dev = self.K.device
+            if self.sched.budget is None:
+                raise ValueError("the device trigger needs a budget (R)")
+            t = math.ceil(self.sched.budget + self.sched.g)
+            self.thr = torch.full((S,), t, dtype=torch.int32, device=dev)
+            self.round_idx = torch.full((S,), self.sched.j, dtype=torch.int32, device=dev)
+        return self.thr, self.round_idx
+
+    def _triggered_round(self, max_len):
+        thr, idx = self._device_schedule()
+        lib.csm_compress_triggered(self.K, self.V, self.N, self.lens, thr, idx, self.n1, self.n2,
+                                   self.c, self.sched.r_init, self.sched.delta, self.sched.r_min,
+                                   self.mask, max_len=max_len, workspace=self.ws_csm)
+
+    def _host_step(self):
+        """Advance the host bookkeeping by one decode step (append, then the trigger)."""
+        self.step_index += 1
+        self.sched.append()
+        self.outlier_len += 1
+        if self.sched.over_budget():
+            return self.sched.next_round(self.step_index)
+        return None
+
+    def decode_step_device(self, q, k_new, v_new, out=None):
+        """decode_step with the trigger and r decided on the device: nothing on the host
+        decides whether the round runs.  The host bookkeeping is advanced in closed form so
+        that it keeps the same lengths.  Returns (O, r the host expects, or None)."""
+        lib.kv_append(self.K, self.V, self.N, self.lens, k_new, v_new, self.err)
+        self.step_index += 1
+        self.sched.append()
+        self.outlier_len += 1
+        bound = self.max_len  # lengths after the append, before any round
+        O = lib.decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
+                                 out=self.out if out is None else out, max_len=bound,
+                                 workspace=self.ws_dec)
+        self._triggered_round(bound)
+        r = self.sched.next_round(self.step_index) if self.sched.over_budget() else None
+        return O, r
+
+    def capture_loop(self, steps):
+        """Capture `steps` decode steps (append, attention, device-triggered round) in one HIP
+        graph.  Inputs are read from the static buffers loop_q [steps, groups, H_q, d],
+        loop_k / loop_v [steps, S, d]; outputs land in loop_out [steps, groups, H_q, d].
+        Launch bounds: attention over the capacity, rounds over the trigger threshold plus
+        the steps of one replay (a round runs as soon as a slice reaches the threshold)."""
+        S, cap, d = self.K.shape
+        dev = self.K.device
+        groups = S // self.H_kv
+        thr, _ = self._device_schedule()
+        round_bound = min(cap, max(int(thr.max().item()), self.sched.s) + steps)
+        if self.ws_csm.numel() < lib.csm_workspace_bytes(self.K, self.n1, self.n2, self.c,
+                                                         max_len=round_bound):
+            raise ValueError("CSM workspace too small for the loop's launch bound")
+        self.loop_q = torch.zeros((steps, groups, self.H_q, d), dtype=self.K.dtype, device=dev)
+        self.loop_k = torch.zeros((steps, S, d), dtype=self.K.dtype, device=dev)
+        self.loop_v = torch.zeros((steps, S, d), dtype=self.K.dtype, device=dev)
+        self.loop_out = torch.empty((steps, groups, self.H_q, d), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                lib.kv_append(self.K, self.V, self.N, self.lens, self.loop_k[i], self.loop_v[i],
+                              self.err)
+                lib.decode_attn_logn(self.loop_q[i], self.K, self.V, self.N, self.lens, self.H_q,
+                                     self.H_kv, out=self.loop_out[i], max_len=cap,
+                                     workspace=self.ws_dec)
+                self._triggered_round(round_bound)
+        self.loop_graph = graph
+        self.loop_steps = steps
+
+    def run_loop(self, q=None, k_new=None, v_new=None):
+        """Replay the captured loop once (inputs, when given, are copied into the static
+        buffers first).  Returns (loop_out, the r of every round the host bookkeeping expects
+        as (step, r) pairs)."""
+        if q is not None:
+            self.loop_q.copy_(q)
+            self.loop_k.copy_(k_new)
+            self.loop_v.copy_(v_new)
+        self.loop_graph.replay()
+        rounds = []
+        for _ in range(self.loop_steps):
+            r = self._host_step()
+            if r is not None:
+                rounds.append((self.step_index, r))
+        return self.loop_out, rounds
 
     def check_errors(self):
         """Synchronise and raise if a kernel flagged a bad length."""

@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.version() == 100
+    assert lib.version() == 101
     for code in range(-6, 1):
         assert lib.status_string(code).startswith("CSMKV_")
     assert "unknown" in lib.status_string(-99)
@@ -101,6 +101,26 @@ def test_compress_into_rejects_aliasing_and_mismatch(lib):
              ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20), ctypes.c_void_p(4 << 20),
              ctypes.byref(d2), 16, 64, 256, 0.5, None, FAKE, 1 << 30, None)
     assert lib.raw.csm_compress_into(*args2) == lib.EINVAL         # slice counts differ
+
+
+def test_triggered_argument_validation(lib):
+    d = _desc(lib)
+
+    def trig(thr=FAKE, idx=FAKE, r_init=0.5, r_delta=0.05, r_min=0.1, c=256, ws_bytes=1 << 30):
+        return lib.raw.csm_compress_triggered(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 16, 64, c,
+                                              thr, idx, r_init, r_delta, r_min, None, FAKE,
+                                              ws_bytes, None)
+
+    assert trig(thr=None) == lib.EINVAL
+    assert trig(idx=None) == lib.EINVAL
+    assert trig(r_init=1.5) == lib.EINVAL
+    assert trig(r_init=0.05) == lib.EINVAL          # below r_min
+    assert trig(r_min=-0.1) == lib.EINVAL
+    assert trig(r_delta=-0.01) == lib.EINVAL
+    assert trig(r_delta=float("nan")) == lib.EINVAL
+    assert trig(r_min=float("nan")) == lib.EINVAL
+    assert trig(c=300) == lib.EUNSUPPORTED
+    assert trig(ws_bytes=8) == lib.EWORKSPACE
 
 
 def test_debug_taps_must_come_together(lib):

@@ -91,9 +91,9 @@ __global__ void csm_prep(CsmArgs a) {
   }
 }
 
-template <typename T>
+template <typename T, int NT>
 __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch, bool outl) {
-  using TL = Tile<T>;
+  using TL = Tile<T, NT>;
   const int t = threadIdx.x;
   const int64_t kin = z * a.cap_in * TL::ROWB, kout = z * a.cap_out * TL::ROWB;
   const char *Ks = a.Kin + kin, *Vs = a.Vin + kin;
@@ -102,14 +102,14 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   int32_t *Nd = a.Nout + z * a.cap_out;
   int32_t *src = a.tap_src ? a.tap_src + z * a.cap_out : nullptr;
   if (nch == 0) {  // nothing to compress: lens unchanged, copy everything out of place
-    if (!a.in_place) copy_rows<T>(Ks, Vs, Ns, Kd, Vd, Nd, s);
+    if (!a.in_place) copy_rows<T, NT>(Ks, Vs, Ns, Kd, Vd, Nd, s);
     if (src)
       for (int i = t; i < s; i += blockDim.x) src[i] = i;
     if (t == 0) a.lens_out[z] = s;
     return;
   }
   const int n1 = a.n1, n2 = a.n2, c = a.c;
-  if (!a.in_place) copy_rows<T>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
+  if (!a.in_place) copy_rows<T, NT>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
   if (a.in_place && !outl && t == 0) {
     // the recent rows land in [s_new - n2, s_new): wait for chunks whose sources overlap it
     const int d0 = s_new - n2, d1 = s_new;
@@ -120,7 +120,7 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   }
   __syncthreads();
   const int64_t so = (int64_t)(s - n2), dof = (int64_t)(s_new - n2);
-  copy_rows<T>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
+  copy_rows<T, NT>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
                Vd + dof * TL::ROWB, Nd + dof, n2);
   if (src) {
     for (int i = t; i < n1; i += blockDim.x) src[i] = i;
@@ -137,19 +137,25 @@ __device__ __forceinline__ uint64_t rank_key(float score, int aidx) {
   return ((uint64_t)ord << 8) | (uint64_t)(255 - aidx);
 }
 
-template <typename T>
+template <typename T, int NT>
 __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
-  using TL = Tile<T>;
+  using TL = Tile<T, NT>;
   constexpr int ROWB = TL::ROWB, SEGS = TL::SEGS, RPI = TL::RPI, NLD = TL::NLD, EPS = TL::EPS;
+  constexpr int NW = NT / 64;    // waves: 4 or 8
+  constexpr int BT = 16 / NW;    // 32-row B tiles per wave in the similarity step
+  constexpr int NQ = NT / 128;   // parts of the rank count
+  static_assert(NW == 4 || NW == 8, "256 or 512 threads");
   __shared__ __attribute__((aligned(16))) char tile[kMaxChunk * ROWB];
   __shared__ __attribute__((aligned(16))) float s_invA[128], s_invB[128];  // 1 / max(|k|, eps)
   __shared__ int32_t s_n[kMaxChunk];
   __shared__ int32_t s_outrow[kMaxChunk];
   __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_list[128];
-  __shared__ int32_t s_cnt0[128], s_cnt1[128], s_rank[2][128];
+  __shared__ int32_t s_cnt0[128], s_cnt1[128], s_rank[NQ][128];
   __shared__ int32_t s_mrg[4][64], s_mcnt[4];
   __shared__ __attribute__((aligned(16))) uint64_t s_key[128];  // rank keys, 0 = no edge
-  __shared__ int32_t s_misc[8];
+  __shared__ float s_bsc[NW / 4][128];  // per B part: best score and index of every A row
+  __shared__ int32_t s_bix[NW / 4][128];
+  __shared__ int32_t s_misc[1 + NW];
 
   const int t = threadIdx.x;
   const int64_t z = blockIdx.x / (uint32_t)a.units;
@@ -169,7 +175,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   const int s_new = a.s_out[z];
 
   if (u == a.units - 1) {
-    tail_unit<T>(a, z, s, s_new, nch, outl);
+    tail_unit<T, NT>(a, z, s, s_new, nch, outl);
     return;
   }
   if (u >= nch) return;
@@ -225,25 +231,28 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
   __syncthreads();
 
-  // 2. similarity tile on MFMA and arg-max over B for every A column
+  // 2. similarity tile on MFMA and arg-max over B for every A column.  Wave w holds A
+  //    columns [32 (w mod 4), +32) against B tiles [BT (w / 4), +BT): with 8 waves the two B
+  //    halves are merged through LDS (half 0 holds the lower B indices and wins ties).
   if (!copy_only && nB > 0) {
     const int w = t >> 6, l = t & 63, h = l >> 5, col = l & 31;
-    const int aidx = 32 * w + col;
-    f32x16 acc[4];
+    const int bq = w >> 2;
+    const int aidx = 32 * (w & 3) + col;
+    f32x16 acc[BT];
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl)
+    for (int tl = 0; tl < BT; ++tl)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tl][q] = 0.f;
-    sim_tile<4>(tile, aidx, col, h, acc, tsel);
+    sim_tile<BT>(tile, aidx, col, h, acc, tsel, bq * BT);
     // cosine = (dot * (1/|b|)) * (1/|a|); lowest B index wins a tie (ascending order, strict >)
     const float ia = s_invA[aidx];
     float best = -__builtin_inff();
-    int bidx = 0x7fffffff;
+    int bidx = 0;
 #pragma unroll
-    for (int tl = 0; tl < 4; ++tl) {
+    for (int tl = 0; tl < BT; ++tl) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int b0 = tl * 32 + 8 * g4 + 4 * h;
+        const int b0 = (bq * BT + tl) * 32 + 8 * g4 + 4 * h;
         const float4 ib = *reinterpret_cast<const float4 *>(&s_invB[b0]);
         const float ibv[4] = {ib.x, ib.y, ib.z, ib.w};
 #pragma unroll
@@ -263,8 +272,13 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
       bidx = oi;
     }
     if (h == 0) {
-      s_best[aidx] = aidx < nA ? bidx : -1;
-      s_key[aidx] = aidx < nA ? rank_key(best, aidx) : 0ull;
+      if (NW == 4) {
+        s_best[aidx] = aidx < nA ? bidx : -1;
+        s_key[aidx] = aidx < nA ? rank_key(best, aidx) : 0ull;
+      } else {
+        s_bsc[bq][aidx] = best;
+        s_bix[bq][aidx] = bidx;
+      }
     }
   } else if (t < 128) {
     s_best[t] = -1;
@@ -275,23 +289,38 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   __syncthreads();
   if (a.in_place && t == 0)
     __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (NW == 8) {
+    if (!copy_only && nB > 0 && t < 128) {
+      const float b0s = s_bsc[0][t], b1s = s_bsc[NW / 4 - 1][t];
+      const bool up = b1s > b0s;
+      const float best = up ? b1s : b0s;
+      const int bidx = up ? s_bix[NW / 4 - 1][t] : s_bix[0][t];
+      s_best[t] = t < nA ? bidx : -1;
+      s_key[t] = t < nA ? rank_key(best, t) : 0ull;
+    }
+    __syncthreads();
+  }
 
   // 3. top-m selection: rank of each A edge by (score desc, index asc), i.e. the number of
-  //    larger unique keys.  Every thread counts over one half of the 128 candidates.
+  //    larger unique keys.  Every thread counts over one of NQ parts of the 128 candidates.
   {
-    const int aa = t & 127, half = t >> 7;
+    constexpr int PART = 128 / NQ;
+    const int aa = t & 127, part = t >> 7;
     const uint64_t my = s_key[aa];
     int cnt = 0;
 #pragma unroll 8
-    for (int q = half * 64; q < half * 64 + 64; q += 2) {
+    for (int q = part * PART; q < part * PART + PART; q += 2) {
       const uint64_t k0 = s_key[q], k1 = s_key[q + 1];
       cnt += (k0 > my) + (k1 > my);
     }
-    s_rank[half][aa] = cnt;
+    s_rank[part][aa] = cnt;
   }
   __syncthreads();
   if (t < 128) {
-    s_sel[t] = (t < nA && m > 0 && nB > 0) ? (s_rank[0][t] + s_rank[1][t] < m) : 0;
+    int rank = 0;
+#pragma unroll
+    for (int p = 0; p < NQ; ++p) rank += s_rank[p][t];
+    s_sel[t] = (t < nA && m > 0 && nB > 0) ? (rank < m) : 0;
     s_cnt0[t] = 0;
     s_cnt1[t] = 0;
     s_wsum[t] = t < nB ? s_n[2 * t + 1] : 0;
@@ -347,7 +376,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
   __syncthreads();
   if (my_b >= 0) s_list[s_off[my_b] + (t >= 64 ? s_cnt0[my_b] : 0) + my_pos] = t;
-  {  // output slots that hold a merged target, compacted per wave
+  if (t < kMaxChunk) {  // output slots that hold a merged target, compacted per wave
     bool mg = false;
     if (t < nout) {
       const int r = s_outrow[t];
@@ -428,10 +457,13 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
 }
 
-// bf16: 72 KB of LDS per workgroup, two workgroups (two waves per SIMD) per CU.
-__global__ void __launch_bounds__(256, 2) csm_round_bf16(CsmArgs a) { csm_round_body<__bf16>(a); }
+// bf16: 512 threads and 78 KB of LDS per workgroup, two workgroups (four waves per SIMD) per CU.
+constexpr int kBf16Threads = 512;
+__global__ void __launch_bounds__(kBf16Threads, 2) csm_round_bf16(CsmArgs a) {
+  csm_round_body<__bf16, kBf16Threads>(a);
+}
 // fp32: the 128 KB key tile allows one workgroup per CU.
-__global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) { csm_round_body<float>(a); }
+__global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) { csm_round_body<float, 256>(a); }
 
 // Host-side launcher used by the C ABI.  Returns 0 or a hipError_t value.
 int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream) {
@@ -444,7 +476,7 @@ int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream) {
   if (dtype_f32)
     hipLaunchKernelGGL(csm_round_f32, dim3((uint32_t)total), dim3(256), 0, stream, args);
   else
-    hipLaunchKernelGGL(csm_round_bf16, dim3((uint32_t)total), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(csm_round_bf16, dim3((uint32_t)total), dim3(kBf16Threads), 0, stream, args);
   e = hipGetLastError();
   return (int)e;
 }

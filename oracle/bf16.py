@@ -44,9 +44,13 @@ def f64_to_bits(x):
 
 
 def round_to_storage(x, storage):
-    """Round fp64 ``x`` to the cache storage format: 'bf16', 'f32' (RNE) or 'f64' (none)."""
+    """Round fp64 ``x`` to the cache storage format: 'bf16', 'f16', 'f32' (RNE) or 'f64'
+    (none)."""
     if storage == "bf16":
         return round_to_bf16(x)
+    if storage == "f16":
+        from .fp16 import round_to_f16
+        return round_to_f16(x)
     if storage == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     if storage == "f64":

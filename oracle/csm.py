@@ -112,6 +112,7 @@ def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64", f
 
     K, V : [cap, d] fp64 arrays holding the stored values; N : [cap] integer degrees;
     s : current length.  Rows at and beyond s are ignored and returned unchanged.
+    storage : format the merged centroids are rounded to ('bf16', 'f16', 'f32' or 'f64').
     forced : optional {chunk start: (best_b, selected)} replacing the match and selection
     decisions of those chunks (used to follow another implementation's decisions where
     they differ only at a near-tie, so that merging and compaction can still be compared).

@@ -43,8 +43,9 @@ def parse():
     ap.add_argument("--cpu-slices", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
-    ap.add_argument("--workloads", default="1,2,3,5",
-                    help="other synthetic workloads to measure and report (comma list, '' for none)")
+    ap.add_argument("--workloads", default="1,2,3,5,4:f16",
+                    help="other synthetic workloads to measure and report (comma list of ids, "
+                         "id:dtype for another storage format, '' for none)")
     return ap.parse_args()
 
 
@@ -314,12 +315,13 @@ def main():
                            args.cpu_slices)
 
     others = []
-    wl = [int(x) for x in args.workloads.split(",") if x.strip()]
+    wl = [x.strip() for x in args.workloads.split(",") if x.strip()]
     if wl:
         del K0, V0, N0, Kw, Vw, Nw, Kd, Vd, Nd, app_k, app_v, c
         torch.cuda.empty_cache()
-        for cid in wl:
-            others.append(measure_workload(cid))
+        for spec in wl:  # "<id>" or "<id>:<dtype>" (the same workload stored in another format)
+            cid, _, dt = spec.partition(":")
+            others.append(measure_workload(int(cid), dt or None))
     out = {
         "metric": METRIC,
         "value": value,
@@ -372,7 +374,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_workload(cid):
+def measure_workload(cid, dtype=None):
     """One synthetic workload: every prefill round in place (HIP events per round), then
     decode steps (append + attention) over the compressed cache.  Figures are algorithmic
     bytes / event time."""
@@ -384,6 +386,8 @@ def measure_workload(cid):
     from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
 
     w = kvsynth.workload(cid)
+    if dtype is not None and dtype != w.dtype:
+        w = kvsynth.workload(cid, dtype=dtype, name=f"{w.name}-as-{dtype}")
     dev = torch.device("cuda:0")
     c = kvsynth.make_cache(w, dev, batch_slices=256)
     K, V, N, L, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]

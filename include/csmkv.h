@@ -52,7 +52,10 @@ typedef enum {
   CSMKV_EDEVICE = -6        /* csmkv_read_error: a kernel flagged a bad lens[] entry */
 } csmkv_status;
 
-typedef enum { CSMKV_BF16 = 0, CSMKV_F32 = 1 } csmkv_dtype;
+/* Storage formats of K, V (and q).  bf16 is the format the pages use; fp16 (IEEE binary16)
+ * and fp32 are supported as well.  Similarities are decided in fp32 in every format and
+ * merged centroids are stored rounded to nearest, ties to even. */
+typedef enum { CSMKV_BF16 = 0, CSMKV_F32 = 1, CSMKV_F16 = 2 } csmkv_dtype;
 
 typedef struct {
   int64_t num_slices; /* number of (batch, layer, kv-head) slices, >= 0 */

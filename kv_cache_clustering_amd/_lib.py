@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsmkv.so")
 
 OK, EINVAL, EDTYPE, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
 
 
 class CsmkvError(RuntimeError):
@@ -72,9 +72,11 @@ def version():
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return BF16
+    if t.dtype == torch.float16:
+        return F16
     if t.dtype == torch.float32:
         return F32
-    raise ValueError(f"cache dtype must be bfloat16 or float32, got {t.dtype}")
+    raise ValueError(f"cache dtype must be bfloat16, float16 or float32, got {t.dtype}")
 
 
 def cache_desc(K, max_len=None):

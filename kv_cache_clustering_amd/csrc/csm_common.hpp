@@ -26,6 +26,17 @@ __device__ __forceinline__ float seg_sumsq(u32x4 v, __bf16 *) {
   }
   return s;
 }
+__device__ __forceinline__ float seg_sumsq(u32x4 v, _Float16 *) {
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // fp16 squares are exact in fp32
+    const uint32_t w = v[q];
+    const float lo = f16_lo(w), hi = f16_hi(w);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
 __device__ __forceinline__ float seg_sumsq(u32x4 v, float *) {
   float s = 0.f;
 #pragma unroll
@@ -44,6 +55,14 @@ __device__ __forceinline__ void seg_unpack(u32x4 v, float *o, __bf16 *) {
     o[2 * q + 1] = bf_hi(v[q]);
   }
 }
+__device__ __forceinline__ void seg_unpack(u32x4 v, float *o, _Float16 *) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = v[q];
+    o[2 * q] = f16_lo(w);
+    o[2 * q + 1] = f16_hi(w);
+  }
+}
 __device__ __forceinline__ void seg_unpack(u32x4 v, float *o, float *) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) o[q] = __uint_as_float(v[q]);
@@ -53,6 +72,15 @@ __device__ __forceinline__ u32x4 seg_pack(const float *o, __bf16 *) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {  // v_cvt_pk_bf16_f32: round to nearest even
     const bf16x2 h = {(__bf16)o[2 * q], (__bf16)o[2 * q + 1]};
+    v[q] = __builtin_bit_cast(uint32_t, h);
+  }
+  return v;
+}
+__device__ __forceinline__ u32x4 seg_pack(const float *o, _Float16 *) {
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // v_cvt_f16_f32: round to nearest even
+    const f16x2 h = {(_Float16)o[2 * q], (_Float16)o[2 * q + 1]};
     v[q] = __builtin_bit_cast(uint32_t, h);
   }
   return v;
@@ -81,6 +109,24 @@ __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h
       u32x4 araw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(brow, seg, ROWB));
       bf16x8 aop = __builtin_bit_cast(bf16x8, araw);
       acc[tl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, acc[tl], 0, 0, 0);
+    }
+  }
+}
+template <int NTL = 4>
+__device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
+                                         _Float16 *, int tl0 = 0) {
+  constexpr int ROWB = Tile<_Float16>::ROWB;
+#pragma unroll
+  for (int kk = 0; kk < kHeadDim / 16; ++kk) {
+    const int seg = 2 * kk + h;
+    u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
+    f16x8 bop = __builtin_bit_cast(f16x8, braw);
+#pragma unroll
+    for (int tl = 0; tl < NTL; ++tl) {
+      const int brow = 2 * ((tl0 + tl) * 32 + col) + 1;
+      u32x4 araw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(brow, seg, ROWB));
+      f16x8 aop = __builtin_bit_cast(f16x8, araw);
+      acc[tl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[tl], 0, 0, 0);
     }
   }
 }

@@ -462,19 +462,24 @@ constexpr int kBf16Threads = 512;
 __global__ void __launch_bounds__(kBf16Threads, 2) csm_round_bf16(CsmArgs a) {
   csm_round_body<__bf16, kBf16Threads>(a);
 }
+__global__ void __launch_bounds__(kBf16Threads, 2) csm_round_f16(CsmArgs a) {
+  csm_round_body<_Float16, kBf16Threads>(a);
+}
 // fp32: the 128 KB key tile allows one workgroup per CU.
 __global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) { csm_round_body<float, 256>(a); }
 
 // Host-side launcher used by the C ABI.  Returns 0 or a hipError_t value.
-int launch_csm(const CsmArgs &args, int dtype_f32, hipStream_t stream) {
+int launch_csm(const CsmArgs &args, int dtype, hipStream_t stream) {
   const int64_t total = args.num_slices * (int64_t)args.units;
   const int prep_blocks = 1 + (int)std::min<int64_t>(1024, (total + 255) / 256);
   hipLaunchKernelGGL(csm_prep, dim3(prep_blocks), dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (total == 0) return 0;
-  if (dtype_f32)
+  if (dtype == kDtypeF32)
     hipLaunchKernelGGL(csm_round_f32, dim3((uint32_t)total), dim3(256), 0, stream, args);
+  else if (dtype == kDtypeF16)
+    hipLaunchKernelGGL(csm_round_f16, dim3((uint32_t)total), dim3(kBf16Threads), 0, stream, args);
   else
     hipLaunchKernelGGL(csm_round_bf16, dim3((uint32_t)total), dim3(kBf16Threads), 0, stream, args);
   e = hipGetLastError();

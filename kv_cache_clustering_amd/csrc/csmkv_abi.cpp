@@ -20,11 +20,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int elem_bytes(int32_t dtype) { return dtype == CSMKV_BF16 ? 2 : 4; }
+int elem_bytes(int32_t dtype) { return dtype == CSMKV_F32 ? 4 : 2; }
 
 int check_cache(const csmkv_cache *c) {
   if (c == nullptr) return CSMKV_EINVAL;
-  if (c->dtype != CSMKV_BF16 && c->dtype != CSMKV_F32) return CSMKV_EDTYPE;
+  if (c->dtype != CSMKV_BF16 && c->dtype != CSMKV_F32 && c->dtype != CSMKV_F16)
+    return CSMKV_EDTYPE;
   if (c->num_slices < 0 || c->cap < 1 || c->d < 1) return CSMKV_EINVAL;
   if (c->max_len < 0 || (int64_t)c->max_len > c->cap) return CSMKV_EINVAL;
   if (c->d != kHeadDim) return CSMKV_EUNSUPPORTED;
@@ -123,7 +124,7 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
   a.tap_sel = tap_sel;
   a.tap_src = tap_src;
   if (S == 0) return CSMKV_OK;
-  const int e = csmkv::launch_csm(a, src->dtype == CSMKV_F32, static_cast<hipStream_t>(stream));
+  const int e = csmkv::launch_csm(a, src->dtype, static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
 }
 
@@ -166,7 +167,7 @@ const char *csmkv_status_string(int status) {
   }
 }
 
-int csmkv_version(void) { return 101; }
+int csmkv_version(void) { return 102; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
   if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
@@ -258,7 +259,7 @@ int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t 
   a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
   a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
   a.part = reinterpret_cast<float *>(w + lay.part);
-  const int e = csmkv::launch_decode(a, cache->dtype == CSMKV_F32, G, items,
+  const int e = csmkv::launch_decode(a, cache->dtype, G, items,
                                      static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
 }

@@ -95,6 +95,16 @@ __device__ __forceinline__ float seg_dot(u32x4 k, const u32x4 &q, __bf16 *) {
   }
   return s;
 }
+__device__ __forceinline__ float seg_dot(u32x4 k, const u32x4 &q, _Float16 *) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t kw = k[i], qw = q[i];
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, kw), __builtin_bit_cast(f16x2, qw), s,
+                               false);
+  }
+  return s;
+}
 __device__ __forceinline__ float seg_dot(u32x4 k, const u32x4 &q, float *) {
   float s = 0.f;
 #pragma unroll
@@ -106,6 +116,14 @@ __device__ __forceinline__ void seg_to_f32(u32x4 v, float *o, __bf16 *) {
   for (int i = 0; i < 4; ++i) {
     o[2 * i] = bf_lo(v[i]);
     o[2 * i + 1] = bf_hi(v[i]);
+  }
+}
+__device__ __forceinline__ void seg_to_f32(u32x4 v, float *o, _Float16 *) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    o[2 * i] = f16_lo(w);
+    o[2 * i + 1] = f16_hi(w);
   }
 }
 __device__ __forceinline__ void seg_to_f32(u32x4 v, float *o, float *) {
@@ -380,12 +398,14 @@ int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
   return num_slices * (int64_t)((max_len + ts - 1) / ts);
 }
 
-int launch_decode(const DecArgs &a, int dtype_f32, int G, int64_t max_items, hipStream_t st) {
+int launch_decode(const DecArgs &a, int dtype, int G, int64_t max_items, hipStream_t st) {
   hipLaunchKernelGGL(dec_prep, dim3(1), dim3(1024), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_items, 256 * 8));
-  int rc = dtype_f32 ? launch_dec_t<float>(a, G, grid, st) : launch_dec_t<__bf16>(a, G, grid, st);
+  int rc = dtype == kDtypeF32   ? launch_dec_t<float>(a, G, grid, st)
+           : dtype == kDtypeF16 ? launch_dec_t<_Float16>(a, G, grid, st)
+                                : launch_dec_t<__bf16>(a, G, grid, st);
   if (rc) return rc;
   const dim3 cg((uint32_t)a.num_slices);
   switch (G) {

@@ -9,6 +9,8 @@ namespace csmkv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kHeadDim = 128;        // the kernels are built for d = 128
@@ -23,6 +25,14 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4
 // bf16 pair packed in one dword -> fp32 (exact)
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp16 pair packed in one dword -> fp32 (exact)
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
 
 // fp32 -> bf16 bits, round to nearest, ties to even (NaN -> quiet NaN)
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {

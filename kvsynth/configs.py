@@ -16,7 +16,7 @@ class Workload:
     H_kv: int
     H_q: int
     d: int
-    dtype: str                      # storage / compute input type: "bf16" or "f32"
+    dtype: str                      # storage / compute input type: "bf16", "f16" or "f32"
     ctx: int                        # prefill length n
     steps: int                      # Gamma: maximum decode length
     cap_extra: int                  # capacity beyond ctx reserved for appends

@@ -101,7 +101,7 @@ def _ar1_scan_torch(x, rho):
 
 def _torch_dtype(w):
     import torch
-    return {"bf16": torch.bfloat16, "f32": torch.float32}[w.dtype]
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
 
 
 def make_cache(w, device, ctx=None, batch_slices=32, with_appends=True):

@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _storage(t):
-    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+    return {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[t.dtype]
 
 
 def run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask=None, sample=None, max_len=None):
@@ -56,6 +56,43 @@ def test_small_caches_bf16(lib, dev, c, r, n1, n2):
     rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
     print(rep)
     parity.check_report(rep, near_bar=5e-3)
+
+
+@pytest.mark.parametrize("c,r,n1,n2", [(256, 0.5, 16, 64), (256, 1.0, 16, 64), (64, 0.77, 3, 5),
+                                       (37, 0.5, 16, 64), (3, 1.0, 1, 1)])
+def test_small_caches_fp16(lib, dev, c, r, n1, n2):
+    """fp16 storage: fp16 MFMA similarity, merges rounded to fp16 (round to nearest even)."""
+    K, V, N, lens = host_cache(len(LENS), 2100, LENS, dtype=torch.float16, seed=c * 5 + 1,
+                               degrees=True)
+    mask = np.zeros(len(LENS), np.uint8)
+    mask[6] = 1
+    rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
+    print(rep)
+    parity.check_report(rep, near_bar=5e-3)
+
+
+def test_fp16_in_place_equals_out_of_place_and_decode(lib, dev):
+    """fp16: the in-place round equals the out-of-place round bit for bit; decode attention
+    over the result matches the oracle."""
+    from oracle import attention as oatt
+    S, cap = 8, 3000
+    lens = [2900, 3000, 17, 1500, 0, 2222, 256 + 80, 999]
+    K, V, N, L = (t.to(dev) for t in host_cache(S, cap, lens, dtype=torch.float16, seed=41,
+                                                 degrees=True))
+    Ko, Vo, No, Lo = torch.empty_like(K), torch.empty_like(V), torch.empty_like(N), torch.empty_like(L)
+    lib.csm_compress_into(K, V, N, L, Ko, Vo, No, Lo, 16, 64, 256, 0.5)
+    lib.csm_compress(K, V, N, L, 16, 64, 256, 0.5)
+    assert torch.equal(L, Lo)
+    for z in range(S):
+        s = int(L[z])
+        assert torch.equal(K[z, :s], Ko[z, :s]) and torch.equal(V[z, :s], Vo[z, :s])
+        assert torch.equal(N[z, :s], No[z, :s])
+    H_q, H_kv = 8, 2
+    q = torch.randn((S // H_kv, H_q, 128), generator=torch.Generator().manual_seed(2)).half()
+    O = lib.decode_attn_logn(q.to(dev), K, V, N, L, H_q, H_kv).cpu().double().numpy()
+    ref = oatt.decode_attn_logn(parity.to_f64(q), parity.to_f64(K.cpu()), parity.to_f64(V.cpu()),
+                                N.cpu().numpy().astype(np.int64), L.cpu().numpy(), H_q, H_kv)
+    assert float(np.abs(O - ref).max()) < 1e-4
 
 
 def test_small_caches_fp32(lib, dev):

@@ -15,12 +15,13 @@ import torch
 
 from oracle import bf16 as obf16
 from oracle import csm as ocsm
+from oracle import fp16 as of16
 
 NEAR = 1e-5
 
 
 def to_f64(t):
-    """Stored cache values (bf16 or fp32 tensor) -> exact fp64 numpy array."""
+    """Stored cache values (bf16, fp16 or fp32 tensor) -> exact fp64 numpy array."""
     if t.dtype == torch.bfloat16:
         return obf16.bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
     return t.cpu().double().numpy()
@@ -41,8 +42,14 @@ def max_ulp_bf16(gpu_vals, oracle_vals):
 ABS_FLOOR = 2.0 ** -20
 
 
+def ordered_f16(bits):
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
 def check_values(rep, gpu_vals, oracle_vals, storage):
-    """Merged values agree within one bf16 ulp of the oracle's value.  Where a weighted mean
+    """Merged values agree within one ulp of the storage format (bf16 steps for bf16 and
+    fp32 storage, fp16 steps for fp16) of the oracle's value.  Where a weighted mean
     cancels to a value far below its terms, fp32 accumulation error (about 2**-24 of the
     terms) can exceed one ulp of the tiny result; such elements pass when the absolute
     difference is below 2**-20 and are counted in rep.abs_floor_used."""
@@ -56,6 +63,10 @@ def check_values(rep, gpu_vals, oracle_vals, storage):
         ulp = np.abs(ordered_bf16(obf16.f64_to_bits(g)) - ordered_bf16(obf16.f64_to_bits(o)))
         rep.max_ulp = max(rep.max_ulp, int(ulp.max()))
         bad = ulp > 1
+    elif storage == "f16":
+        ulp = np.abs(ordered_f16(of16.f64_to_bits(g)) - ordered_f16(of16.f64_to_bits(o)))
+        rep.max_ulp = max(rep.max_ulp, int(ulp.max()))
+        bad = ulp > 1
     else:
         _, e = np.frexp(o)
         ulp_bf16 = np.ldexp(1.0, np.maximum(e, -125) - 8)
@@ -63,7 +74,7 @@ def check_values(rep, gpu_vals, oracle_vals, storage):
     floor_ok = bad & (diff <= ABS_FLOOR)
     rep.abs_floor_used += int(floor_ok.sum())
     hard = bad & ~floor_ok
-    assert not hard.any(), ("K/V differ by more than one bf16 ulp", float(diff[hard].max()))
+    assert not hard.any(), ("K/V differ by more than one ulp", storage, float(diff[hard].max()))
 
 
 def max_ulp_f32(gpu_vals, oracle_vals):

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.version() == 101
+    assert lib.version() == 102
     for code in range(-6, 1):
         assert lib.status_string(code).startswith("CSMKV_")
     assert "unknown" in lib.status_string(-99)

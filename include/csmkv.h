@@ -60,7 +60,7 @@ typedef enum { CSMKV_BF16 = 0, CSMKV_F32 = 1, CSMKV_F16 = 2 } csmkv_dtype;
 typedef struct {
   int64_t num_slices; /* number of (batch, layer, kv-head) slices, >= 0 */
   int64_t cap;        /* rows allocated per slice, >= 1 */
-  int32_t d;          /* head dimension; the kernels are built for d = 128 */
+  int32_t d;          /* head dimension: 64 or 128 (other values: CSMKV_EUNSUPPORTED) */
   int32_t dtype;      /* csmkv_dtype of K, V (and q) */
   int32_t max_len;    /* host-known bound on every lens[] entry, 0 <= max_len <= cap;
                          sizes the launch grids (entries above it are device errors) */

@@ -6,9 +6,9 @@
 
 namespace csmkv {
 
-template <typename T, int NT = 256>
+template <typename T, int NT = 256, int D = 128>
 struct Tile {
-  static constexpr int ROWB = kHeadDim * (int)sizeof(T);  // bytes per row
+  static constexpr int ROWB = D * (int)sizeof(T);         // bytes per row (head dim D)
   static constexpr int SEGS = ROWB / 16;                  // 16-byte segments per row
   static constexpr int RPI = NT / SEGS;                   // rows covered by one block-wide load
   static constexpr int NLD = kMaxChunk / RPI;             // loads per thread for 256 rows
@@ -94,12 +94,12 @@ __device__ __forceinline__ u32x4 seg_pack(const float *o, float *) {
 
 // S^T tiles for one wave: acc[i][q] = <key of B row ((tl0 + i)*32 + row_q), key of A row a>
 // for NTL consecutive 32-row B tiles starting at tl0.
-template <int NTL = 4>
+template <int NTL, int D>
 __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
                                          __bf16 *, int tl0 = 0) {
-  constexpr int ROWB = Tile<__bf16>::ROWB;
+  constexpr int ROWB = Tile<__bf16, 256, D>::ROWB;
 #pragma unroll
-  for (int kk = 0; kk < kHeadDim / 16; ++kk) {
+  for (int kk = 0; kk < D / 16; ++kk) {
     const int seg = 2 * kk + h;
     u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
     bf16x8 bop = __builtin_bit_cast(bf16x8, braw);
@@ -112,12 +112,12 @@ __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h
     }
   }
 }
-template <int NTL = 4>
+template <int NTL, int D>
 __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
                                          _Float16 *, int tl0 = 0) {
-  constexpr int ROWB = Tile<_Float16>::ROWB;
+  constexpr int ROWB = Tile<_Float16, 256, D>::ROWB;
 #pragma unroll
-  for (int kk = 0; kk < kHeadDim / 16; ++kk) {
+  for (int kk = 0; kk < D / 16; ++kk) {
     const int seg = 2 * kk + h;
     u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
     f16x8 bop = __builtin_bit_cast(f16x8, braw);
@@ -130,14 +130,14 @@ __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h
     }
   }
 }
-template <int NTL = 4>
+template <int NTL, int D>
 __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h, f32x16 *acc,
                                          float *, int tl0 = 0) {
-  constexpr int ROWB = Tile<float>::ROWB;
+  constexpr int ROWB = Tile<float, 256, D>::ROWB;
   // Half-wave h supplies elements 8q + 4h + i at k-step 4q + i: every element is used
   // once and both operands use the same assignment.
 #pragma unroll 2
-  for (int q = 0; q < kHeadDim / 8; ++q) {
+  for (int q = 0; q < D / 8; ++q) {
     const int seg = 2 * q + h;
     u32x4 braw = *reinterpret_cast<const u32x4 *>(tile + lds_swz(2 * a, seg, ROWB));
 #pragma unroll
@@ -155,10 +155,10 @@ __device__ __forceinline__ void sim_tile(const char *tile, int a, int col, int h
 // Copy `nrows` rows (K, V, N) from src to dst in ascending blocks of ROWS rows.  Each block
 // is fully read before any of it is written, so dst <= src (a shift to lower rows) is safe
 // in place.
-template <typename T, int NT = 256, int ROWS = kMaxChunk>
+template <typename T, int NT, int D, int ROWS = kMaxChunk>
 __device__ void copy_rows(const char *Ks, const char *Vs, const int32_t *Ns, char *Kd, char *Vd,
                           int32_t *Nd, int nrows) {
-  using TL = Tile<T, NT>;
+  using TL = Tile<T, NT, D>;
   constexpr int NB = ROWS / TL::RPI;  // loads per thread per block of ROWS rows
   const int t = threadIdx.x, sg = t % TL::SEGS, r0 = t / TL::SEGS;
   for (int blk = 0; blk < nrows; blk += ROWS) {

@@ -28,7 +28,7 @@
 // without waiting on anything, so every wait ends.  Lower chunks never write into a
 // higher chunk's source.
 //
-// Per chunk (c <= 256, d = 128):
+// Per chunk (c <= 256, head dim d = 64 or 128):
 //   keys -> LDS tile (swizzled rows), fp32 norms from the same registers;
 //   S^T = B_keys . A_keys^T on MFMA (bf16: v_mfma_f32_32x32x16_bf16, fp32:
 //   v_mfma_f32_32x32x2_f32), wave w owning A columns [32w, 32w+32) and all B rows;
@@ -91,9 +91,9 @@ __global__ void csm_prep(CsmArgs a) {
   }
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int D>
 __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch, bool outl) {
-  using TL = Tile<T, NT>;
+  using TL = Tile<T, NT, D>;
   const int t = threadIdx.x;
   const int64_t kin = z * a.cap_in * TL::ROWB, kout = z * a.cap_out * TL::ROWB;
   const char *Ks = a.Kin + kin, *Vs = a.Vin + kin;
@@ -102,14 +102,14 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   int32_t *Nd = a.Nout + z * a.cap_out;
   int32_t *src = a.tap_src ? a.tap_src + z * a.cap_out : nullptr;
   if (nch == 0) {  // nothing to compress: lens unchanged, copy everything out of place
-    if (!a.in_place) copy_rows<T, NT>(Ks, Vs, Ns, Kd, Vd, Nd, s);
+    if (!a.in_place) copy_rows<T, NT, D>(Ks, Vs, Ns, Kd, Vd, Nd, s);
     if (src)
       for (int i = t; i < s; i += blockDim.x) src[i] = i;
     if (t == 0) a.lens_out[z] = s;
     return;
   }
   const int n1 = a.n1, n2 = a.n2, c = a.c;
-  if (!a.in_place) copy_rows<T, NT>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
+  if (!a.in_place) copy_rows<T, NT, D>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
   if (a.in_place && !outl && t == 0) {
     // the recent rows land in [s_new - n2, s_new): wait for chunks whose sources overlap it
     const int d0 = s_new - n2, d1 = s_new;
@@ -120,7 +120,7 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   }
   __syncthreads();
   const int64_t so = (int64_t)(s - n2), dof = (int64_t)(s_new - n2);
-  copy_rows<T, NT>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
+  copy_rows<T, NT, D>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
                Vd + dof * TL::ROWB, Nd + dof, n2);
   if (src) {
     for (int i = t; i < n1; i += blockDim.x) src[i] = i;
@@ -137,9 +137,9 @@ __device__ __forceinline__ uint64_t rank_key(float score, int aidx) {
   return ((uint64_t)ord << 8) | (uint64_t)(255 - aidx);
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int D>
 __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
-  using TL = Tile<T, NT>;
+  using TL = Tile<T, NT, D>;
   constexpr int ROWB = TL::ROWB, SEGS = TL::SEGS, RPI = TL::RPI, NLD = TL::NLD, EPS = TL::EPS;
   constexpr int NW = NT / 64;    // waves: 4 or 8
   constexpr int BT = 16 / NW;    // 32-row B tiles per wave in the similarity step
@@ -175,7 +175,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   const int s_new = a.s_out[z];
 
   if (u == a.units - 1) {
-    tail_unit<T, NT>(a, z, s, s_new, nch, outl);
+    tail_unit<T, NT, D>(a, z, s, s_new, nch, outl);
     return;
   }
   if (u >= nch) return;
@@ -220,8 +220,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     for (int i = 0; i < NLD; ++i) {
       const int r = r0 + RPI * i;
       *reinterpret_cast<u32x4 *>(tile + lds_swz(r, sg, ROWB)) = kreg[i];
-      float ss = row16_sum(seg_sumsq(kreg[i], tsel));
-      if (SEGS == 32) ss += __shfl_xor(ss, 16);
+      const float ss = lanes_sum<SEGS>(seg_sumsq(kreg[i], tsel));
       if (sg == 0) {
         const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
         if (r & 1) s_invB[r >> 1] = inv; else s_invA[r >> 1] = inv;
@@ -243,7 +242,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     for (int tl = 0; tl < BT; ++tl)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[tl][q] = 0.f;
-    sim_tile<BT>(tile, aidx, col, h, acc, tsel, bq * BT);
+    sim_tile<BT, D>(tile, aidx, col, h, acc, tsel, bq * BT);
     // cosine = (dot * (1/|b|)) * (1/|a|); lowest B index wins a tie (ascending order, strict >)
     const float ia = s_invA[aidx];
     float best = -__builtin_inff();
@@ -457,31 +456,56 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
 }
 
-// bf16: 512 threads and 78 KB of LDS per workgroup, two workgroups (four waves per SIMD) per CU.
-constexpr int kBf16Threads = 512;
-__global__ void __launch_bounds__(kBf16Threads, 2) csm_round_bf16(CsmArgs a) {
-  csm_round_body<__bf16, kBf16Threads>(a);
+// Head dim 128.  bf16 / fp16: 512 threads and 78 KB of LDS per workgroup, two workgroups
+// (four waves per SIMD) per CU.  fp32: the 128 KB key tile allows one workgroup per CU.
+constexpr int kWideThreads = 512;
+__global__ void __launch_bounds__(kWideThreads, 2) csm_round_bf16(CsmArgs a) {
+  csm_round_body<__bf16, kWideThreads, 128>(a);
 }
-__global__ void __launch_bounds__(kBf16Threads, 2) csm_round_f16(CsmArgs a) {
-  csm_round_body<_Float16, kBf16Threads>(a);
+__global__ void __launch_bounds__(kWideThreads, 2) csm_round_f16(CsmArgs a) {
+  csm_round_body<_Float16, kWideThreads, 128>(a);
 }
-// fp32: the 128 KB key tile allows one workgroup per CU.
-__global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) { csm_round_body<float, 256>(a); }
+__global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) {
+  csm_round_body<float, 256, 128>(a);
+}
+// Head dim 64: half the tile.  bf16 / fp16: 46 KB of LDS, so three 512-thread workgroups fit
+// a CU when a thread holds at most 85 VGPRs (six waves per SIMD); fp32: 79 KB, two per CU.
+__global__ void __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
+csm_round_bf16_d64(CsmArgs a) {
+  csm_round_body<__bf16, kWideThreads, 64>(a);
+}
+__global__ void __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
+csm_round_f16_d64(CsmArgs a) {
+  csm_round_body<_Float16, kWideThreads, 64>(a);
+}
+__global__ void __launch_bounds__(kWideThreads, 2) csm_round_f32_d64(CsmArgs a) {
+  csm_round_body<float, kWideThreads, 64>(a);
+}
 
-// Host-side launcher used by the C ABI.  Returns 0 or a hipError_t value.
-int launch_csm(const CsmArgs &args, int dtype, hipStream_t stream) {
+// Host-side launcher used by the C ABI (d is 64 or 128).  Returns 0 or a hipError_t value.
+int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
   const int64_t total = args.num_slices * (int64_t)args.units;
   const int prep_blocks = 1 + (int)std::min<int64_t>(1024, (total + 255) / 256);
   hipLaunchKernelGGL(csm_prep, dim3(prep_blocks), dim3(256), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (total == 0) return 0;
-  if (dtype == kDtypeF32)
-    hipLaunchKernelGGL(csm_round_f32, dim3((uint32_t)total), dim3(256), 0, stream, args);
-  else if (dtype == kDtypeF16)
-    hipLaunchKernelGGL(csm_round_f16, dim3((uint32_t)total), dim3(kBf16Threads), 0, stream, args);
-  else
-    hipLaunchKernelGGL(csm_round_bf16, dim3((uint32_t)total), dim3(kBf16Threads), 0, stream, args);
+  const dim3 grid((uint32_t)total), wide(kWideThreads);
+  if (d == 64) {
+    if (dtype == kDtypeF32)
+      hipLaunchKernelGGL(csm_round_f32_d64, grid, wide, 0, stream, args);
+    else if (dtype == kDtypeF16)
+      hipLaunchKernelGGL(csm_round_f16_d64, grid, wide, 0, stream, args);
+    else
+      hipLaunchKernelGGL(csm_round_bf16_d64, grid, wide, 0, stream, args);
+  } else {
+    if (dtype == kDtypeF32)
+      hipLaunchKernelGGL(csm_round_f32, grid, dim3(256), 0, stream, args);
+    else if (dtype == kDtypeF16)
+      hipLaunchKernelGGL(csm_round_f16, grid, wide, 0, stream, args);
+    else
+      hipLaunchKernelGGL(csm_round_bf16, grid, wide, 0, stream, args);
+  }
   e = hipGetLastError();
   return (int)e;
 }

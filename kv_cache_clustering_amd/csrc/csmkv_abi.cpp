@@ -14,7 +14,6 @@ namespace {
 
 constexpr int64_t kMaxCap = int64_t(1) << 24;  // degrees and row indices stay exact in fp32 / int32
 constexpr size_t kAlign = 256;
-constexpr int kHeadDim = 128;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -28,7 +27,7 @@ int check_cache(const csmkv_cache *c) {
     return CSMKV_EDTYPE;
   if (c->num_slices < 0 || c->cap < 1 || c->d < 1) return CSMKV_EINVAL;
   if (c->max_len < 0 || (int64_t)c->max_len > c->cap) return CSMKV_EINVAL;
-  if (c->d != kHeadDim) return CSMKV_EUNSUPPORTED;
+  if (c->d != 64 && c->d != 128) return CSMKV_EUNSUPPORTED;
   if (c->cap > kMaxCap) return CSMKV_EUNSUPPORTED;
   return CSMKV_OK;
 }
@@ -124,7 +123,7 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
   a.tap_sel = tap_sel;
   a.tap_src = tap_src;
   if (S == 0) return CSMKV_OK;
-  const int e = csmkv::launch_csm(a, src->dtype, static_cast<hipStream_t>(stream));
+  const int e = csmkv::launch_csm(a, src->dtype, src->d, static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
 }
 
@@ -138,7 +137,7 @@ DecLayout dec_layout(const csmkv_cache *c, int G) {
   L.item_off = kAlign;
   L.item_zp = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
   L.part = L.item_zp + align_up((size_t)items * 16);
-  L.total = L.part + align_up((size_t)items * G * (4 + kHeadDim) * 4);
+  L.total = L.part + align_up((size_t)items * G * (4 + c->d) * 4);
   return L;
 }
 
@@ -167,7 +166,7 @@ const char *csmkv_status_string(int status) {
   }
 }
 
-int csmkv_version(void) { return 102; }
+int csmkv_version(void) { return 103; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
   if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
@@ -259,7 +258,7 @@ int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t 
   a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
   a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
   a.part = reinterpret_cast<float *>(w + lay.part);
-  const int e = csmkv::launch_decode(a, cache->dtype, G, items,
+  const int e = csmkv::launch_decode(a, cache->dtype, cache->d, G, items,
                                      static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
 }

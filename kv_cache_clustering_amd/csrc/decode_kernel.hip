@@ -28,7 +28,9 @@ namespace csmkv {
 
 constexpr int kTSplitMin = 512, kTSplitMax = 1024;  // tokens per work item
 constexpr int64_t kItemTarget = 2048;               // work items a call aims for
-constexpr int kPartWidth = 4 + kHeadDim;  // floats per (item, head) partial: 16-byte rows
+// floats per (item, head) partial: (max, sum, 0, 0, o[d]), 16-byte aligned rows
+template <int D>
+constexpr int part_width() { return 4 + D; }
 constexpr int kDecThreads = 256;
 
 
@@ -73,9 +75,9 @@ __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
   if (t == (int)blockDim.x - 1) a.item_off[S] = before + incl;
 }
 
-template <typename T, int G>
+template <typename T, int G, int D>
 struct DecTile {
-  static constexpr int ROWB = kHeadDim * (int)sizeof(T);
+  static constexpr int ROWB = D * (int)sizeof(T);
   static constexpr int LPR = ROWB / 16;     // lanes per row
   static constexpr int RPW = 64 / LPR;      // rows per wave-wide load
   static constexpr int NR = G >= 8 ? 2 : 4;  // wave loads per sub-block (8 heads: fewer, no spills)
@@ -141,10 +143,10 @@ struct DecStage {
   int32_t n[NR];
 };
 
-template <typename T, int G>
-__device__ __forceinline__ void dec_load(DecStage<DecTile<T, G>::NR> &st, const char *Kz, const char *Vz,
+template <typename T, int G, int D>
+__device__ __forceinline__ void dec_load(DecStage<DecTile<T, G, D>::NR> &st, const char *Kz, const char *Vz,
                                          const int32_t *Nz, int sb, int we, int rw, int sg) {
-  using DT = DecTile<T, G>;
+  using DT = DecTile<T, G, D>;
 #pragma unroll
   for (int i = 0; i < DT::NR; ++i) {
     const int tok = sb + DT::RPW * i + rw;
@@ -160,11 +162,11 @@ __device__ __forceinline__ void dec_load(DecStage<DecTile<T, G>::NR> &st, const 
 }
 
 // Online-softmax update of (mrun, lrun, o) with one sub-block, base 2.
-template <typename T, int G>
-__device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G>::NR> &st, int sb, int we, int rw,
+template <typename T, int G, int D>
+__device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR> &st, int sb, int we, int rw,
                                             const u32x4 *qv, float scale_log2, float *mrun,
-                                            float *lrun, float (*o)[DecTile<T, G>::EPL]) {
-  using DT = DecTile<T, G>;
+                                            float *lrun, float (*o)[DecTile<T, G, D>::EPL]) {
+  using DT = DecTile<T, G, D>;
   constexpr int EPL = DT::EPL;
   T *tsel = nullptr;
   const float NEG_INF = -__builtin_inff();
@@ -175,8 +177,7 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G>::NR> &s
     const float ln = __builtin_amdgcn_logf((float)st.n[i]);  // log2
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float d = row16_sum(seg_dot(st.k[i], qv[h], tsel));
-      if (DT::LPR == 32) d += __shfl_xor(d, 16);
+      const float d = lanes_sum<DT::LPR>(seg_dot(st.k[i], qv[h], tsel));
       zs[i][h] = ok ? fmaf(d, scale_log2, ln) : NEG_INF;
     }
   }
@@ -185,8 +186,8 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G>::NR> &s
     float mx = zs[0][h];
 #pragma unroll
     for (int i = 1; i < DT::NR; ++i) mx = fmaxf(mx, zs[i][h]);
-    if (DT::RPW == 4) mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+    for (int o2 = DT::LPR; o2 < 64; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
     const float mn = fmaxf(mrun[h], mx);
     const float alpha = fast_exp2(mrun[h] - mn);
     mrun[h] = mn;
@@ -208,11 +209,11 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G>::NR> &s
   }
 }
 
-template <typename T, int G>
+template <typename T, int G, int D>
 __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
-  using DT = DecTile<T, G>;
+  using DT = DecTile<T, G, D>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
-  constexpr int PW = kPartWidth;  // (max, sum, pad, pad, o[d]) per head
+  constexpr int PW = part_width<D>();  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][G][PW];
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int sg = l % LPR, rw = l / LPR;
@@ -231,12 +232,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
     // two register stages: the next sub-block loads while the current one is computed
     DecStage<DT::NR> A, B;
-    if (wb < we) dec_load<T, G>(A, Kz, Vz, Nz, wb, we, rw, sg);
+    if (wb < we) dec_load<T, G, D>(A, Kz, Vz, Nz, wb, we, rw, sg);
     // this lane's q segment for each head of the group
     u32x4 qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h)
-      qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + h) * (int64_t)kHeadDim) * sizeof(T) + sg * 16);
+      qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + h) * (int64_t)D) * sizeof(T) + sg * 16);
     float mrun[G], lrun[G], o[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -247,22 +248,21 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     }
     for (int sb = wb; sb < we; sb += 2 * SUB) {
       const int sb1 = sb + SUB;
-      if (sb1 < we) dec_load<T, G>(B, Kz, Vz, Nz, sb1, we, rw, sg);
-      dec_compute<T, G>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
+      if (sb1 < we) dec_load<T, G, D>(B, Kz, Vz, Nz, sb1, we, rw, sg);
+      dec_compute<T, G, D>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
       if (sb1 >= we) break;
-      if (sb1 + SUB < we) dec_load<T, G>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
-      dec_compute<T, G>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
+      if (sb1 + SUB < we) dec_load<T, G, D>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
+      dec_compute<T, G, D>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
     }
     // sum the row groups of the wave (they hold different tokens, same segment)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (RPW == 4) lrun[h] += __shfl_xor(lrun[h], 16);
-      lrun[h] += __shfl_xor(lrun[h], 32);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        if (RPW == 4) o[h][e] += __shfl_xor(o[h][e], 16);
-        o[h][e] += __shfl_xor(o[h][e], 32);
-      }
+      for (int o2 = LPR; o2 < 64; o2 <<= 1) lrun[h] += __shfl_xor(lrun[h], o2);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+#pragma unroll
+        for (int o2 = LPR; o2 < 64; o2 <<= 1) o[h][e] += __shfl_xor(o[h][e], o2);
     }
     if (rw == 0) {
 #pragma unroll
@@ -305,13 +305,14 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
 // 2. each thread takes 4 output elements of one head and one of 8/G item groups and sums the
 // rescaled partials, four independent items per step; 3. the item groups are summed through
 // LDS and divided.
-template <int G>
+template <int G, int D>
 __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
-  constexpr int PW = kPartWidth;
-  constexpr int COLS = 32 * G;    // 4-element columns over the G heads
+  constexpr int PW = part_width<D>();
+  constexpr int CPH = D / 4;      // 4-element columns per head
+  constexpr int COLS = CPH * G;   // columns over the G heads
   constexpr int IG = 256 / COLS;  // item groups
   __shared__ float s_mx[4][G];
-  __shared__ __attribute__((aligned(16))) float s_acc[IG][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_acc[IG][G][D];
   __shared__ float s_l[IG][G];
   const int64_t z = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
@@ -328,7 +329,7 @@ __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
     if (l < G) s_mx[w][l] = m;
   }
   __syncthreads();
-  const int col = t % COLS, grp = t / COLS, h = col / 32, e4 = (col % 32) * 4;
+  const int col = t % COLS, grp = t / COLS, h = col / CPH, e4 = (col % CPH) * 4;
   const float M = fmaxf(fmaxf(s_mx[0][h], s_mx[1][h]), fmaxf(s_mx[2][h], s_mx[3][h]));
   float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
   auto add = [&](float m, float lsum, float4 o) {
@@ -362,28 +363,48 @@ __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
   *reinterpret_cast<float4 *>(&s_acc[grp][h][e4]) = make_float4(acc0, acc1, acc2, acc3);
   if (e4 == 0) s_l[grp][h] = L;
   __syncthreads();
-  for (int i = t; i < G * kHeadDim; i += 256) {
-    const int hh = i / kHeadDim, d = i % kHeadDim;
+  for (int i = t; i < G * D; i += 256) {
+    const int hh = i / D, d = i % D;
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int q = 0; q < IG; ++q) {
       num += s_acc[q][hh][d];
       den += s_l[q][hh];
     }
-    a.O[(g * a.H_q + kvh * G + hh) * (int64_t)kHeadDim + d] = den > 0.f ? num / den : 0.f;
+    a.O[(g * a.H_q + kvh * G + hh) * (int64_t)D + d] = den > 0.f ? num / den : 0.f;
   }
 }
 
-template <typename T>
+template <typename T, int D>
 static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((dec_split<T, 1>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((dec_split<T, 2>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((dec_split<T, 4>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_split<T, 8>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((dec_split<T, 1, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((dec_split<T, 2, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((dec_split<T, 4, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_split<T, 8, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+template <int D>
+static int launch_combine(const DecArgs &a, int G, hipStream_t st) {
+  const dim3 cg((uint32_t)a.num_slices);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((dec_combine<1, D>), cg, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((dec_combine<2, D>), cg, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((dec_combine<4, D>), cg, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_combine<8, D>), cg, dim3(256), 0, st, a); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+template <int D>
+static int launch_split(const DecArgs &a, int dtype, int G, int grid, hipStream_t st) {
+  return dtype == kDtypeF32   ? launch_dec_t<float, D>(a, G, grid, st)
+         : dtype == kDtypeF16 ? launch_dec_t<_Float16, D>(a, G, grid, st)
+                              : launch_dec_t<__bf16, D>(a, G, grid, st);
 }
 
 int32_t dec_split_tokens(int64_t num_slices, int32_t max_len) {
@@ -398,24 +419,14 @@ int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
   return num_slices * (int64_t)((max_len + ts - 1) / ts);
 }
 
-int launch_decode(const DecArgs &a, int dtype, int G, int64_t max_items, hipStream_t st) {
+int launch_decode(const DecArgs &a, int dtype, int d, int G, int64_t max_items, hipStream_t st) {
   hipLaunchKernelGGL(dec_prep, dim3(1), dim3(1024), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_items, 256 * 8));
-  int rc = dtype == kDtypeF32   ? launch_dec_t<float>(a, G, grid, st)
-           : dtype == kDtypeF16 ? launch_dec_t<_Float16>(a, G, grid, st)
-                                : launch_dec_t<__bf16>(a, G, grid, st);
+  int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
   if (rc) return rc;
-  const dim3 cg((uint32_t)a.num_slices);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(dec_combine<1>, cg, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(dec_combine<2>, cg, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(dec_combine<4>, cg, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(dec_combine<8>, cg, dim3(256), 0, st, a); break;
-    default: return (int)hipErrorInvalidValue;
-  }
-  return (int)hipGetLastError();
+  return d == 64 ? launch_combine<64>(a, G, st) : launch_combine<128>(a, G, st);
 }
 
 // ------------------------------------------------------------------ append

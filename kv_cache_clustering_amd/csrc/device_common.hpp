@@ -13,7 +13,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kHeadDim = 128;        // the kernels are built for d = 128
 constexpr int kMaxChunk = 256;       // largest chunk c (128 x 128 similarity tile)
 constexpr int kDeviceError = -6;     // CSMKV_EDEVICE
 
@@ -47,9 +46,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Byte offset of 16-byte segment `seg` of row `row` in an LDS tile with `rowbytes` per row.
 // The XOR spreads the rows a half-wave reads at one segment (consecutive A or B rows,
-// i.e. rows 2i or 2i+1) over distinct bank groups.
+// i.e. rows 2i or 2i+1) over distinct bank groups; it stays inside the row (at most 16
+// segments are permuted).
 __device__ __forceinline__ int lds_swz(int row, int seg, int rowbytes) {
-  return row * rowbytes + ((seg ^ ((row >> 1) & 15)) << 4);
+  const int mask = (rowbytes / 16 - 1) & 15;
+  return row * rowbytes + ((seg ^ ((row >> 1) & mask)) << 4);
 }
 
 // Sum over the 16 lanes of a DPP row; every lane of the row receives the sum.
@@ -62,6 +63,17 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f<0x4e>(x);   // quad_perm [2,3,0,1]
   x += dpp_f<0x141>(x);  // row_half_mirror
   x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+// Sum over aligned groups of LANES (8, 16 or 32) lanes; every lane of a group receives it.
+template <int LANES>
+__device__ __forceinline__ float lanes_sum(float x) {
+  static_assert(LANES == 8 || LANES == 16 || LANES == 32, "8, 16 or 32 lanes");
+  x += dpp_f<0xb1>(x);
+  x += dpp_f<0x4e>(x);
+  x += dpp_f<0x141>(x);                    // now summed over 8 lanes
+  if (LANES >= 16) x += dpp_f<0x140>(x);  // 16
+  if (LANES == 32) x += __shfl_xor(x, 16);
   return x;
 }
 

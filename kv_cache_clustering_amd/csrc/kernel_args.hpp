@@ -61,8 +61,8 @@ struct AppArgs {
 constexpr int kDtypeBf16 = 0, kDtypeF32 = 1, kDtypeF16 = 2;
 
 // Each returns 0 or a hipError_t value.
-int launch_csm(const CsmArgs &args, int dtype, hipStream_t stream);
-int launch_decode(const DecArgs &a, int dtype, int G, int64_t max_items, hipStream_t st);
+int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream);
+int launch_decode(const DecArgs &a, int dtype, int d, int G, int64_t max_items, hipStream_t st);
 int launch_append(const AppArgs &a, hipStream_t st);
 // Tokens per decode work item for a geometry, and the upper bound on work items (sizes the
 // partial buffer).  Both depend only on the slice count and the host-known length bound.

@@ -229,3 +229,32 @@ def test_bad_length_sets_error_and_leaves_slice(lib, dev):
     assert int(Ld[0]) < 3000 and int(Ld[2]) < 3000
     ws = lib.csm_compress(Kd, Vd, Nd, Ld, 16, 64, 256, 0.5, max_len=3100)   # now valid
     assert lib.read_error(ws) == lib.OK
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("c,r,n1,n2", [(256, 0.5, 16, 64), (64, 0.77, 3, 5), (37, 1.0, 16, 64)])
+def test_small_caches_head_dim_64(lib, dev, dtype, c, r, n1, n2):
+    """Head dim 64: the same round on half-width rows (32-byte MFMA k-steps: 4 per tile)."""
+    K, V, N, lens = host_cache(len(LENS), 2100, LENS, d=64, dtype=dtype, seed=c + 64,
+                               degrees=True)
+    mask = np.zeros(len(LENS), np.uint8)
+    mask[1] = 1
+    rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
+    print(rep)
+    parity.check_report(rep, near_bar=5e-3)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_head_dim_64_in_place_equals_out_of_place(lib, dev, dtype):
+    S, cap = 6, 3000
+    lens = [2900, 3000, 17, 1500, 0, 336]
+    K, V, N, L = (t.to(dev) for t in host_cache(S, cap, lens, d=64, dtype=dtype, seed=5,
+                                                 degrees=True))
+    Ko, Vo, No, Lo = torch.empty_like(K), torch.empty_like(V), torch.empty_like(N), torch.empty_like(L)
+    lib.csm_compress_into(K, V, N, L, Ko, Vo, No, Lo, 16, 64, 256, 0.5)
+    lib.csm_compress(K, V, N, L, 16, 64, 256, 0.5)
+    assert torch.equal(L, Lo)
+    for z in range(S):
+        s = int(L[z])
+        assert torch.equal(K[z, :s], Ko[z, :s]) and torch.equal(V[z, :s], Vo[z, :s])
+        assert torch.equal(N[z, :s], No[z, :s])

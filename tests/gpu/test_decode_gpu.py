@@ -43,6 +43,29 @@ def test_ragged_lengths_random_degrees(lib, dev, dtype, H_q, H_kv):
             assert torch.all(O[g, kvh * G:(kvh + 1) * G] == 0)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("H_q,H_kv", [(8, 2), (4, 4), (16, 2)])
+def test_head_dim_64_ragged(lib, dev, dtype, H_q, H_kv):
+    """Head dim 64: 8 lanes per bf16/fp16 row (16 per fp32 row), scale 1/8."""
+    groups = 3
+    S = groups * H_kv
+    rng = np.random.default_rng(H_q + 64)
+    lens = [int(x) for x in rng.choice([0, 1, 511, 512, 513, 1500, 2600], size=S)]
+    lens[0] = 2600
+    K, V, N, L = host_cache(S, 2600, lens, d=64, dtype=dtype, seed=H_q + 1, degrees=True)
+    q = torch.randn((groups, H_q, 64), generator=torch.Generator().manual_seed(3)).to(dtype)
+    O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), L.to(dev), H_q, H_kv)
+    ref = _oracle_all(q, K, V, N, L, H_q, H_kv)
+    err = float(np.abs(O.cpu().double().numpy() - ref).max())
+    print(dtype, H_q, H_kv, "max abs", err)
+    assert err < (2e-5 if dtype == torch.float32 else 2e-4)
+    k = torch.randn((S, 64)).to(dtype).to(dev)
+    Kd, Vd, Nd, Ld = (t.to(dev) for t in (K, V, N, L))
+    Ld[0] = 2599
+    lib.kv_append(Kd, Vd, Nd, Ld, k, k)
+    assert int(Ld[0]) == 2600 and torch.equal(Kd[0, 2599], k[0]) and int(Nd[0, 2599]) == 1
+
+
 def _split_tokens(S, max_len):
     """The work-item size rule stated in the decode kernel: 512 tokens when that gives at most
     about 2048 items over the length bound, else 1024."""

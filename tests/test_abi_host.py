@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.version() == 102
+    assert lib.version() == 103
     for code in range(-6, 1):
         assert lib.status_string(code).startswith("CSMKV_")
     assert "unknown" in lib.status_string(-99)
@@ -52,7 +52,7 @@ def test_workspace_sizes(lib):
     ws = lib.raw.csm_compress_workspace_bytes(ctypes.byref(d), 16, 64, 256)
     assert ws >= 4 * (4 * units) + 2 * 4 * 4 and ws % 256 == 0
     assert lib.raw.csm_compress_workspace_bytes(ctypes.byref(d), 16, 64, 1) == 0
-    assert lib.raw.csm_compress_workspace_bytes(ctypes.byref(_desc(lib, d=64)), 16, 64, 256) == 0
+    assert lib.raw.csm_compress_workspace_bytes(ctypes.byref(_desc(lib, d=96)), 16, 64, 256) == 0
     dws = lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(d), 8, 2)
     assert dws >= 4 * 2 * (2 + 128) * 4 * 2
     assert lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(d), 6, 4) == 0
@@ -82,7 +82,7 @@ def test_compress_argument_validation(lib):
     assert _compress(lib, d, ws_bytes=16) == lib.EWORKSPACE
     assert _compress(lib, d, ws=ctypes.c_void_p((1 << 20) + 64)) == lib.EWORKSPACE
     assert _compress(lib, _desc(lib, dtype=7)) == lib.EDTYPE
-    assert _compress(lib, _desc(lib, d=64)) == lib.EUNSUPPORTED
+    assert _compress(lib, _desc(lib, d=96)) == lib.EUNSUPPORTED
     assert _compress(lib, _desc(lib, max_len=1001)) == lib.EINVAL
     assert _compress(lib, _desc(lib, cap=0, max_len=0)) == lib.EINVAL
     assert _compress(lib, _desc(lib, cap=(1 << 24) + 1, max_len=10)) == lib.EUNSUPPORTED

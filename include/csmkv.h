@@ -93,7 +93,9 @@ CSMKV_API size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t 
  *   merged A rows are removed and the slice is compacted in its original order;
  *   lens[z] becomes s - sum(m).  Similarities are decided in fp32 (bf16 products are
  *   exact, sums rounded in fp32).
- * Arguments: n1, n2 >= 0; 2 <= c <= 256; 0 <= r <= 1 (not NaN); outlier_mask is a device
+ * Arguments: n1, n2 >= 0; 2 <= c <= 512 (c > 256 needs bf16 or fp16 storage: the
+ *   similarity tile grows to 256 x 256 and the key tile to c * d * 2 bytes of LDS);
+ *   0 <= r <= 1 (not NaN); outlier_mask is a device
  *   [num_slices] uint8 array or NULL (no outliers); workspace: device memory of at least
  *   csm_compress_workspace_bytes() bytes, 256-byte aligned.  Its first int32 is the error
  *   word of this call.
@@ -120,8 +122,9 @@ CSMKV_API int csm_compress_into(const void *K_in, const void *V_in, const int32_
 /*
  * csm_compress_debug -- csm_compress (in place) that also records its decisions.
  * Not for timed runs.  Any tap may be NULL.
- *   best_b   : [num_slices][units][128] int32, per chunk the matched B index of each A
- *              row (-1 where the row does not exist); units = csm_compress_units().
+ *   best_b   : [num_slices][units][W] int32, per chunk the matched B index of each A
+ *              row (-1 where the row does not exist); units = csm_compress_units();
+ *              W = 128 for c <= 256, 256 for larger c.
  *   selected : same shape, uint8, 1 where the A row was merged.
  *   src_pos  : [num_slices][cap] int32, for each output row < new lens the input row it
  *              came from (entries at or beyond the new length are not written).

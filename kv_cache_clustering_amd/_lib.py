@@ -200,8 +200,9 @@ def csm_compress_debug(K, V, N, lens, n1=16, n2=64, c=256, r=0.5, outlier_mask=N
     desc = cache_desc(K, max_len)
     units = _lib.csm_compress_units(ctypes.byref(desc), n1, n2, c)
     S, cap = K.shape[0], K.shape[1]
-    best_b = torch.full((S, max(units, 1), 128), -1, dtype=torch.int32, device=K.device)
-    selected = torch.zeros((S, max(units, 1), 128), dtype=torch.uint8, device=K.device)
+    W = 128 if c <= 256 else 256  # A rows per chunk in the tap layout
+    best_b = torch.full((S, max(units, 1), W), -1, dtype=torch.int32, device=K.device)
+    selected = torch.zeros((S, max(units, 1), W), dtype=torch.uint8, device=K.device)
     src_pos = torch.full((S, cap), -1, dtype=torch.int32, device=K.device)
     ws = _workspace(_lib.csm_compress_workspace_bytes(ctypes.byref(desc), n1, n2, c), K.device,
                     workspace)

@@ -6,12 +6,12 @@
 
 namespace csmkv {
 
-template <typename T, int NT = 256, int D = 128>
+template <typename T, int NT = 256, int D = 128, int CMAX = kMaxChunk>
 struct Tile {
   static constexpr int ROWB = D * (int)sizeof(T);         // bytes per row (head dim D)
   static constexpr int SEGS = ROWB / 16;                  // 16-byte segments per row
   static constexpr int RPI = NT / SEGS;                   // rows covered by one block-wide load
-  static constexpr int NLD = kMaxChunk / RPI;             // loads per thread for 256 rows
+  static constexpr int NLD = CMAX / RPI;                  // loads per thread for CMAX rows
   static constexpr int EPS = 16 / (int)sizeof(T);         // elements per segment
 };
 

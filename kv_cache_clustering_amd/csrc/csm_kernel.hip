@@ -137,24 +137,36 @@ __device__ __forceinline__ uint64_t rank_key(float score, int aidx) {
   return ((uint64_t)ord << 8) | (uint64_t)(255 - aidx);
 }
 
-template <typename T, int NT, int D>
+// One unit of the round.  T: storage type; NT: threads; D: head dim; CMAX: chunk capacity
+// (256: A and B up to 128 rows; 512: up to 256).  NA = CMAX / 2 A rows; the A x B tile is
+// split over the waves as AG = NA / 32 column groups times NT / 64 / AG B parts.
+template <typename T, int NT, int D, int CMAX>
 __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
-  using TL = Tile<T, NT, D>;
+  using TL = Tile<T, NT, D, CMAX>;
   constexpr int ROWB = TL::ROWB, SEGS = TL::SEGS, RPI = TL::RPI, NLD = TL::NLD, EPS = TL::EPS;
-  constexpr int NW = NT / 64;    // waves: 4 or 8
-  constexpr int BT = 16 / NW;    // 32-row B tiles per wave in the similarity step
-  constexpr int NQ = NT / 128;   // parts of the rank count
-  static_assert(NW == 4 || NW == 8, "256 or 512 threads");
-  __shared__ __attribute__((aligned(16))) char tile[kMaxChunk * ROWB];
-  __shared__ __attribute__((aligned(16))) float s_invA[128], s_invB[128];  // 1 / max(|k|, eps)
-  __shared__ int32_t s_n[kMaxChunk];
-  __shared__ int32_t s_outrow[kMaxChunk];
-  __shared__ int32_t s_best[128], s_sel[128], s_cnt[128], s_wsum[128], s_off[128], s_list[128];
-  __shared__ int32_t s_cnt0[128], s_cnt1[128], s_rank[NQ][128];
-  __shared__ int32_t s_mrg[4][64], s_mcnt[4];
-  __shared__ __attribute__((aligned(16))) uint64_t s_key[128];  // rank keys, 0 = no edge
-  __shared__ float s_bsc[NW / 4][128];  // per B part: best score and index of every A row
-  __shared__ int32_t s_bix[NW / 4][128];
+  constexpr int NA = CMAX / 2;       // A (and B) rows per chunk at most
+  constexpr int NW = NT / 64;        // waves
+  constexpr int AG = NA / 32;        // 32-column A groups
+  constexpr int BP = NW / AG;        // B parts (waves per A group)
+  constexpr int BT = AG / BP;        // 32-row B tiles per wave
+  // B tiles per MFMA pass (bounds the live accumulators; d = 64 kernels run at 6 waves/SIMD)
+  constexpr int TP = (BT < 2 || D == 64) ? 1 : 2;
+  constexpr int NQ = NT / NA;        // parts of the rank count
+  constexpr int LW = NA / 64;        // waves holding the A rows in the list step
+  constexpr int TBITS = NA == 128 ? 7 : 8;  // bits of a target index
+  constexpr int OW = CMAX / 64;      // waves covering the output slots
+  static_assert(NT >= CMAX && BP >= 1 && AG % BP == 0 && BT % TP == 0, "tile split");
+  static_assert(NA == 128 || NA == 256, "chunk capacity 256 or 512");
+  __shared__ __attribute__((aligned(16))) char tile[CMAX * ROWB];
+  __shared__ __attribute__((aligned(16))) float s_invA[NA], s_invB[NA];  // 1 / max(|k|, eps)
+  __shared__ int32_t s_n[CMAX];
+  __shared__ int32_t s_outrow[CMAX];
+  __shared__ int32_t s_best[NA], s_sel[NA], s_cnt[NA], s_wsum[NA], s_off[NA], s_list[NA];
+  __shared__ int32_t s_cntw[LW][NA], s_rank[NQ][NA];
+  __shared__ int32_t s_mrg[OW][64], s_mcnt[OW];
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[NA];  // rank keys, 0 = no edge
+  __shared__ float s_bsc[BP][NA];  // per B part: best score and index of every A row
+  __shared__ int32_t s_bix[BP][NA];
   __shared__ int32_t s_misc[1 + NW];
 
   const int t = threadIdx.x;
@@ -231,36 +243,40 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   __syncthreads();
 
   // 2. similarity tile on MFMA and arg-max over B for every A column.  Wave w holds A
-  //    columns [32 (w mod 4), +32) against B tiles [BT (w / 4), +BT): with 8 waves the two B
-  //    halves are merged through LDS (half 0 holds the lower B indices and wins ties).
+  //    columns [32 (w mod AG), +32) against the BT B tiles of part w / AG, TP tiles per MFMA
+  //    pass; with several B parts the parts are merged through LDS (a lower part holds lower
+  //    B indices and wins ties).
   if (!copy_only && nB > 0) {
     const int w = t >> 6, l = t & 63, h = l >> 5, col = l & 31;
-    const int bq = w >> 2;
-    const int aidx = 32 * (w & 3) + col;
-    f32x16 acc[BT];
-#pragma unroll
-    for (int tl = 0; tl < BT; ++tl)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[tl][q] = 0.f;
-    sim_tile<BT, D>(tile, aidx, col, h, acc, tsel, bq * BT);
-    // cosine = (dot * (1/|b|)) * (1/|a|); lowest B index wins a tie (ascending order, strict >)
+    const int bq = w / AG;
+    const int aidx = 32 * (w % AG) + col;
     const float ia = s_invA[aidx];
     float best = -__builtin_inff();
     int bidx = 0;
 #pragma unroll
-    for (int tl = 0; tl < BT; ++tl) {
+    for (int tp = 0; tp < BT; tp += TP) {
+      f32x16 acc[TP];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int b0 = (bq * BT + tl) * 32 + 8 * g4 + 4 * h;
-        const float4 ib = *reinterpret_cast<const float4 *>(&s_invB[b0]);
-        const float ibv[4] = {ib.x, ib.y, ib.z, ib.w};
+      for (int tl = 0; tl < TP; ++tl)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sc = (acc[tl][4 * g4 + i] * ibv[i]) * ia;
-          sc = (b0 + i < nB) ? sc : -__builtin_inff();
-          const bool up = sc > best;
-          best = up ? sc : best;
-          bidx = up ? b0 + i : bidx;
+        for (int q = 0; q < 16; ++q) acc[tl][q] = 0.f;
+      sim_tile<TP, D>(tile, aidx, col, h, acc, tsel, bq * BT + tp);
+      // cosine = (dot * (1/|b|)) * (1/|a|); lowest B index wins a tie (ascending, strict >)
+#pragma unroll
+      for (int tl = 0; tl < TP; ++tl) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int b0 = (bq * BT + tp + tl) * 32 + 8 * g4 + 4 * h;
+          const float4 ib = *reinterpret_cast<const float4 *>(&s_invB[b0]);
+          const float ibv[4] = {ib.x, ib.y, ib.z, ib.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float sc = (acc[tl][4 * g4 + i] * ibv[i]) * ia;
+            sc = (b0 + i < nB) ? sc : -__builtin_inff();
+            const bool up = sc > best;
+            best = up ? sc : best;
+            bidx = up ? b0 + i : bidx;
+          }
         }
       }
     }
@@ -271,7 +287,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
       bidx = oi;
     }
     if (h == 0) {
-      if (NW == 4) {
+      if (BP == 1) {
         s_best[aidx] = aidx < nA ? bidx : -1;
         s_key[aidx] = aidx < nA ? rank_key(best, aidx) : 0ull;
       } else {
@@ -279,7 +295,7 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
         s_bix[bq][aidx] = bidx;
       }
     }
-  } else if (t < 128) {
+  } else if (t < NA) {
     s_best[t] = -1;
     s_key[t] = 0ull;
   }
@@ -288,12 +304,17 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   __syncthreads();
   if (a.in_place && t == 0)
     __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (NW == 8) {
-    if (!copy_only && nB > 0 && t < 128) {
-      const float b0s = s_bsc[0][t], b1s = s_bsc[NW / 4 - 1][t];
-      const bool up = b1s > b0s;
-      const float best = up ? b1s : b0s;
-      const int bidx = up ? s_bix[NW / 4 - 1][t] : s_bix[0][t];
+  if (BP > 1) {
+    if (!copy_only && nB > 0 && t < NA) {
+      float best = s_bsc[0][t];
+      int bidx = s_bix[0][t];
+#pragma unroll
+      for (int p = 1; p < BP; ++p) {
+        const float sc = s_bsc[p][t];
+        const bool up = sc > best;
+        best = up ? sc : best;
+        bidx = up ? s_bix[p][t] : bidx;
+      }
       s_best[t] = t < nA ? bidx : -1;
       s_key[t] = t < nA ? rank_key(best, t) : 0ull;
     }
@@ -301,10 +322,10 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
 
   // 3. top-m selection: rank of each A edge by (score desc, index asc), i.e. the number of
-  //    larger unique keys.  Every thread counts over one of NQ parts of the 128 candidates.
+  //    larger unique keys.  Every thread counts over one of NQ parts of the NA candidates.
   {
-    constexpr int PART = 128 / NQ;
-    const int aa = t & 127, part = t >> 7;
+    constexpr int PART = NA / NQ;
+    const int aa = t % NA, part = t / NA;
     const uint64_t my = s_key[aa];
     int cnt = 0;
 #pragma unroll 8
@@ -315,37 +336,35 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     s_rank[part][aa] = cnt;
   }
   __syncthreads();
-  if (t < 128) {
+  if (t < NA) {
     int rank = 0;
 #pragma unroll
     for (int p = 0; p < NQ; ++p) rank += s_rank[p][t];
     s_sel[t] = (t < nA && m > 0 && nB > 0) ? (rank < m) : 0;
-    s_cnt0[t] = 0;
-    s_cnt1[t] = 0;
+#pragma unroll
+    for (int w = 0; w < LW; ++w) s_cntw[w][t] = 0;
     s_wsum[t] = t < nB ? s_n[2 * t + 1] : 0;
   }
   __syncthreads();
 
-  // 4. source lists.  Waves 0 and 1 hold A rows 0..63 and 64..127; lanes with the same
-  //    target are found with seven ballots over the bits of the target index, which gives
-  //    each source its slot among the same-target sources of its wave (ascending A).
+  // 4. source lists.  Waves 0 .. LW-1 hold the A rows, 64 each; lanes with the same target
+  //    are found with TBITS ballots over the bits of the target index, which gives each
+  //    source its slot among the same-target sources of its wave (ascending A).
   int my_pos = 0, my_b = -1;
-  if (t < 128) {
+  if (t < NA) {
     const int aa = t;
     const bool sa = s_sel[aa] != 0;
     const int b = sa ? s_best[aa] : 0;
     uint64_t eq = __ballot(sa);
 #pragma unroll
-    for (int bit = 0; bit < 7; ++bit) {
+    for (int bit = 0; bit < TBITS; ++bit) {
       const uint64_t mb = __ballot(sa && ((b >> bit) & 1));
       eq &= ((b >> bit) & 1) ? mb : ~mb;
     }
     if (sa) {
       my_b = b;
       my_pos = lanes_below(eq);
-      if (my_pos == 0) {
-        if (t < 64) s_cnt0[b] = __popcll(eq); else s_cnt1[b] = __popcll(eq);
-      }
+      if (my_pos == 0) s_cntw[t >> 6][b] = __popcll(eq);
       atomicAdd(&s_wsum[b], s_n[2 * aa]);
     }
   }
@@ -354,19 +373,30 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   const int pre = lanes_below(bal);
   if ((t & 63) == 0) s_misc[1 + (t >> 6)] = __popcll(bal);
   __syncthreads();
-  if (t < 64) {  // per-target counts and their exclusive scan (2 targets per lane)
-    const int c0 = s_cnt0[2 * t] + s_cnt1[2 * t], c1 = s_cnt0[2 * t + 1] + s_cnt1[2 * t + 1];
-    int incl = c0 + c1;
+  if (t < 64) {  // per-target counts and their exclusive scan (NA / 64 targets per lane)
+    constexpr int TPL = NA / 64;
+    int cnt[TPL], tot = 0;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      int cc = 0;
+#pragma unroll
+      for (int w = 0; w < LW; ++w) cc += s_cntw[w][TPL * t + k];
+      cnt[k] = cc;
+      tot += cc;
+    }
+    int incl = tot;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(incl, o);
       if (t >= o) incl += y;
     }
-    const int ex = incl - c0 - c1;
-    s_off[2 * t] = ex;
-    s_off[2 * t + 1] = ex + c0;
-    s_cnt[2 * t] = c0;
-    s_cnt[2 * t + 1] = c1;
+    int ex = incl - tot;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      s_off[TPL * t + k] = ex;
+      s_cnt[TPL * t + k] = cnt[k];
+      ex += cnt[k];
+    }
   }
   {
     int off = 0;
@@ -374,8 +404,12 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     if (keep) s_outrow[off + pre] = t;
   }
   __syncthreads();
-  if (my_b >= 0) s_list[s_off[my_b] + (t >= 64 ? s_cnt0[my_b] : 0) + my_pos] = t;
-  if (t < kMaxChunk) {  // output slots that hold a merged target, compacted per wave
+  if (my_b >= 0) {
+    int before = 0;  // same-target sources of the lower waves come first
+    for (int w = 0; w < (t >> 6); ++w) before += s_cntw[w][my_b];
+    s_list[s_off[my_b] + before + my_pos] = t;
+  }
+  if (t < CMAX) {  // output slots that hold a merged target, compacted per wave
     bool mg = false;
     if (t < nout) {
       const int r = s_outrow[t];
@@ -392,8 +426,8 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
   __syncthreads();
 
-  if (a.tap_best != nullptr && t < 128) {
-    const int64_t o = (z * a.units + j) * 128 + t;
+  if (a.tap_best != nullptr && t < NA) {
+    const int64_t o = (z * a.units + j) * NA + t;
     a.tap_best[o] = (t < nA && !copy_only) ? s_best[t] : -1;
     a.tap_sel[o] = (uint8_t)s_sel[t];
   }
@@ -402,8 +436,9 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   // 5. write K (merged rows averaged in fp32), then V through the same LDS tile, then N
   char *Kdst = a.Kout + (z * a.cap_out + base) * (int64_t)ROWB;
   char *Vdst = a.Vout + (z * a.cap_out + base) * (int64_t)ROWB;
-  const int m0 = s_mcnt[0], m1 = s_mcnt[1], m2 = s_mcnt[2], m3 = s_mcnt[3];
-  const int nmerged = m0 + m1 + m2 + m3;
+  int nmerged = 0;
+#pragma unroll
+  for (int w = 0; w < OW; ++w) nmerged += s_mcnt[w];
   for (int pass = 0; pass < 2; ++pass) {
     char *dst = pass == 0 ? Kdst : Vdst;
     if (pass == 1) {
@@ -425,8 +460,15 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
     }
     // merge targets: (N_b x_b + sum N_a x_a) * (1 / W), fp32, sources in ascending A order
     for (int idx = r0; idx < nmerged; idx += RPI) {
-      const int wv = idx < m0 ? 0 : idx < m0 + m1 ? 1 : idx < m0 + m1 + m2 ? 2 : 3;
-      const int p = s_mrg[wv][idx - (wv > 0 ? m0 : 0) - (wv > 1 ? m1 : 0) - (wv > 2 ? m2 : 0)];
+      int wv = 0, rem = idx;  // the wave list holding merged slot idx, and its position
+#pragma unroll
+      for (int w = 0; w < OW - 1; ++w) {
+        const int cw = s_mcnt[w];
+        const bool past = wv == w && rem >= cw;
+        rem -= past ? cw : 0;
+        wv += past ? 1 : 0;
+      }
+      const int p = s_mrg[wv][rem];
       const int r = s_outrow[p];
       const int b = r >> 1;
       float accv[EPS], tmp[EPS];
@@ -459,30 +501,46 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
 // Head dim 128.  bf16 / fp16: 512 threads and 78 KB of LDS per workgroup, two workgroups
 // (four waves per SIMD) per CU.  fp32: the 128 KB key tile allows one workgroup per CU.
 constexpr int kWideThreads = 512;
+constexpr int kBigThreads = 1024;
 __global__ void __launch_bounds__(kWideThreads, 2) csm_round_bf16(CsmArgs a) {
-  csm_round_body<__bf16, kWideThreads, 128>(a);
+  csm_round_body<__bf16, kWideThreads, 128, kMaxChunk>(a);
 }
 __global__ void __launch_bounds__(kWideThreads, 2) csm_round_f16(CsmArgs a) {
-  csm_round_body<_Float16, kWideThreads, 128>(a);
+  csm_round_body<_Float16, kWideThreads, 128, kMaxChunk>(a);
 }
 __global__ void __launch_bounds__(256, 1) csm_round_f32(CsmArgs a) {
-  csm_round_body<float, 256, 128>(a);
+  csm_round_body<float, 256, 128, kMaxChunk>(a);
 }
 // Head dim 64: half the tile.  bf16 / fp16: 46 KB of LDS, so three 512-thread workgroups fit
 // a CU when a thread holds at most 85 VGPRs (six waves per SIMD); fp32: 79 KB, two per CU.
 __global__ void __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
 csm_round_bf16_d64(CsmArgs a) {
-  csm_round_body<__bf16, kWideThreads, 64>(a);
+  csm_round_body<__bf16, kWideThreads, 64, kMaxChunk>(a);
 }
 __global__ void __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(6, 8)))
 csm_round_f16_d64(CsmArgs a) {
-  csm_round_body<_Float16, kWideThreads, 64>(a);
+  csm_round_body<_Float16, kWideThreads, 64, kMaxChunk>(a);
 }
 __global__ void __launch_bounds__(kWideThreads, 2) csm_round_f32_d64(CsmArgs a) {
-  csm_round_body<float, kWideThreads, 64>(a);
+  csm_round_body<float, kWideThreads, 64, kMaxChunk>(a);
+}
+// Chunks up to 512 rows (256 x 256 similarity tile), bf16 / fp16: 1024 threads, one workgroup
+// per CU (the d = 128 key tile is 128 KB).
+__global__ void __launch_bounds__(kBigThreads, 1) csm_round_bf16_c512(CsmArgs a) {
+  csm_round_body<__bf16, kBigThreads, 128, kMaxChunkWide>(a);
+}
+__global__ void __launch_bounds__(kBigThreads, 1) csm_round_f16_c512(CsmArgs a) {
+  csm_round_body<_Float16, kBigThreads, 128, kMaxChunkWide>(a);
+}
+__global__ void __launch_bounds__(kBigThreads, 1) csm_round_bf16_d64_c512(CsmArgs a) {
+  csm_round_body<__bf16, kBigThreads, 64, kMaxChunkWide>(a);
+}
+__global__ void __launch_bounds__(kBigThreads, 1) csm_round_f16_d64_c512(CsmArgs a) {
+  csm_round_body<_Float16, kBigThreads, 64, kMaxChunkWide>(a);
 }
 
-// Host-side launcher used by the C ABI (d is 64 or 128).  Returns 0 or a hipError_t value.
+// Host-side launcher used by the C ABI (d is 64 or 128; c <= 512, and c <= 256 for fp32).
+// Returns 0 or a hipError_t value.
 int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
   const int64_t total = args.num_slices * (int64_t)args.units;
   const int prep_blocks = 1 + (int)std::min<int64_t>(1024, (total + 255) / 256);
@@ -490,21 +548,25 @@ int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (total == 0) return 0;
-  const dim3 grid((uint32_t)total), wide(kWideThreads);
-  if (d == 64) {
-    if (dtype == kDtypeF32)
-      hipLaunchKernelGGL(csm_round_f32_d64, grid, wide, 0, stream, args);
-    else if (dtype == kDtypeF16)
-      hipLaunchKernelGGL(csm_round_f16_d64, grid, wide, 0, stream, args);
-    else
-      hipLaunchKernelGGL(csm_round_bf16_d64, grid, wide, 0, stream, args);
+  const dim3 grid((uint32_t)total), wide(kWideThreads), big(kBigThreads);
+  const bool f32 = dtype == kDtypeF32, f16 = dtype == kDtypeF16;
+  if (args.c > kMaxChunk) {
+    if (f32) return (int)hipErrorInvalidValue;  // rejected by the C ABI before this point
+    if (d == 64) {
+      if (f16) hipLaunchKernelGGL(csm_round_f16_d64_c512, grid, big, 0, stream, args);
+      else hipLaunchKernelGGL(csm_round_bf16_d64_c512, grid, big, 0, stream, args);
+    } else {
+      if (f16) hipLaunchKernelGGL(csm_round_f16_c512, grid, big, 0, stream, args);
+      else hipLaunchKernelGGL(csm_round_bf16_c512, grid, big, 0, stream, args);
+    }
+  } else if (d == 64) {
+    if (f32) hipLaunchKernelGGL(csm_round_f32_d64, grid, wide, 0, stream, args);
+    else if (f16) hipLaunchKernelGGL(csm_round_f16_d64, grid, wide, 0, stream, args);
+    else hipLaunchKernelGGL(csm_round_bf16_d64, grid, wide, 0, stream, args);
   } else {
-    if (dtype == kDtypeF32)
-      hipLaunchKernelGGL(csm_round_f32, grid, dim3(256), 0, stream, args);
-    else if (dtype == kDtypeF16)
-      hipLaunchKernelGGL(csm_round_f16, grid, wide, 0, stream, args);
-    else
-      hipLaunchKernelGGL(csm_round_bf16, grid, wide, 0, stream, args);
+    if (f32) hipLaunchKernelGGL(csm_round_f32, grid, dim3(256), 0, stream, args);
+    else if (f16) hipLaunchKernelGGL(csm_round_f16, grid, wide, 0, stream, args);
+    else hipLaunchKernelGGL(csm_round_bf16, grid, wide, 0, stream, args);
   }
   e = hipGetLastError();
   return (int)e;

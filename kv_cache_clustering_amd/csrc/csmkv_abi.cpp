@@ -41,7 +41,7 @@ int64_t units_per_slice(int32_t max_len, int32_t n1, int32_t n2, int32_t c) {
 int check_csm_params(int32_t n1, int32_t n2, int32_t c, double r) {
   if (n1 < 0 || n2 < 0) return CSMKV_EINVAL;
   if (c < 2) return CSMKV_EINVAL;
-  if (c > 256) return CSMKV_EUNSUPPORTED;
+  if (c > 512) return CSMKV_EUNSUPPORTED;
   if (!(r >= 0.0 && r <= 1.0)) return CSMKV_EINVAL;  // also rejects NaN
   return CSMKV_OK;
 }
@@ -76,6 +76,7 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
     return CSMKV_EINVAL;
   rc = check_csm_params(n1, n2, c, r);
   if (rc) return rc;
+  if (c > 256 && src->dtype == CSMKV_F32) return CSMKV_EUNSUPPORTED;  // no fp32 512-row tile
   if (!K_in || !V_in || !N_in || !lens_in || !K_out || !V_out || !N_out || !lens_out)
     return CSMKV_EINVAL;
   if (!aligned(K_in, 16) || !aligned(V_in, 16) || !aligned(K_out, 16) || !aligned(V_out, 16))
@@ -169,7 +170,7 @@ const char *csmkv_status_string(int status) {
 int csmkv_version(void) { return 103; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
-  if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
+  if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 512) return 0;
   const int64_t units = units_per_slice(cache->max_len, n1, n2, c);
   return csm_layout(cache->num_slices, units).total;
 }
@@ -188,7 +189,7 @@ int csm_compress_triggered(void *K, void *V, int32_t *N, int32_t *lens,
 }
 
 int64_t csm_compress_units(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
-  if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 256) return 0;
+  if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 512) return 0;
   return units_per_slice(cache->max_len, n1, n2, c);
 }
 

@@ -13,7 +13,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMaxChunk = 256;       // largest chunk c (128 x 128 similarity tile)
+constexpr int kMaxChunk = 256;       // chunk capacity of the main kernels (128 x 128 tile)
+constexpr int kMaxChunkWide = 512;   // capacity of the wide-chunk kernels (256 x 256 tile)
 constexpr int kDeviceError = -6;     // CSMKV_EDEVICE
 
 __device__ __forceinline__ u32x4 ld16(const void *p) {

@@ -258,3 +258,36 @@ def test_head_dim_64_in_place_equals_out_of_place(lib, dev, dtype):
         s = int(L[z])
         assert torch.equal(K[z, :s], Ko[z, :s]) and torch.equal(V[z, :s], Vo[z, :s])
         assert torch.equal(N[z, :s], No[z, :s])
+
+
+LENS_WIDE = [4100, 1111, 81, 600, 2000, 0, 3001, 4100]
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 128),
+                                     (torch.bfloat16, 64), (torch.float16, 64)])
+@pytest.mark.parametrize("c,r,n1,n2", [(512, 0.5, 16, 64), (512, 1.0, 0, 0), (300, 0.77, 3, 5),
+                                       (511, 0.1, 16, 64)])
+def test_wide_chunks(lib, dev, dtype, d, c, r, n1, n2):
+    """Chunks of up to 512 rows: 256 x 256 similarity tile, ranks over 256 candidates, 8-bit
+    target ballots, 512-row compaction, 1024-thread workgroups."""
+    K, V, N, lens = host_cache(len(LENS_WIDE), 4100, LENS_WIDE, d=d, dtype=dtype,
+                               seed=c + d + (dtype == torch.float16), degrees=True)
+    mask = np.zeros(len(LENS_WIDE), np.uint8)
+    mask[4] = 1
+    rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
+    print(rep)
+    parity.check_report(rep, near_bar=5e-3)
+
+
+def test_wide_chunks_in_place_equals_out_of_place(lib, dev):
+    S, cap = 6, 5000
+    lens = [4999, 5000, 17, 1500, 0, 592]
+    K, V, N, L = (t.to(dev) for t in host_cache(S, cap, lens, seed=8, degrees=True))
+    Ko, Vo, No, Lo = torch.empty_like(K), torch.empty_like(V), torch.empty_like(N), torch.empty_like(L)
+    lib.csm_compress_into(K, V, N, L, Ko, Vo, No, Lo, 16, 64, 512, 0.5)
+    lib.csm_compress(K, V, N, L, 16, 64, 512, 0.5)
+    assert torch.equal(L, Lo)
+    for z in range(S):
+        s = int(L[z])
+        assert torch.equal(K[z, :s], Ko[z, :s]) and torch.equal(V[z, :s], Vo[z, :s])
+        assert torch.equal(N[z, :s], No[z, :s])

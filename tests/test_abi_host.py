@@ -73,7 +73,8 @@ def test_compress_argument_validation(lib):
     assert _compress(lib, d, r=-0.1) == lib.EINVAL
     assert _compress(lib, d, r=float("nan")) == lib.EINVAL
     assert _compress(lib, d, c=1) == lib.EINVAL
-    assert _compress(lib, d, c=257) == lib.EUNSUPPORTED
+    assert _compress(lib, d, c=513) == lib.EUNSUPPORTED
+    assert _compress(lib, _desc(lib, dtype=1), c=257) == lib.EUNSUPPORTED  # fp32: c <= 256
     assert _compress(lib, d, n1=-1) == lib.EINVAL
     assert _compress(lib, d, n2=-3) == lib.EINVAL
     assert _compress(lib, d, K=None) == lib.EINVAL
@@ -119,7 +120,7 @@ def test_triggered_argument_validation(lib):
     assert trig(r_delta=-0.01) == lib.EINVAL
     assert trig(r_delta=float("nan")) == lib.EINVAL
     assert trig(r_min=float("nan")) == lib.EINVAL
-    assert trig(c=300) == lib.EUNSUPPORTED
+    assert trig(c=600) == lib.EUNSUPPORTED
     assert trig(ws_bytes=8) == lib.EWORKSPACE
 
 

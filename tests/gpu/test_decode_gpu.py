@@ -223,3 +223,35 @@ def test_bad_length_gives_zeros_and_error(lib, dev):
                              workspace=ws)
     assert lib.read_error(ws) == lib.EDEVICE
     assert torch.all(O[1] == 0) and torch.any(O[0] != 0)
+    # the error word belongs to one call: the next call on the same workspace is clean
+    Kd, Vd, Nd = K.to(dev), V.to(dev), N.to(dev)
+    Ld[1] = 650
+    O2 = lib.decode_attn_logn(q.to(dev), Kd, Vd, Nd, Ld, 1, 1, max_len=700, workspace=ws)
+    assert lib.read_error(ws) == lib.OK
+    assert torch.equal(O2[0], O[0]) and torch.any(O2[1] != 0)
+
+
+def test_workspace_reused_across_calls_and_geometries(lib, dev):
+    """One workspace (uninitialised memory), many calls: slice counts, length bounds and
+    work-item sizes change from call to call."""
+    S, cap = 64, 5000
+    gen = torch.Generator(device=dev).manual_seed(12)
+    K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.randint(1, 5, (S, cap), generator=gen, device=dev, dtype=torch.int32)
+    L = torch.randint(0, cap + 1, (S,), generator=gen, device=dev, dtype=torch.int32)
+    ws = torch.full((lib.decode_workspace_bytes(K, 16, 4, max_len=cap),), 0xA5, dtype=torch.uint8,
+                    device=dev)
+    for call, (n, ml) in enumerate([(64, cap), (8, cap), (64, 3000), (4, 900), (64, cap)]):
+        Lc = torch.clamp(L[:n], max=ml)
+        q = torch.randn((n // 4, 16, 128), generator=gen, device=dev).to(torch.bfloat16)
+        O = lib.decode_attn_logn(q, K[:n], V[:n], N[:n], Lc, 16, 4, max_len=ml, workspace=ws)
+        assert lib.read_error(ws) == lib.OK, call
+        for z in (0, n - 1):
+            s = int(Lc[z])
+            ref = oatt.logn_attention_one(parity.to_f64(q[z // 4, 4 * (z % 4)].cpu()),
+                                          parity.to_f64(K[z, :s].cpu()),
+                                          parity.to_f64(V[z, :s].cpu()),
+                                          N[z, :s].cpu().numpy().astype(np.int64))
+            got = O[z // 4, 4 * (z % 4)].cpu().double().numpy()
+            assert (np.abs(got - ref).max() if s else np.abs(got).max()) < 2e-4, (call, z)

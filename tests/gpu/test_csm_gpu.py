@@ -291,3 +291,40 @@ def test_wide_chunks_in_place_equals_out_of_place(lib, dev):
         s = int(L[z])
         assert torch.equal(K[z, :s], Ko[z, :s]) and torch.equal(V[z, :s], Vo[z, :s])
         assert torch.equal(N[z, :s], No[z, :s])
+
+
+def test_one_million_token_slice_round_and_decode(lib, dev):
+    """Maximum-size case: one slice of 2**20 tokens (4096 chunks, 268 MB of K + V), a round in
+    place compared with the oracle on the whole slice, then decode attention over the
+    result for 8 query heads compared head by head."""
+    from oracle import attention as oatt
+    n = 1 << 20
+    gen = torch.Generator(device=dev).manual_seed(2024)
+    # AR(1) keys along the sequence (rho = 0.95, unit stationary variance), on the device
+    from kvsynth.gen import _ar1_scan_torch
+    rho = torch.tensor([0.95], device=dev)
+    eps = torch.randn((1, n, 128), generator=gen, device=dev) * (1 - 0.95 ** 2) ** 0.5
+    eps[:, 0] = torch.randn((1, 128), generator=gen, device=dev)
+    K = _ar1_scan_torch(eps, rho).to(torch.bfloat16).contiguous()
+    V = torch.randn((1, n, 128), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.randint(1, 4, (1, n), generator=gen, device=dev, dtype=torch.int32)
+    L = torch.tensor([n], dtype=torch.int32, device=dev)
+    Kin, Vin, Nin = parity.to_f64(K[0].cpu()), parity.to_f64(V[0].cpu()), N[0].cpu().numpy().astype(np.int64)
+    best, sel, src, ws = lib.csm_compress_debug(K, V, N, L, 16, 64, 256, 0.5, max_len=n)
+    assert lib.read_error(ws) == lib.OK
+    rep = parity.Report()
+    parity.compare_slice(rep, Kin, Vin, Nin, n, 16, 64, 256, 0.5, "bf16", best[0].cpu().numpy(),
+                         sel[0].cpu().numpy(), src[0].cpu().numpy(), parity.to_f64(K[0].cpu()),
+                         parity.to_f64(V[0].cpu()), N[0].cpu().numpy().astype(np.int64), int(L[0]))
+    print(rep)
+    parity.check_report(rep)
+    s = int(L[0])
+    q = torch.randn((1, 8, 128), generator=gen, device=dev).to(torch.bfloat16)
+    O = lib.decode_attn_logn(q, K, V, N, L, 8, 1, max_len=n).cpu().double().numpy()
+    Kz, Vz = parity.to_f64(K[0, :s].cpu()), parity.to_f64(V[0, :s].cpu())
+    Nz = N[0, :s].cpu().numpy().astype(np.int64)
+    worst = max(float(np.abs(O[0, h] - oatt.logn_attention_one(parity.to_f64(q[0, h].cpu()), Kz,
+                                                                Vz, Nz)).max())
+                for h in range(8))
+    print("decode max abs", worst)
+    assert worst < 2e-4

@@ -328,3 +328,32 @@ def test_one_million_token_slice_round_and_decode(lib, dev):
                 for h in range(8))
     print("decode max abs", worst)
     assert worst < 2e-4
+
+
+def test_seeded_sweep_of_shapes_and_parameters(lib, dev):
+    """150 seeded random configurations: chunk size 2..512, sinks / recent 0..100, r in [0, 1],
+    ragged lengths (including 0, 1, n1 + n2 and just past it), every storage format and both
+    head dims, random outlier masks; each compared with the oracle on every slice."""
+    rng = np.random.default_rng(2026)
+    dtypes = [torch.bfloat16, torch.float16, torch.float32]
+    total = parity.Report()
+    for case in range(150):
+        dtype = dtypes[case % 3]
+        d = 64 if (case // 3) % 2 else 128
+        cmax = 256 if dtype == torch.float32 else 512
+        c = int(rng.choice([2, 3, 5, 17, 64, 100, 128, 200, 255, 256, cmax, int(rng.integers(2, cmax + 1))]))
+        n1, n2 = int(rng.integers(0, 101)), int(rng.integers(0, 101))
+        r = float(rng.choice([0.0, 1.0, 0.5, 0.05, float(rng.random())]))
+        S = int(rng.integers(1, 6))
+        cap = int(rng.integers(n1 + n2 + 2, n1 + n2 + 3 * c + 300))
+        lens = [int(rng.choice([0, 1, n1 + n2, min(cap, n1 + n2 + 1), min(cap, n1 + n2 + 2), cap,
+                                int(rng.integers(0, cap + 1))])) for _ in range(S)]
+        K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=1000 + case, degrees=True)
+        mask = (rng.random(S) < 0.25).astype(np.uint8)
+        rep = run_and_compare(lib, dev, K, V, N, L, n1, n2, c, r, mask)
+        for f in ("edges", "match_near", "match_hard", "sel_near", "sel_hard", "followed_chunks",
+                  "abs_floor_used", "slices"):
+            setattr(total, f, getattr(total, f) + getattr(rep, f))
+        total.max_ulp = max(total.max_ulp, rep.max_ulp)
+    print(total)
+    parity.check_report(total, near_bar=5e-3)

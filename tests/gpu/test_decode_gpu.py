@@ -255,3 +255,33 @@ def test_workspace_reused_across_calls_and_geometries(lib, dev):
                                           N[z, :s].cpu().numpy().astype(np.int64))
             got = O[z // 4, 4 * (z % 4)].cpu().double().numpy()
             assert (np.abs(got - ref).max() if s else np.abs(got).max()) < 2e-4, (call, z)
+
+
+def test_seeded_sweep_decode(lib, dev):
+    """80 seeded random decode configurations: storage format, head dim, heads per group
+    (1, 2, 4, 8), slice counts, ragged lengths (0 .. cap), degrees 1..1000, length bounds;
+    every head compared with the oracle."""
+    rng = np.random.default_rng(77)
+    dtypes = [torch.bfloat16, torch.float16, torch.float32]
+    worst = {dt: 0.0 for dt in dtypes}
+    for case in range(80):
+        dtype = dtypes[case % 3]
+        d = 64 if (case // 3) % 2 else 128
+        G = int(rng.choice([1, 2, 4, 8]))
+        H_kv = int(rng.choice([1, 2, 4]))
+        groups = int(rng.integers(1, 4))
+        S = groups * H_kv
+        cap = int(rng.integers(1, 3000))
+        lens = [int(rng.choice([0, 1, cap, int(rng.integers(0, cap + 1))])) for _ in range(S)]
+        K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=500 + case, degrees=True)
+        N[N > 0] = torch.from_numpy(rng.integers(1, 1001, size=int((N > 0).sum())).astype(np.int32))
+        q = torch.from_numpy(rng.standard_normal((groups, G * H_kv, d))).float().to(dtype)
+        max_len = max(max(lens), int(rng.integers(max(lens), cap + 1)))
+        O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), L.to(dev), G * H_kv,
+                                 H_kv, max_len=max_len)
+        ref = _oracle_all(q, K, V, N, L, G * H_kv, H_kv)
+        err = float(np.abs(O.cpu().double().numpy() - ref).max())
+        worst[dtype] = max(worst[dtype], err)
+    print({str(k): v for k, v in worst.items()})
+    assert worst[torch.float32] < 2e-5
+    assert worst[torch.bfloat16] < 2e-4 and worst[torch.float16] < 2e-4

@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--cpu-slices", type=int, default=32)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
-    ap.add_argument("--workloads", default="1,2,3,5,4:f16,4:d64,4:c512",
+    ap.add_argument("--workloads", default="1,2,3,5,4:f16,4:d64,4:c512,4:g8",
                     help="other synthetic workloads to measure and report (comma list of ids, "
                          "id:dtype for another storage format, '' for none)")
     return ap.parse_args()
@@ -319,11 +319,11 @@ def main():
     if wl:
         del K0, V0, N0, Kw, Vw, Nw, Kd, Vd, Nd, app_k, app_v, c
         torch.cuda.empty_cache()
-        for spec in wl:  # "<id>[:<dtype>][:d<head dim>][:c<chunk>]": optionally re-shaped
+        for spec in wl:  # "<id>[:<dtype>][:d<head dim>][:c<chunk>][:g<q heads per kv head>]"
             cid, *mods = spec.split(":")
-            num = {m[0]: int(m[1:]) for m in mods if m[:1] in ("d", "c") and m[1:].isdigit()}
-            dt = next((m for m in mods if not (m[:1] in ("d", "c") and m[1:].isdigit())), None)
-            others.append(measure_workload(int(cid), dt, num.get("d"), num.get("c")))
+            num = {m[0]: int(m[1:]) for m in mods if m[:1] in ("d", "c", "g") and m[1:].isdigit()}
+            dt = next((m for m in mods if not (m[:1] in ("d", "c", "g") and m[1:].isdigit())), None)
+            others.append(measure_workload(int(cid), dt, num.get("d"), num.get("c"), num.get("g")))
     out = {
         "metric": METRIC,
         "value": value,
@@ -376,7 +376,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_workload(cid, dtype=None, head_dim=None, chunk=None):
+def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
     """One synthetic workload: every prefill round in place (HIP events per round), then
     decode steps (append + attention) over the compressed cache.  Figures are algorithmic
     bytes / event time."""
@@ -394,6 +394,9 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None):
         w = kvsynth.workload(cid, dtype=w.dtype, d=head_dim, name=f"{w.name}-d{head_dim}")
     if chunk is not None and chunk != w.c:
         w = kvsynth.workload(cid, dtype=w.dtype, d=w.d, c=chunk, name=f"{w.name}-c{chunk}")
+    if group is not None and group != w.G:
+        w = kvsynth.workload(cid, dtype=w.dtype, d=w.d, c=w.c, H_q=group * w.H_kv,
+                             name=f"{w.name}-g{group}")
     dev = torch.device("cuda:0")
     c = kvsynth.make_cache(w, dev, batch_slices=256)
     K, V, N, L, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]
@@ -426,7 +429,8 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None):
         s = s2
     assert lib.read_error(ws) == lib.OK
     assert int(L[int(np.argmin(maskh))]) == s
-    out = {"workload": w.name, "slices": S, "dtype": w.dtype, "d": w.d, "c": w.c, "ctx": w.ctx,
+    out = {"workload": w.name, "slices": S, "dtype": w.dtype, "d": w.d, "c": w.c, "G": w.G,
+           "ctx": w.ctx,
            "round0": rounds[0],
            "prefill": {"rounds": len(rounds), "len": s, "ms": sum(x["ms"] for x in rounds),
                        "GBps": sum(n_comp * ((x["s_in"] - w.n1) + (x["s_out"] - w.n1)) * row

@@ -80,7 +80,7 @@ struct DecTile {
   static constexpr int ROWB = D * (int)sizeof(T);
   static constexpr int LPR = ROWB / 16;     // lanes per row
   static constexpr int RPW = 64 / LPR;      // rows per wave-wide load
-  static constexpr int NR = G >= 8 ? 2 : 4;  // wave loads per sub-block (8 heads: fewer, no spills)
+  static constexpr int NR = G >= 8 ? 2 : 4;  // wave loads per sub-block (fewer for 8 heads a wave)
   static constexpr int SUB = NR * RPW;      // rows per sub-block
   static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
 };
@@ -143,7 +143,9 @@ struct DecStage {
   int32_t n[NR];
 };
 
-template <typename T, int G, int D>
+// NTL: non-temporal loads (each row is read by one wave only); plain loads where two waves
+// read the same rows, so that the second read is served by the cache.
+template <typename T, int G, int D, bool NTL = true>
 __device__ __forceinline__ void dec_load(DecStage<DecTile<T, G, D>::NR> &st, const char *Kz, const char *Vz,
                                          const int32_t *Nz, int sb, int we, int rw, int sg) {
   using DT = DecTile<T, G, D>;
@@ -151,12 +153,10 @@ __device__ __forceinline__ void dec_load(DecStage<DecTile<T, G, D>::NR> &st, con
   for (int i = 0; i < DT::NR; ++i) {
     const int tok = sb + DT::RPW * i + rw;
     const bool ok = tok < we;
-    st.k[i] = ok ? __builtin_nontemporal_load(
-                       reinterpret_cast<const u32x4 *>(Kz + (int64_t)tok * DT::ROWB + sg * 16))
-                 : u32x4{0u, 0u, 0u, 0u};
-    st.v[i] = ok ? __builtin_nontemporal_load(
-                       reinterpret_cast<const u32x4 *>(Vz + (int64_t)tok * DT::ROWB + sg * 16))
-                 : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(Kz + (int64_t)tok * DT::ROWB + sg * 16);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(Vz + (int64_t)tok * DT::ROWB + sg * 16);
+    st.k[i] = ok ? (NTL ? __builtin_nontemporal_load(kp) : *kp) : u32x4{0u, 0u, 0u, 0u};
+    st.v[i] = ok ? (NTL ? __builtin_nontemporal_load(vp) : *vp) : u32x4{0u, 0u, 0u, 0u};
     st.n[i] = ok ? Nz[tok] : 0;
   }
 }
@@ -209,13 +209,22 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
   }
 }
 
+// Threads of a dec_split workgroup: G = 8 splits the heads over two sets of four waves that
+// stream the same tokens (heads 0-3 and 4-7), so that every wave holds the registers of four
+// heads (eight spill); the second read of a row is served by the cache.
+template <int G>
+constexpr int dec_head_sets() { return G >= 8 ? 2 : 1; }
+template <int G>
+constexpr int dec_threads() { return kDecThreads * dec_head_sets<G>(); }
+
 template <typename T, int G, int D>
-__global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
-  using DT = DecTile<T, G, D>;
+__global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_split(DecArgs a) {
+  constexpr int HS = dec_head_sets<G>(), GW = G / HS, NT = dec_threads<G>();
+  using DT = DecTile<T, GW, D>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
   constexpr int PW = part_width<D>();  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][G][PW];
-  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int t = threadIdx.x, w = (t >> 6) & 3, hs = t >> 8, l = t & 63;
   const int sg = l % LPR, rw = l / LPR;
   const int64_t S = a.num_slices;
   const int total = a.item_off[S];
@@ -232,15 +241,15 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
     // two register stages: the next sub-block loads while the current one is computed
     DecStage<DT::NR> A, B;
-    if (wb < we) dec_load<T, G, D>(A, Kz, Vz, Nz, wb, we, rw, sg);
-    // this lane's q segment for each head of the group
-    u32x4 qv[G];
+    if (wb < we) dec_load<T, GW, D, HS == 1>(A, Kz, Vz, Nz, wb, we, rw, sg);
+    // this lane's q segment for each head of the wave's head set
+    u32x4 qv[GW];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + h) * (int64_t)D) * sizeof(T) + sg * 16);
-    float mrun[G], lrun[G], o[G][EPL];
+    for (int h = 0; h < GW; ++h)
+      qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + hs * GW + h) * (int64_t)D) * sizeof(T) + sg * 16);
+    float mrun[GW], lrun[GW], o[GW][EPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GW; ++h) {
       mrun[h] = NEG_INF;
       lrun[h] = 0.f;
 #pragma unroll
@@ -248,15 +257,15 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     }
     for (int sb = wb; sb < we; sb += 2 * SUB) {
       const int sb1 = sb + SUB;
-      if (sb1 < we) dec_load<T, G, D>(B, Kz, Vz, Nz, sb1, we, rw, sg);
-      dec_compute<T, G, D>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
+      if (sb1 < we) dec_load<T, GW, D, HS == 1>(B, Kz, Vz, Nz, sb1, we, rw, sg);
+      dec_compute<T, GW, D>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
       if (sb1 >= we) break;
-      if (sb1 + SUB < we) dec_load<T, G, D>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
-      dec_compute<T, G, D>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
+      if (sb1 + SUB < we) dec_load<T, GW, D, HS == 1>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
+      dec_compute<T, GW, D>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
     }
     // sum the row groups of the wave (they hold different tokens, same segment)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GW; ++h) {
 #pragma unroll
       for (int o2 = LPR; o2 < 64; o2 <<= 1) lrun[h] += __shfl_xor(lrun[h], o2);
 #pragma unroll
@@ -266,18 +275,19 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     }
     if (rw == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < GW; ++h) {
+        const int hh = hs * GW + h;
         if (sg == 0) {
-          s_part[w][h][0] = mrun[h];
-          s_part[w][h][1] = lrun[h];
+          s_part[w][hh][0] = mrun[h];
+          s_part[w][hh][1] = lrun[h];
         }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_part[w][h][4 + sg * EPL + e] = o[h][e];
+        for (int e = 0; e < EPL; ++e) s_part[w][hh][4 + sg * EPL + e] = o[h][e];
       }
     }
     __syncthreads();
     float *dst = a.part + (int64_t)item * G * PW;
-    for (int i = t; i < G * PW; i += kDecThreads) {
+    for (int i = t; i < G * PW; i += NT) {
       const int h = i / PW, k = i % PW;
       float M = NEG_INF;
 #pragma unroll
@@ -381,7 +391,7 @@ static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
     case 1: hipLaunchKernelGGL((dec_split<T, 1, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
     case 2: hipLaunchKernelGGL((dec_split<T, 2, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
     case 4: hipLaunchKernelGGL((dec_split<T, 4, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_split<T, 8, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_split<T, 8, D>), dim3(grid), dim3(dec_threads<8>()), 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -32,6 +32,54 @@ constexpr int64_t kItemTarget = 2048;               // work items a call aims fo
 template <int D>
 constexpr int part_width() { return 4 + D; }
 constexpr int kDecThreads = 256;
+// Split workgroups per call at most (eight per CU); larger calls loop over their items.
+constexpr int64_t kMaxSplitGroups = 256 * 8;
+// Calls over at most kInlineSlices slices whose items (at the smallest item size) fit one pass
+// of the grid skip the plan kernel: every split workgroup scans the lengths into LDS itself,
+// picks the item size from the total length and finds its item there.  Larger calls keep the
+// plan kernel, whose cost is then shared by several items per workgroup.
+constexpr int kInlineSlices = 1024;
+constexpr int kInlineTSplitMin = 256, kInlineItems = 256;  // one item per CU
+
+static bool dec_inline(int64_t num_slices, int32_t max_len) {
+  return num_slices <= kInlineSlices &&
+         num_slices * (int64_t)((max_len + kInlineTSplitMin - 1) / kInlineTSplitMin) <= kMaxSplitGroups;
+}
+
+// Item size of an in-kernel plan from the total length T of the call: about one item per CU
+// (a short call is bound by each wave's chain of dependent loads, so it pays to spread it over
+// every CU once), a multiple of 16 tokens, within [kInlineTSplitMin, kTSplitMax].
+__device__ __forceinline__ int inline_split_tokens(int T) {
+  const int ts = ((T + kInlineItems - 1) / kInlineItems + 15) / 16 * 16;
+  return min(max(ts, kInlineTSplitMin), kTSplitMax);
+}
+
+__device__ __forceinline__ bool len_ok(const DecArgs &a, int s) {
+  return s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
+}
+
+// Exclusive prefix sum of one value per thread over a block of NT threads; *total gets the
+// block's sum.  wsum: NT / 64 ints of LDS.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    before += i < w ? wsum[i] : 0;
+    all += wsum[i];
+  }
+  *total = all;
+  return before + incl - v;
+}
 
 
 __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
@@ -40,39 +88,27 @@ __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
   if (t == 0) *a.err = 0;
   __syncthreads();
   const int64_t S = a.num_slices;
-  const int64_t per = (S + blockDim.x - 1) / blockDim.x;
+  const int64_t per = (S + 1023) / 1024;
   const int64_t z0 = t * per, z1 = min(S, z0 + per);
   int local = 0;
   for (int64_t z = z0; z < z1; ++z) {
     const int s = a.lens[z];
-    const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
+    const bool ok = len_ok(a, s);
     if (!ok) atomicExch(a.err, kDeviceError);
     local += ok ? (s + a.tsplit - 1) / a.tsplit : 0;
   }
-  // block exclusive scan of `local`
-  int incl = local;
-  const int lane = t & 63, w = t >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += wsum[i];
-  int run = before + incl - local;
+  int total;
+  int run = block_excl_scan<1024>(local, wsum, &total);
   for (int64_t z = z0; z < z1; ++z) {
     a.item_off[z] = run;
     const int s = a.lens[z];
-    const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
-    const int cnt = ok ? (s + a.tsplit - 1) / a.tsplit : 0;
+    const int cnt = len_ok(a, s) ? (s + a.tsplit - 1) / a.tsplit : 0;
     for (int p = 0; p < cnt; ++p)  // (slice, first token, end token): one load in dec_split
       *reinterpret_cast<int4 *>(a.item_zp + 4 * (int64_t)(run + p)) =
           make_int4((int)z, p * a.tsplit, min(s, (p + 1) * a.tsplit), 0);
     run += cnt;
   }
-  if (t == (int)blockDim.x - 1) a.item_off[S] = before + incl;
+  if (t == 1023) a.item_off[S] = total;
 }
 
 template <typename T, int G, int D>
@@ -217,27 +253,59 @@ constexpr int dec_head_sets() { return G >= 8 ? 2 : 1; }
 template <int G>
 constexpr int dec_threads() { return kDecThreads * dec_head_sets<G>(); }
 
-template <typename T, int G, int D>
+// INL: the items are found from the lengths in the kernel (calls over at most kInlineSlices
+// slices), else read from the plan kernel's table.
+template <typename T, int G, int D, bool INL>
 __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_split(DecArgs a) {
   constexpr int HS = dec_head_sets<G>(), GW = G / HS, NT = dec_threads<G>();
   using DT = DecTile<T, GW, D>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
   constexpr int PW = part_width<D>();  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][G][PW];
+  __shared__ int32_t s_off[kInlineSlices + 1], s_len[kInlineSlices], s_wsum[NT / 64],
+      s_wsum2[NT / 64];
   const int t = threadIdx.x, w = (t >> 6) & 3, hs = t >> 8, l = t & 63;
   const int sg = l % LPR, rw = l / LPR;
-  const int64_t S = a.num_slices;
-  const int total = a.item_off[S];
+  const int S = (int)a.num_slices;
   const float NEG_INF = -__builtin_inff();
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int4 it4 = *reinterpret_cast<const int4 *>(a.item_zp + 4 * (int64_t)item);
-    const int64_t z = it4.x;
-    const int tok0 = it4.y, tok1 = it4.z;
+  int total, ts = a.tsplit;
+  if constexpr (INL) {
+    // item counts of all slices, scanned into LDS (a bad length counts 0 items).  Workgroup
+    // 0 also stores the offsets for the combine kernel and sets the error word.
+    const int per = (S + NT - 1) / NT, z0 = t * per, z1 = min(S, z0 + per);
+    int sum = 0, bad = 0;
+    for (int z = z0; z < z1; ++z) {
+      const int s = a.lens[z];
+      const bool ok = len_ok(a, s);
+      bad |= !ok;
+      s_len[z] = ok ? s : 0;
+      sum += ok ? s : 0;
+    }
+    int tot_len;
+    block_excl_scan<NT>(sum, s_wsum, &tot_len);
+    ts = __builtin_amdgcn_readfirstlane(inline_split_tokens(tot_len));
+    int local = 0;
+    for (int z = z0; z < z1; ++z) local += (s_len[z] + ts - 1) / ts;
+    int run = block_excl_scan<NT>(local, s_wsum2, &total);
+    total = __builtin_amdgcn_readfirstlane(total);
+    for (int z = z0; z < z1; ++z) {
+      s_off[z] = run;
+      if (blockIdx.x == 0) a.item_off[z] = run;
+      run += (s_len[z] + ts - 1) / ts;
+    }
+    if (blockIdx.x == 0 && t == 0) a.item_off[S] = total;
+    const int any_bad = __syncthreads_or(bad);
+    if (blockIdx.x == 0 && t == 0) *a.err = any_bad ? kDeviceError : 0;
+  } else {
+    total = a.item_off[S];
+  }
+  // one work item: tokens [tok0, tok1) of slice z
+  auto process = [&](int item, int64_t z, int tok0, int tok1) {
     const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
     const char *Kz = a.K + z * a.cap * ROWB;
     const char *Vz = a.V + z * a.cap * ROWB;
     const int32_t *Nz = a.N + z * a.cap;
-    const int wq = a.tsplit / 4;
+    const int wq = ts / 4;
     const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
     // two register stages: the next sub-block loads while the current one is computed
     DecStage<DT::NR> A, B;
@@ -307,41 +375,60 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
       dst[i] = v;
     }
     __syncthreads();
+  };
+  if constexpr (INL) {
+    // the grid covers every item once (at most one per workgroup).  The item's slice is the
+    // last z with s_off[z] <= item (slices without items share their offset with the next
+    // one).  The LDS values are the same in every lane; readfirstlane keeps the search and
+    // the item bounds in scalar registers.
+    const int item = blockIdx.x;
+    if (item >= total) return;
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= item) lo = mid; else hi = mid - 1;
+    }
+    const int tok0 = (item - __builtin_amdgcn_readfirstlane(s_off[lo])) * ts;
+    process(item, lo, tok0, min(__builtin_amdgcn_readfirstlane(s_len[lo]), tok0 + ts));
+  } else {
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+      const int4 it4 = *reinterpret_cast<const int4 *>(a.item_zp + 4 * (int64_t)item);
+      process(item, it4.x, it4.y, it4.z);
+    }
   }
 }
 
-// One workgroup per slice, every head at once.  1. per-head maximum of the item maxima
-// (strided loads, wave reductions over the lanes of one head, four waves through LDS);
-// 2. each thread takes 4 output elements of one head and one of 8/G item groups and sums the
-// rescaled partials, four independent items per step; 3. the item groups are summed through
-// LDS and divided.
+// One workgroup per slice, every head at once, in one pass over the partials: each thread
+// takes 4 output elements of one head and one of 8/G item groups and sums the partials against
+// a running maximum (rescaling its sums when the maximum grows), four independent items per
+// step; the item groups are then merged through LDS against their common maximum and divided.
 template <int G, int D>
 __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
   constexpr int PW = part_width<D>();
   constexpr int CPH = D / 4;      // 4-element columns per head
   constexpr int COLS = CPH * G;   // columns over the G heads
   constexpr int IG = 256 / COLS;  // item groups
-  __shared__ float s_mx[4][G];
   __shared__ __attribute__((aligned(16))) float s_acc[IG][G][D];
-  __shared__ float s_l[IG][G];
+  __shared__ float s_l[IG][G], s_m[IG][G];
   const int64_t z = blockIdx.x;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63;
-  const int i0 = a.item_off[z], i1 = a.item_off[z + 1];
+  const int t = threadIdx.x;
   const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
   const float NEG_INF = -__builtin_inff();
-  {
-    const int h = t % G;
-    float m = NEG_INF;
-    for (int it = i0 + t / G; it < i1; it += 256 / G)
-      m = fmaxf(m, a.part[((int64_t)it * G + h) * PW]);
-#pragma unroll
-    for (int o = G; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (l < G) s_mx[w][l] = m;
-  }
-  __syncthreads();
+  const int i0 = a.item_off[z], i1 = a.item_off[z + 1];
+  // one pass: a running maximum per thread, the sums rescaled when it grows
   const int col = t % COLS, grp = t / COLS, h = col / CPH, e4 = (col % CPH) * 4;
-  const float M = fmaxf(fmaxf(s_mx[0][h], s_mx[1][h]), fmaxf(s_mx[2][h], s_mx[3][h]));
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
+  float M = NEG_INF, acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
+  auto rescale = [&](float mnew) {
+    if (mnew > M) {
+      const float sc = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
+      L *= sc;
+      acc0 *= sc;
+      acc1 *= sc;
+      acc2 *= sc;
+      acc3 *= sc;
+      M = mnew;
+    }
+  };
   auto add = [&](float m, float lsum, float4 o) {
     const float wgt = m == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m - M);
     L = fmaf(wgt, lsum, L);
@@ -362,39 +449,56 @@ __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
       ls[k] = head.y;
       o[k] = *reinterpret_cast<const float4 *>(pp + 4 + e4);
     }
+    rescale(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])));
 #pragma unroll
     for (int k = 0; k < 4; ++k) add(m[k], ls[k], o[k]);
   }
   for (; it < i1; it += IG) {
     const float *pp = a.part + ((int64_t)it * G + h) * PW;
     const float4 head = *reinterpret_cast<const float4 *>(pp);
+    rescale(head.x);
     add(head.x, head.y, *reinterpret_cast<const float4 *>(pp + 4 + e4));
   }
+  // every column of (grp, h) saw the same maxima, so one of them records M and L
   *reinterpret_cast<float4 *>(&s_acc[grp][h][e4]) = make_float4(acc0, acc1, acc2, acc3);
-  if (e4 == 0) s_l[grp][h] = L;
+  if (e4 == 0) {
+    s_l[grp][h] = L;
+    s_m[grp][h] = M;
+  }
   __syncthreads();
   for (int i = t; i < G * D; i += 256) {
     const int hh = i / D, d = i % D;
+    float Mx = NEG_INF;
+#pragma unroll
+    for (int q = 0; q < IG; ++q) Mx = fmaxf(Mx, s_m[q][hh]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int q = 0; q < IG; ++q) {
-      num += s_acc[q][hh][d];
-      den += s_l[q][hh];
+      const float mq = s_m[q][hh];
+      const float wq = mq == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mq - Mx);
+      num = fmaf(wq, s_acc[q][hh][d], num);
+      den = fmaf(wq, s_l[q][hh], den);
     }
     a.O[(g * a.H_q + kvh * G + hh) * (int64_t)D + d] = den > 0.f ? num / den : 0.f;
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool INL>
 static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((dec_split<T, 1, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((dec_split<T, 2, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((dec_split<T, 4, D>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_split<T, 8, D>), dim3(grid), dim3(dec_threads<8>()), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((dec_split<T, 1, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((dec_split<T, 2, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((dec_split<T, 4, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_split<T, 8, D, INL>), dim3(grid), dim3(dec_threads<8>()), 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+template <typename T, int D>
+static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
+  return a.inline_items ? launch_dec_t<T, D, true>(a, G, grid, st)
+                        : launch_dec_t<T, D, false>(a, G, grid, st);
 }
 
 template <int D>
@@ -425,15 +529,20 @@ int32_t dec_split_tokens(int64_t num_slices, int32_t max_len) {
 }
 
 int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
-  const int32_t ts = dec_split_tokens(num_slices, max_len);
+  const int32_t ts = dec_inline(num_slices, max_len) ? kInlineTSplitMin
+                                                     : dec_split_tokens(num_slices, max_len);
   return num_slices * (int64_t)((max_len + ts - 1) / ts);
 }
 
-int launch_decode(const DecArgs &a, int dtype, int d, int G, int64_t max_items, hipStream_t st) {
-  hipLaunchKernelGGL(dec_prep, dim3(1), dim3(1024), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_items, 256 * 8));
+int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_items, hipStream_t st) {
+  DecArgs a = args;
+  a.inline_items = dec_inline(a.num_slices, a.max_len);
+  if (!a.inline_items) {
+    hipLaunchKernelGGL(dec_prep, dim3(1), dim3(1024), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_items, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
   if (rc) return rc;
   return d == 64 ? launch_combine<64>(a, G, st) : launch_combine<128>(a, G, st);

@@ -40,11 +40,12 @@ struct DecArgs {
   float *O;
   int64_t num_slices, cap;
   int32_t max_len, H_q, H_kv;
-  int32_t tsplit;     // tokens per work item (dec_split_tokens of num_slices, max_len)
+  int32_t tsplit;     // tokens per work item of the plan kernel (dec_split_tokens)
   float scale_log2;   // log2(e) / sqrt(d)
   int32_t *err;       // device error word of this call
-  int32_t *item_off;  // [num_slices + 1] first work item of each slice
+  int32_t *item_off;  // [num_slices + 1] first work item of each slice (plan kernel only)
   int32_t *item_zp;   // [items][4] (slice, first token, end token, 0) of every work item
+  int32_t inline_items;  // 1: the split and combine kernels derive the items from lens
   float *part;        // [items][G][4 + d] (max, sum, 0, 0, o) partials
 };
 

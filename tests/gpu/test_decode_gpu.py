@@ -67,8 +67,9 @@ def test_head_dim_64_ragged(lib, dev, dtype, H_q, H_kv):
 
 
 def _split_tokens(S, max_len):
-    """The work-item size rule stated in the decode kernel: 512 tokens when that gives at most
-    about 2048 items over the length bound, else 1024."""
+    """The work-item size rule stated in the decode kernel for calls planned by the plan
+    kernel: 512 tokens when that gives at most about 2048 items over the length bound, else
+    1024."""
     want = S * max_len // 2048
     ts = 512
     while ts < 1024 and ts < want:
@@ -76,26 +77,31 @@ def _split_tokens(S, max_len):
     return ts
 
 
-@pytest.mark.parametrize("ts,S,cap", [(512, 16, 1544), (512, 400, 1544), (1024, 400, 3080)])
-def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
-    """Each work-item size, with lengths on both sides of item boundaries; the cache is built
-    on the device and one slice of every distinct length is checked against the oracle."""
-    assert _split_tokens(S, cap) == ts
+def _plans_inline(S, max_len):
+    """Calls over at most 1024 slices with at most 2048 items of 256 tokens over the length
+    bound find their items inside the split kernel."""
+    return S <= 1024 and S * -(-max_len // 256) <= 2048
+
+
+def _inline_split_tokens(lens, max_len):
+    """The in-kernel item size: the total length over 256 items, rounded up to 16 tokens,
+    within [256, 1024]."""
+    T = sum(int(s) for s in lens if 0 <= s <= max_len)
+    return min(max(-(-(-(-T // 256)) // 16) * 16, 256), 1024)
+
+
+def _check_item_sizes(lib, dev, S, cap, lens, ts, seed, check):
     H_q, H_kv = 8, 2
     G = H_q // H_kv
-    gen = torch.Generator(device=dev).manual_seed(ts)
+    gen = torch.Generator(device=dev).manual_seed(seed)
     K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
     V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
     N = torch.randint(1, 30, (S, cap), generator=gen, device=dev, dtype=torch.int32)
-    choices = [0, 1, ts - 1, ts, ts + 1, 2 * ts, 2 * ts + 1, 3 * ts - 1, 3 * ts, cap]
-    rng = np.random.default_rng(ts)
-    lens = rng.choice(choices, size=S)
-    lens[:len(choices)] = choices
-    L = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    L = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(dev)
     q = torch.randn((S // H_kv, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
     O = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, max_len=cap).cpu().double().numpy()
     worst = 0.0
-    for z in range(len(choices)):
+    for z in check:
         g, kvh = divmod(z, H_kv)
         s = int(lens[z])
         Kz, Vz = parity.to_f64(K[z, :s].cpu()), parity.to_f64(V[z, :s].cpu())
@@ -109,6 +115,30 @@ def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
             worst = max(worst, float(np.abs(O[g, hq] - ref).max()))
     print("tsplit", ts, "max abs", worst)
     assert worst < 2e-4
+
+
+@pytest.mark.parametrize("ts,S,cap", [(512, 400, 1544), (1024, 400, 3080)])
+def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
+    """Each work-item size of the plan kernel, with lengths on both sides of item boundaries;
+    the cache is built on the device and one slice of every distinct length is checked
+    against the oracle."""
+    assert not _plans_inline(S, cap) and _split_tokens(S, cap) == ts
+    choices = [0, 1, ts - 1, ts, ts + 1, 2 * ts, 2 * ts + 1, 3 * ts - 1, 3 * ts, cap]
+    rng = np.random.default_rng(ts)
+    lens = rng.choice(choices, size=S)
+    lens[:len(choices)] = choices
+    _check_item_sizes(lib, dev, S, cap, lens, ts, ts, range(len(choices)))
+
+
+@pytest.mark.parametrize("ts,S,cap,lens", [
+    (256, 16, 1544, [0, 1, 255, 256, 257, 512, 513, 767, 768, 1544, 1544, 0, 300, 1000, 7, 256]),
+    (400, 8, 50000, [0, 1, 399, 400, 401, 1199, 48001, 49599]),
+])
+def test_inline_work_item_sizes(lib, dev, ts, S, cap, lens):
+    """Small calls pick the item size in the kernel from the total length (about one item per
+    CU); lengths on both sides of its item boundaries, every slice against the oracle."""
+    assert _plans_inline(S, cap) and _inline_split_tokens(lens, cap) == ts
+    _check_item_sizes(lib, dev, S, cap, lens, ts, ts + 1, range(S))
 
 
 def test_per_layer_calls_match_one_call(lib, dev):
@@ -229,6 +259,46 @@ def test_bad_length_gives_zeros_and_error(lib, dev):
     O2 = lib.decode_attn_logn(q.to(dev), Kd, Vd, Nd, Ld, 1, 1, max_len=700, workspace=ws)
     assert lib.read_error(ws) == lib.OK
     assert torch.equal(O2[0], O[0]) and torch.any(O2[1] != 0)
+
+
+def test_item_plan_kernel_and_inline_plan_agree(lib, dev):
+    """The same call planned both ways: under a tight length bound the split kernel finds its
+    items from the lengths (item size from the total length: 512 here), under a loose one the
+    plan kernel lays them out (512 again).  Same items, so bit-identical outputs; a bad length
+    is reported by both and gives zeros; every slice against the oracle."""
+    S, cap, H_q, tight = 20, 40000, 4, 16384
+    lens = [0, 1, 511, 512, 513, 1023, 1024, 1025, tight, cap + 1]   # slice 9: above every bound
+    rest = 129000 - sum(x for x in lens if x <= tight)                 # total length 129000
+    lens += [rest // 10] * 9 + [rest - 9 * (rest // 10)]
+    assert _plans_inline(S, tight) and _inline_split_tokens(lens, tight) == 512
+    assert not _plans_inline(S, cap) and _split_tokens(S, cap) == 512
+    gen = torch.Generator(device=dev).manual_seed(31)
+    K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.randint(1, 40, (S, cap), generator=gen, device=dev, dtype=torch.int32)
+    L = torch.tensor(lens, dtype=torch.int32, device=dev)
+    q = torch.randn((S, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
+    outs = []
+    for ml in (tight, cap):
+        ws = torch.full((lib.decode_workspace_bytes(K, H_q, 1, max_len=ml),), 0x5A,
+                        dtype=torch.uint8, device=dev)
+        outs.append(lib.decode_attn_logn(q, K, V, N, L, H_q, 1, max_len=ml, workspace=ws))
+        assert lib.read_error(ws) == lib.EDEVICE, ml
+    assert torch.equal(outs[0], outs[1])
+    assert torch.all(outs[0][9] == 0)
+    worst = 0.0
+    for z in range(S):
+        s = lens[z]
+        for h in range(H_q):
+            got = outs[0][z, h].cpu().double().numpy()
+            if s == 0 or s > tight:
+                assert np.all(got == 0)
+                continue
+            ref = oatt.logn_attention_one(parity.to_f64(q[z, h].cpu()), parity.to_f64(K[z, :s].cpu()),
+                                          parity.to_f64(V[z, :s].cpu()),
+                                          N[z, :s].cpu().numpy().astype(np.int64))
+            worst = max(worst, float(np.abs(got - ref).max()))
+    assert worst < 2e-4
 
 
 def test_workspace_reused_across_calls_and_geometries(lib, dev):

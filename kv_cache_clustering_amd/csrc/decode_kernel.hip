@@ -32,6 +32,9 @@ constexpr int64_t kItemTarget = 2048;               // work items a call aims fo
 template <int D>
 constexpr int part_width() { return 4 + D; }
 constexpr int kDecThreads = 256;
+#ifndef DEC_NS
+#define DEC_NS 3
+#endif
 // Split workgroups per call at most (eight per CU); larger calls loop over their items.
 constexpr int64_t kMaxSplitGroups = 256 * 8;
 // Calls over at most kInlineSlices slices whose items (at the smallest item size) fit one pass
@@ -117,6 +120,7 @@ struct DecTile {
   static constexpr int LPR = ROWB / 16;     // lanes per row
   static constexpr int RPW = 64 / LPR;      // rows per wave-wide load
   static constexpr int NR = G >= 8 ? 2 : 4;  // wave loads per sub-block (fewer for 8 heads a wave)
+  static constexpr int NS = DEC_NS;          // register stages
   static constexpr int SUB = NR * RPW;      // rows per sub-block
   static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
 };
@@ -179,21 +183,48 @@ struct DecStage {
   int32_t n[NR];
 };
 
+// A wave's rows [wb, we) of one slice as three buffer resources (K, V, N).  Loads through
+// them are range-checked by the hardware: a row at or past `we` reads as zeros without touching
+// memory, so every load of the stream is issued unconditionally.  (Loads guarded by per-lane
+// branches made the compiler wait for all outstanding loads before each sub-block, which turned
+// the register stages into one memory round trip per sub-block.)
+struct DecRows {
+  __amdgpu_buffer_rsrc_t k, v, n;
+};
+constexpr int kBufWord3 = 0x00020000;  // raw (unformatted) buffer, 32-bit data format
+// A pointer that holds the same value in every lane, moved to scalar registers (the compiler
+// cannot always prove that a slice index found at run time is wave-uniform).
+__device__ __forceinline__ void *wave_uniform(const void *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<void *>(lo | (hi << 32));
+}
+__device__ __forceinline__ DecRows dec_rows(const char *Kz, const char *Vz, const int32_t *Nz,
+                                            int rowb, int wb, int we) {
+  const int rows = __builtin_amdgcn_readfirstlane(max(we - wb, 0));
+  return {__builtin_amdgcn_make_buffer_rsrc(wave_uniform(Kz + (int64_t)wb * rowb), 0, rows * rowb,
+                                            kBufWord3),
+          __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Vz + (int64_t)wb * rowb), 0, rows * rowb,
+                                            kBufWord3),
+          __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Nz + wb), 0, rows * 4, kBufWord3)};
+}
+
+// Rows rel .. rel + SUB - 1 (relative to wb) of the wave's range, 16 B per lane per row.
 // NTL: non-temporal loads (each row is read by one wave only); plain loads where two waves
 // read the same rows, so that the second read is served by the cache.
 template <typename T, int G, int D, bool NTL = true>
-__device__ __forceinline__ void dec_load(DecStage<DecTile<T, G, D>::NR> &st, const char *Kz, const char *Vz,
-                                         const int32_t *Nz, int sb, int we, int rw, int sg) {
+__device__ __forceinline__ void dec_load(DecStage<DecTile<T, G, D>::NR> &st, const DecRows &rs,
+                                         int rel, int rw, int sg) {
   using DT = DecTile<T, G, D>;
+  constexpr int aux = NTL ? 2 : 0;  // nt
 #pragma unroll
   for (int i = 0; i < DT::NR; ++i) {
-    const int tok = sb + DT::RPW * i + rw;
-    const bool ok = tok < we;
-    const u32x4 *kp = reinterpret_cast<const u32x4 *>(Kz + (int64_t)tok * DT::ROWB + sg * 16);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(Vz + (int64_t)tok * DT::ROWB + sg * 16);
-    st.k[i] = ok ? (NTL ? __builtin_nontemporal_load(kp) : *kp) : u32x4{0u, 0u, 0u, 0u};
-    st.v[i] = ok ? (NTL ? __builtin_nontemporal_load(vp) : *vp) : u32x4{0u, 0u, 0u, 0u};
-    st.n[i] = ok ? Nz[tok] : 0;
+    const int row = rel + DT::RPW * i + rw;
+    const int off = row * DT::ROWB + sg * 16;
+    st.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, off, 0, aux));
+    st.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, off, 0, aux));
+    st.n[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs.n, row * 4, 0, 0);
   }
 }
 
@@ -306,15 +337,21 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
     const char *Vz = a.V + z * a.cap * ROWB;
     const int32_t *Nz = a.N + z * a.cap;
     const int wq = ts / 4;
-    const int wb = tok0 + w * wq, we = min(tok1, wb + wq);
-    // two register stages: the next sub-block loads while the current one is computed
-    DecStage<DT::NR> A, B;
-    if (wb < we) dec_load<T, GW, D, HS == 1>(A, Kz, Vz, Nz, wb, we, rw, sg);
-    // this lane's q segment for each head of the wave's head set
+    // the wave's token range, in scalar registers (the buffer resources must be wave-uniform)
+    const int wb = __builtin_amdgcn_readfirstlane(tok0 + w * wq);
+    const int we = __builtin_amdgcn_readfirstlane(min(tok1, wb + wq));
+    const DecRows rs = dec_rows(Kz, Vz, Nz, ROWB, wb, we);
+    // this lane's q segment for each head of the wave's head set, loaded first: loads retire in
+    // order, so q issued after the stages would make the first sub-block wait for all of them
     u32x4 qv[GW];
 #pragma unroll
     for (int h = 0; h < GW; ++h)
       qv[h] = ld16(a.q + ((g * a.H_q + kvh * G + hs * GW + h) * (int64_t)D) * sizeof(T) + sg * 16);
+    // NS register stages: the next NS - 1 sub-blocks load while the current one is computed
+    constexpr int NS = DT::NS;
+    DecStage<DT::NR> st[NS];
+#pragma unroll
+    for (int k = 0; k + 1 < NS; ++k) dec_load<T, GW, D, HS == 1>(st[k], rs, k * SUB, rw, sg);
     float mrun[GW], lrun[GW], o[GW][EPL];
 #pragma unroll
     for (int h = 0; h < GW; ++h) {
@@ -323,13 +360,16 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
     }
-    for (int sb = wb; sb < we; sb += 2 * SUB) {
-      const int sb1 = sb + SUB;
-      if (sb1 < we) dec_load<T, GW, D, HS == 1>(B, Kz, Vz, Nz, sb1, we, rw, sg);
-      dec_compute<T, GW, D>(A, sb, we, rw, qv, a.scale_log2, mrun, lrun, o);
-      if (sb1 >= we) break;
-      if (sb1 + SUB < we) dec_load<T, GW, D, HS == 1>(A, Kz, Vz, Nz, sb1 + SUB, we, rw, sg);
-      dec_compute<T, GW, D>(B, sb1, we, rw, qv, a.scale_log2, mrun, lrun, o);
+    for (int sb = wb; sb < we; sb += NS * SUB) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int cur = sb + k * SUB, nxt = cur + (NS - 1) * SUB;
+        if (cur >= we) break;
+        // stage (k + NS - 1) % NS was computed last: refill it with the sub-block NS - 1 ahead
+        // (past the range the loads read zeros and move no data)
+        dec_load<T, GW, D, HS == 1>(st[(k + NS - 1) % NS], rs, nxt - wb, rw, sg);
+        dec_compute<T, GW, D>(st[k], cur, we, rw, qv, a.scale_log2, mrun, lrun, o);
+      }
     }
     // sum the row groups of the wave (they hold different tokens, same segment)
 #pragma unroll

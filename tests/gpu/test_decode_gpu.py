@@ -355,3 +355,44 @@ def test_seeded_sweep_decode(lib, dev):
     print({str(k): v for k, v in worst.items()})
     assert worst[torch.float32] < 2e-5
     assert worst[torch.bfloat16] < 2e-4 and worst[torch.float16] < 2e-4
+
+
+def test_seeded_sweep_decode_plan_kernel(lib, dev):
+    """Every storage format, head dim and head group (1, 2, 4, 8) on calls large enough to be
+    planned by the plan kernel (40 slices of up to 14000 tokens): ragged lengths including 0 and
+    the bound, degrees 1..1000; sampled slices, every head, against the oracle."""
+    rng = np.random.default_rng(91)
+    S, H_kv, cap = 40, 2, 14000
+    assert not _plans_inline(S, cap)
+    worst = {}
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
+        for d in (64, 128):
+            for G in (1, 2, 4, 8):
+                H_q = G * H_kv
+                gen = torch.Generator(device=dev).manual_seed(int(rng.integers(1 << 30)))
+                K = torch.randn((S, cap, d), generator=gen, device=dev).to(dtype)
+                V = torch.randn((S, cap, d), generator=gen, device=dev).to(dtype)
+                N = torch.randint(1, 1001, (S, cap), generator=gen, device=dev, dtype=torch.int32)
+                lens = rng.integers(0, cap + 1, size=S)
+                lens[:4] = [0, 1, cap, 513]
+                L = torch.from_numpy(lens.astype(np.int32)).to(dev)
+                q = torch.randn((S // H_kv, H_q, d), generator=gen, device=dev).to(dtype)
+                O = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, max_len=cap).cpu().double().numpy()
+                for z in [0, 1, 2, 3, int(rng.integers(4, S)), S - 1]:
+                    g, kvh = divmod(z, H_kv)
+                    s = int(lens[z])
+                    for h in range(G):
+                        hq = kvh * G + h
+                        if s == 0:
+                            assert np.all(O[g, hq] == 0)
+                            continue
+                        ref = oatt.logn_attention_one(parity.to_f64(q[g, hq].cpu()),
+                                                      parity.to_f64(K[z, :s].cpu()),
+                                                      parity.to_f64(V[z, :s].cpu()),
+                                                      N[z, :s].cpu().numpy().astype(np.int64))
+                        key = str(dtype)
+                        worst[key] = max(worst.get(key, 0.0), float(np.abs(O[g, hq] - ref).max()))
+                del K, V, N
+    print(worst)
+    assert worst[str(torch.float32)] < 2e-5
+    assert worst[str(torch.bfloat16)] < 2e-4 and worst[str(torch.float16)] < 2e-4

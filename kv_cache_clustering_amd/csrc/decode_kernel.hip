@@ -26,7 +26,7 @@
 
 namespace csmkv {
 
-constexpr int kTSplitMin = 512, kTSplitMax = 1024;  // tokens per work item
+constexpr int kTSplitMin = 512, kTSplitMax = 2048;  // tokens per work item
 constexpr int64_t kItemTarget = 2048;               // work items a call aims for
 // floats per (item, head) partial: (max, sum, 0, 0, o[d]), 16-byte aligned rows
 template <int D>
@@ -55,6 +55,12 @@ static bool dec_inline(int64_t num_slices, int32_t max_len) {
 __device__ __forceinline__ int inline_split_tokens(int T) {
   const int ts = ((T + kInlineItems - 1) / kInlineItems + 15) / 16 * 16;
   return min(max(ts, kInlineTSplitMin), kTSplitMax);
+}
+
+// First token of item p when a slice of s tokens is cut into cnt items of as equal a length
+// as tokens allow (cnt = ceil(s / item size), so no item is longer than the item size).
+__device__ __forceinline__ int item_bound(int p, int s, int cnt) {
+  return (int)((int64_t)p * s / cnt);
 }
 
 __device__ __forceinline__ bool len_ok(const DecArgs &a, int s) {
@@ -108,7 +114,7 @@ __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
     const int cnt = len_ok(a, s) ? (s + a.tsplit - 1) / a.tsplit : 0;
     for (int p = 0; p < cnt; ++p)  // (slice, first token, end token): one load in dec_split
       *reinterpret_cast<int4 *>(a.item_zp + 4 * (int64_t)(run + p)) =
-          make_int4((int)z, p * a.tsplit, min(s, (p + 1) * a.tsplit), 0);
+          make_int4((int)z, item_bound(p, s, cnt), item_bound(p + 1, s, cnt), 0);
     run += cnt;
   }
   if (t == 1023) a.item_off[S] = total;
@@ -336,7 +342,7 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
     const char *Kz = a.K + z * a.cap * ROWB;
     const char *Vz = a.V + z * a.cap * ROWB;
     const int32_t *Nz = a.N + z * a.cap;
-    const int wq = ts / 4;
+    const int wq = (tok1 - tok0 + 3) / 4;  // the item's tokens over the four waves
     // the wave's token range, in scalar registers (the buffer resources must be wave-uniform)
     const int wb = __builtin_amdgcn_readfirstlane(tok0 + w * wq);
     const int we = __builtin_amdgcn_readfirstlane(min(tok1, wb + wq));
@@ -428,8 +434,9 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
       const int mid = (lo + hi + 1) >> 1;
       if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= item) lo = mid; else hi = mid - 1;
     }
-    const int tok0 = (item - __builtin_amdgcn_readfirstlane(s_off[lo])) * ts;
-    process(item, lo, tok0, min(__builtin_amdgcn_readfirstlane(s_len[lo]), tok0 + ts));
+    const int p = item - __builtin_amdgcn_readfirstlane(s_off[lo]);
+    const int len = __builtin_amdgcn_readfirstlane(s_len[lo]), cnt = (len + ts - 1) / ts;
+    process(item, lo, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
   } else {
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
       const int4 it4 = *reinterpret_cast<const int4 *>(a.item_zp + 4 * (int64_t)item);

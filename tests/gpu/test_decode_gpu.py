@@ -68,11 +68,11 @@ def test_head_dim_64_ragged(lib, dev, dtype, H_q, H_kv):
 
 def _split_tokens(S, max_len):
     """The work-item size rule stated in the decode kernel for calls planned by the plan
-    kernel: 512 tokens when that gives at most about 2048 items over the length bound, else
-    1024."""
+    kernel: the smallest of 512, 1024 and 2048 tokens that gives at most about 2048 items over
+    the length bound (2048 if none does)."""
     want = S * max_len // 2048
     ts = 512
-    while ts < 1024 and ts < want:
+    while ts < 2048 and ts < want:
         ts *= 2
     return ts
 
@@ -85,9 +85,9 @@ def _plans_inline(S, max_len):
 
 def _inline_split_tokens(lens, max_len):
     """The in-kernel item size: the total length over 256 items, rounded up to 16 tokens,
-    within [256, 1024]."""
+    within [256, 2048]."""
     T = sum(int(s) for s in lens if 0 <= s <= max_len)
-    return min(max(-(-(-(-T // 256)) // 16) * 16, 256), 1024)
+    return min(max(-(-(-(-T // 256)) // 16) * 16, 256), 2048)
 
 
 def _check_item_sizes(lib, dev, S, cap, lens, ts, seed, check):
@@ -117,7 +117,7 @@ def _check_item_sizes(lib, dev, S, cap, lens, ts, seed, check):
     assert worst < 2e-4
 
 
-@pytest.mark.parametrize("ts,S,cap", [(512, 400, 1544), (1024, 400, 3080)])
+@pytest.mark.parametrize("ts,S,cap", [(512, 400, 1544), (1024, 400, 3080), (2048, 400, 6200)])
 def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
     """Each work-item size of the plan kernel, with lengths on both sides of item boundaries;
     the cache is built on the device and one slice of every distinct length is checked

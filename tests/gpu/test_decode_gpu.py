@@ -119,9 +119,10 @@ def _check_item_sizes(lib, dev, S, cap, lens, ts, seed, check):
 
 @pytest.mark.parametrize("ts,S,cap", [(512, 400, 1544), (1024, 400, 3080), (2048, 400, 6200)])
 def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
-    """Each work-item size of the plan kernel, with lengths on both sides of item boundaries;
-    the cache is built on the device and one slice of every distinct length is checked
-    against the oracle."""
+    """Each work-item size of the plan kernel, with lengths on both sides of its multiples
+    (where a slice's item count, and so the cut of its tokens into items, changes); the cache
+    is built on the device and one slice of every distinct length is checked against the
+    oracle."""
     assert not _plans_inline(S, cap) and _split_tokens(S, cap) == ts
     choices = [0, 1, ts - 1, ts, ts + 1, 2 * ts, 2 * ts + 1, 3 * ts - 1, 3 * ts, cap]
     rng = np.random.default_rng(ts)
@@ -136,7 +137,8 @@ def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
 ])
 def test_inline_work_item_sizes(lib, dev, ts, S, cap, lens):
     """Small calls pick the item size in the kernel from the total length (about one item per
-    CU); lengths on both sides of its item boundaries, every slice against the oracle."""
+    CU); lengths on both sides of its multiples (where a slice's item count changes), every
+    slice against the oracle."""
     assert _plans_inline(S, cap) and _inline_split_tokens(lens, cap) == ts
     _check_item_sizes(lib, dev, S, cap, lens, ts, ts + 1, range(S))
 

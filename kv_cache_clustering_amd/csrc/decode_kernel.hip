@@ -3,11 +3,12 @@
 // cluster degrees n_t; Algorithm 1 decode output), and the Algorithm 1 append step.
 //
 // Split-K over the sequence, HBM-bound:
-//   dec_prep    : one workgroup validates lens[], gives every slice ceil(len / tsplit)
-//                 work items and scans them into item offsets.  tsplit (512 or 1024
-//                 tokens) is chosen on the host from the slice count and the length bound so
-//                 that a call has about 2048 items: a call over one layer's few slices still
-//                 spreads over every CU, a call over many slices keeps items long.
+//   dec_prep    : (calls over more than 1024 slices) one workgroup validates lens[], gives
+//                 every slice ceil(len / tsplit) work items and scans them into item offsets.
+//                 tsplit (512 to 2048 tokens) is chosen on the host from the slice count and
+//                 the length bound so that a call has about 2048 items.  Smaller calls plan
+//                 in the split kernel itself, from the total length: about one item per CU
+//                 for a layer's few slices, items of up to 2048 tokens for many slices.
 //   dec_split   : persistent workgroups stride over the work items.  A work item is
 //                 tsplit tokens of one slice, shared by the G query heads of that KV
 //                 head, so K, V and N are read once per step.  Each wave streams a
@@ -37,16 +38,21 @@ constexpr int kDecThreads = 256;
 #endif
 // Split workgroups per call at most (eight per CU); larger calls loop over their items.
 constexpr int64_t kMaxSplitGroups = 256 * 8;
-// Calls over at most kInlineSlices slices whose items (at the smallest item size) fit one pass
-// of the grid skip the plan kernel: every split workgroup scans the lengths into LDS itself,
-// picks the item size from the total length and finds its item there.  Larger calls keep the
-// plan kernel, whose cost is then shared by several items per workgroup.
+// Calls over at most kInlineSlices slices skip the plan kernel: every split workgroup scans
+// the lengths into LDS itself, picks the item size from the total length and finds its items
+// there.  Larger calls keep the plan kernel (its table costs no LDS per slice).
 constexpr int kInlineSlices = 1024;
 constexpr int kInlineTSplitMin = 256, kInlineItems = 256;  // one item per CU
 
-static bool dec_inline(int64_t num_slices, int32_t max_len) {
-  return num_slices <= kInlineSlices &&
-         num_slices * (int64_t)((max_len + kInlineTSplitMin - 1) / kInlineTSplitMin) <= kMaxSplitGroups;
+static bool dec_inline(int64_t num_slices, int32_t) { return num_slices <= kInlineSlices; }
+
+// Upper bound on the items of an in-kernel plan.  The item size ts is at least 256 tokens,
+// and at least T / 256 unless it is capped at kTSplitMax, so the item count
+// sum ceil(s_z / ts) < T / ts + S is below S + 256, or S + T / kTSplitMax when capped.
+static int64_t dec_inline_items(int64_t num_slices, int32_t max_len) {
+  const int64_t by_min = num_slices * (int64_t)((max_len + kInlineTSplitMin - 1) / kInlineTSplitMin);
+  const int64_t capped = (num_slices * (int64_t)max_len + kTSplitMax - 1) / kTSplitMax;
+  return std::min(by_min, num_slices + std::max<int64_t>(kInlineItems, capped));
 }
 
 // Item size of an in-kernel plan from the total length T of the call: about one item per CU
@@ -57,10 +63,13 @@ __device__ __forceinline__ int inline_split_tokens(int T) {
   return min(max(ts, kInlineTSplitMin), kTSplitMax);
 }
 
-// First token of item p when a slice of s tokens is cut into cnt items of as equal a length
-// as tokens allow (cnt = ceil(s / item size), so no item is longer than the item size).
+// First token of item p when a slice of s tokens is cut into cnt items whose lengths differ
+// by at most one token (the first s % cnt items take the extra token; cnt = ceil(s / item
+// size), so no item is longer than the item size).  32-bit arithmetic only: p * (s / cnt)
+// is at most s.
 __device__ __forceinline__ int item_bound(int p, int s, int cnt) {
-  return (int)((int64_t)p * s / cnt);
+  const int q = s / cnt, rem = s - q * cnt;
+  return p * q + min(p, rem);
 }
 
 __device__ __forceinline__ bool len_ok(const DecArgs &a, int s) {
@@ -423,20 +432,20 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
     __syncthreads();
   };
   if constexpr (INL) {
-    // the grid covers every item once (at most one per workgroup).  The item's slice is the
-    // last z with s_off[z] <= item (slices without items share their offset with the next
-    // one).  The LDS values are the same in every lane; readfirstlane keeps the search and
-    // the item bounds in scalar registers.
-    const int item = blockIdx.x;
-    if (item >= total) return;
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= item) lo = mid; else hi = mid - 1;
+    // workgroups stride over the items (one each when the grid covers them).  The item's
+    // slice is the last z with s_off[z] <= item (slices without items share their offset
+    // with the next one).  The LDS values are the same in every lane; readfirstlane keeps
+    // the search and the item bounds in scalar registers.
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+      int lo = 0, hi = S - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= item) lo = mid; else hi = mid - 1;
+      }
+      const int p = item - __builtin_amdgcn_readfirstlane(s_off[lo]);
+      const int len = __builtin_amdgcn_readfirstlane(s_len[lo]), cnt = (len + ts - 1) / ts;
+      process(item, lo, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
     }
-    const int p = item - __builtin_amdgcn_readfirstlane(s_off[lo]);
-    const int len = __builtin_amdgcn_readfirstlane(s_len[lo]), cnt = (len + ts - 1) / ts;
-    process(item, lo, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
   } else {
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
       const int4 it4 = *reinterpret_cast<const int4 *>(a.item_zp + 4 * (int64_t)item);
@@ -576,8 +585,8 @@ int32_t dec_split_tokens(int64_t num_slices, int32_t max_len) {
 }
 
 int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
-  const int32_t ts = dec_inline(num_slices, max_len) ? kInlineTSplitMin
-                                                     : dec_split_tokens(num_slices, max_len);
+  if (dec_inline(num_slices, max_len)) return dec_inline_items(num_slices, max_len);
+  const int32_t ts = dec_split_tokens(num_slices, max_len);
   return num_slices * (int64_t)((max_len + ts - 1) / ts);
 }
 

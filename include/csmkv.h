@@ -62,8 +62,11 @@ typedef struct {
   int64_t cap;        /* rows allocated per slice, >= 1 */
   int32_t d;          /* head dimension: 64 or 128 (other values: CSMKV_EUNSUPPORTED) */
   int32_t dtype;      /* csmkv_dtype of K, V (and q) */
-  int32_t max_len;    /* host-known bound on every lens[] entry, 0 <= max_len <= cap;
-                         sizes the launch grids (entries above it are device errors) */
+  int32_t max_len;    /* host-known bound on the lens[] entries a call reads, 0 <= max_len
+                         <= cap; sizes the launch grids (entries above it are device
+                         errors).  In-place rounds exempt outlier slices and
+                         csm_compress_triggered slices below their threshold: those are not
+                         read, so a bound on the other slices suffices */
 } csmkv_cache;
 
 /* Human-readable name of a status code (static string). */

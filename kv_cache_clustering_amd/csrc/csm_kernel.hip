@@ -60,8 +60,9 @@ __global__ void csm_prep(CsmArgs a) {
       const int s = a.lens_in[z];
       const bool outl = a.mask != nullptr && a.mask[z] != 0;
       bool ok = s >= 0 && (int64_t)s <= a.cap_in;
-      // Algorithm 1 trigger (when thresholds are given): cluster when s >= B + g
-      const bool run = a.thr == nullptr || (ok && !outl && s >= a.thr[z]);
+      // Algorithm 1 trigger (when thresholds are given): cluster when s >= B + g.  An outlier
+      // slice in place is neither read nor written, so it needs no cover by the launch.
+      const bool run = !(outl && a.in_place) && (a.thr == nullptr || (ok && !outl && s >= a.thr[z]));
       if (run && s > a.max_len) ok = false;  // the launch covers max_len rows
       double r = a.r;
       if (a.thr != nullptr && run && ok) {  // r annealed over this slice's rounds

@@ -56,8 +56,9 @@ class ClusteredKVCache:
         return max(self.sched.s, self.outlier_len if self.has_outliers else 0)
 
     def _round(self, r, s_before):
-        """One clustering round; s_before (host-known length before it) bounds the launch."""
-        max_len = max(s_before, self.outlier_len if self.has_outliers else 0)
+        """One clustering round in place; s_before (host-known length of the compressed slices
+        before it) bounds the launch: outlier slices are not read, so they need no cover."""
+        max_len = s_before
         if self.observer is None:
             lib.csm_compress(self.K, self.V, self.N, self.lens, self.n1, self.n2, self.c, r,
                              self.mask, max_len=max_len, workspace=self.ws_csm)
@@ -175,7 +176,7 @@ class ClusteredKVCache:
         O = lib.decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
                                  out=self.out if out is None else out, max_len=bound,
                                  workspace=self.ws_dec)
-        self._triggered_round(bound)
+        self._triggered_round(self.sched.s)  # slices that can run share this length
         r = self.sched.next_round(self.step_index) if self.sched.over_budget() else None
         return O, r
 

@@ -231,6 +231,34 @@ def test_bad_length_sets_error_and_leaves_slice(lib, dev):
     assert lib.read_error(ws) == lib.OK
 
 
+def test_in_place_outlier_slices_need_no_length_cover(lib, dev):
+    """In place, an outlier slice is neither read nor written, so the length bound (which sizes
+    the launch) need only cover the slices that are compressed: an outlier longer than the
+    bound is no error, stays untouched, and the other slices come out as under a bound that
+    covers every slice.  Out of place the outlier is copied, so there it must be covered."""
+    lens = [3000, 5000, 3000, 2990]
+    K, V, N, L = host_cache(4, 5100, lens, seed=5, degrees=True)
+    mask = torch.tensor([0, 1, 0, 0], dtype=torch.uint8, device=dev)
+    outs = []
+    for bound in (3000, 5000):
+        Kd, Vd, Nd, Ld = K.to(dev), V.to(dev), N.to(dev), L.to(dev)
+        ws = lib.csm_compress(Kd, Vd, Nd, Ld, 16, 64, 256, 0.5, mask, max_len=bound)
+        assert lib.read_error(ws) == lib.OK, bound
+        outs.append((Kd.cpu(), Vd.cpu(), Nd.cpu(), Ld.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    Kg, Vg, Ng, Lg = outs[0]
+    assert int(Lg[1]) == 5000 and torch.equal(Kg[1], K[1]) and torch.equal(Vg[1], V[1])
+    assert torch.equal(Ng[1], N[1])
+    assert int(Lg[0]) < 3000 and int(Lg[3]) < 2990
+    Ki, Vi, Ni, Li = K.to(dev), V.to(dev), N.to(dev), L.to(dev)
+    Ko, Vo = torch.zeros_like(Ki), torch.zeros_like(Vi)
+    No, Lo = torch.zeros_like(Ni), torch.zeros_like(Li)
+    ws = lib.csm_compress_into(Ki, Vi, Ni, Li, Ko, Vo, No, Lo, 16, 64, 256, 0.5, mask, max_len=3000)
+    assert lib.read_error(ws) == lib.EDEVICE
+    assert int(Lo[1]) == 0 and torch.all(Ko[1] == 0)      # the uncovered outlier is not copied
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("c,r,n1,n2", [(256, 0.5, 16, 64), (64, 0.77, 3, 5), (37, 1.0, 16, 64)])
 def test_small_caches_head_dim_64(lib, dev, dtype, c, r, n1, n2):

@@ -78,9 +78,9 @@ def _split_tokens(S, max_len):
 
 
 def _plans_inline(S, max_len):
-    """Calls over at most 1024 slices with at most 2048 items of 256 tokens over the length
-    bound find their items inside the split kernel."""
-    return S <= 1024 and S * -(-max_len // 256) <= 2048
+    """Calls over at most 1024 slices find their items inside the split kernel; larger calls
+    read them from the plan kernel's table."""
+    return S <= 1024
 
 
 def _inline_split_tokens(lens, max_len):
@@ -117,14 +117,15 @@ def _check_item_sizes(lib, dev, S, cap, lens, ts, seed, check):
     assert worst < 2e-4
 
 
-@pytest.mark.parametrize("ts,S,cap", [(512, 400, 1544), (1024, 400, 3080), (2048, 400, 6200)])
+@pytest.mark.parametrize("ts,S,cap", [(512, 1040, 1000), (1024, 1040, 2000), (2048, 1040, 6200)])
 def test_work_item_sizes_ragged(lib, dev, ts, S, cap):
     """Each work-item size of the plan kernel, with lengths on both sides of its multiples
     (where a slice's item count, and so the cut of its tokens into items, changes); the cache
     is built on the device and one slice of every distinct length is checked against the
     oracle."""
     assert not _plans_inline(S, cap) and _split_tokens(S, cap) == ts
-    choices = [0, 1, ts - 1, ts, ts + 1, 2 * ts, 2 * ts + 1, 3 * ts - 1, 3 * ts, cap]
+    choices = [x for x in [0, 1, ts - 1, ts, ts + 1, 2 * ts, 2 * ts + 1, 3 * ts - 1, 3 * ts]
+               if x < cap] + [cap]
     rng = np.random.default_rng(ts)
     lens = rng.choice(choices, size=S)
     lens[:len(choices)] = choices
@@ -264,42 +265,88 @@ def test_bad_length_gives_zeros_and_error(lib, dev):
 
 
 def test_item_plan_kernel_and_inline_plan_agree(lib, dev):
-    """The same call planned both ways: under a tight length bound the split kernel finds its
-    items from the lengths (item size from the total length: 512 here), under a loose one the
-    plan kernel lays them out (512 again).  Same items, so bit-identical outputs; a bad length
-    is reported by both and gives zeros; every slice against the oracle."""
-    S, cap, H_q, tight = 20, 40000, 4, 16384
-    lens = [0, 1, 511, 512, 513, 1023, 1024, 1025, tight, cap + 1]   # slice 9: above every bound
-    rest = 129000 - sum(x for x in lens if x <= tight)                 # total length 129000
-    lens += [rest // 10] * 9 + [rest - 9 * (rest // 10)]
-    assert _plans_inline(S, tight) and _inline_split_tokens(lens, tight) == 512
-    assert not _plans_inline(S, cap) and _split_tokens(S, cap) == 512
+    """The same slices planned both ways: one call over 1030 slices reads its items from the
+    plan kernel's table (2048-token items: 1030 slices x 3000 tokens over 2048 items), two calls
+    over 515 slices each find them in the split kernel (2048-token items again: each call's
+    total length over 256 items is above the cap).  Same items, so bit-identical outputs; a bad
+    length is reported by both and gives zeros; sampled slices against the oracle."""
+    S, cap, H_q = 1030, 3000, 4
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1000, cap + 1, size=S)
+    lens[:9] = [0, 1, 2047, 2048, 2049, 1024, 4095 - 1096, cap, cap]
+    lens[600] = cap + 1                                     # above the bound: a device error
+    half = S // 2
+    assert not _plans_inline(S, cap) and _split_tokens(S, cap) == 2048
+    for part in (lens[:half], lens[half:]):
+        assert _plans_inline(half, cap) and _inline_split_tokens(part, cap) == 2048
     gen = torch.Generator(device=dev).manual_seed(31)
     K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
     V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
     N = torch.randint(1, 40, (S, cap), generator=gen, device=dev, dtype=torch.int32)
-    L = torch.tensor(lens, dtype=torch.int32, device=dev)
+    L = torch.from_numpy(lens.astype(np.int32)).to(dev)
     q = torch.randn((S, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
-    outs = []
-    for ml in (tight, cap):
-        ws = torch.full((lib.decode_workspace_bytes(K, H_q, 1, max_len=ml),), 0x5A,
-                        dtype=torch.uint8, device=dev)
-        outs.append(lib.decode_attn_logn(q, K, V, N, L, H_q, 1, max_len=ml, workspace=ws))
-        assert lib.read_error(ws) == lib.EDEVICE, ml
-    assert torch.equal(outs[0], outs[1])
-    assert torch.all(outs[0][9] == 0)
+    ws = torch.full((lib.decode_workspace_bytes(K, H_q, 1, max_len=cap),), 0x5A,
+                    dtype=torch.uint8, device=dev)
+    O_plan = lib.decode_attn_logn(q, K, V, N, L, H_q, 1, max_len=cap, workspace=ws)
+    assert lib.read_error(ws) == lib.EDEVICE
+    O_inl = torch.empty_like(O_plan)
+    errs = []
+    for lo, hi in ((0, half), (half, S)):
+        wsh = torch.full((lib.decode_workspace_bytes(K[lo:hi], H_q, 1, max_len=cap),), 0x5A,
+                         dtype=torch.uint8, device=dev)
+        lib.decode_attn_logn(q[lo:hi], K[lo:hi], V[lo:hi], N[lo:hi], L[lo:hi], H_q, 1,
+                             out=O_inl[lo:hi], max_len=cap, workspace=wsh)
+        errs.append(lib.read_error(wsh))
+    assert errs == [lib.OK, lib.EDEVICE]
+    assert torch.equal(O_plan, O_inl)
+    assert torch.all(O_plan[600] == 0)
     worst = 0.0
-    for z in range(S):
-        s = lens[z]
+    for z in list(range(9)) + [600, 601, S - 1]:
+        s = int(lens[z])
         for h in range(H_q):
-            got = outs[0][z, h].cpu().double().numpy()
-            if s == 0 or s > tight:
+            got = O_plan[z, h].cpu().double().numpy()
+            if s == 0 or s > cap:
                 assert np.all(got == 0)
                 continue
             ref = oatt.logn_attention_one(parity.to_f64(q[z, h].cpu()), parity.to_f64(K[z, :s].cpu()),
                                           parity.to_f64(V[z, :s].cpu()),
                                           N[z, :s].cpu().numpy().astype(np.int64))
             worst = max(worst, float(np.abs(got - ref).max()))
+    assert worst < 2e-4
+
+
+def test_inline_plan_with_more_items_than_workgroups(lib, dev):
+    """A call over 1024 slices of 4097..6200 tokens plans in the split kernel with 2048-token
+    items: three or four per slice, more than the 2048 workgroups of the grid, so workgroups
+    stride over several items.  Sampled slices, every head, against the oracle."""
+    S, cap, H_q, H_kv = 1024, 6200, 8, 2
+    rng = np.random.default_rng(43)
+    lens = rng.integers(4097, cap + 1, size=S)
+    lens[:4] = [4097, 6143, 6144, cap]
+    assert _plans_inline(S, cap) and _inline_split_tokens(lens, cap) == 2048
+    assert sum(-(-int(s) // 2048) for s in lens) > 2048
+    gen = torch.Generator(device=dev).manual_seed(43)
+    K = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    V = torch.randn((S, cap, 128), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.randint(1, 100, (S, cap), generator=gen, device=dev, dtype=torch.int32)
+    L = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    q = torch.randn((S // H_kv, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
+    ws = torch.full((lib.decode_workspace_bytes(K, H_q, H_kv, max_len=cap),), 0x33,
+                    dtype=torch.uint8, device=dev)
+    O = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, max_len=cap, workspace=ws)
+    assert lib.read_error(ws) == lib.OK
+    O = O.cpu().double().numpy()
+    G = H_q // H_kv
+    worst = 0.0
+    for z in [0, 1, 2, 3] + [int(x) for x in rng.integers(4, S, size=12)] + [S - 1]:
+        g, kvh = divmod(z, H_kv)
+        s = int(lens[z])
+        Kz, Vz = parity.to_f64(K[z, :s].cpu()), parity.to_f64(V[z, :s].cpu())
+        Nz = N[z, :s].cpu().numpy().astype(np.int64)
+        for h in range(G):
+            ref = oatt.logn_attention_one(parity.to_f64(q[g, kvh * G + h].cpu()), Kz, Vz, Nz)
+            worst = max(worst, float(np.abs(O[g, kvh * G + h] - ref).max()))
+    print("max abs", worst)
     assert worst < 2e-4
 
 
@@ -361,10 +408,10 @@ def test_seeded_sweep_decode(lib, dev):
 
 def test_seeded_sweep_decode_plan_kernel(lib, dev):
     """Every storage format, head dim and head group (1, 2, 4, 8) on calls large enough to be
-    planned by the plan kernel (40 slices of up to 14000 tokens): ragged lengths including 0 and
-    the bound, degrees 1..1000; sampled slices, every head, against the oracle."""
+    planned by the plan kernel (1040 slices of up to 6000 tokens): ragged lengths including 0
+    and the bound, degrees 1..1000; sampled slices, every head, against the oracle."""
     rng = np.random.default_rng(91)
-    S, H_kv, cap = 40, 2, 14000
+    S, H_kv, cap = 1040, 2, 6000
     assert not _plans_inline(S, cap)
     worst = {}
     for dtype in (torch.bfloat16, torch.float16, torch.float32):

@@ -80,7 +80,7 @@ __global__ void csm_prep(CsmArgs a) {
       if (ok && (int64_t)s_new > a.cap_out) ok = false;
       a.s_in[z] = ok ? s : -1;
       a.s_out[z] = s_new;
-      a.s_r[z] = run ? r : -1.0;
+      a.s_r[z] = run && ok ? r : -1.0;  // the round's workgroups exit on this one load
       a.ticket[z] = 0u;
       if (!ok) atomicExch(a.err, kDeviceError);
     }
@@ -172,10 +172,12 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
 
   const int t = threadIdx.x;
   const int64_t z = blockIdx.x / (uint32_t)a.units;
-  const int s = a.s_in[z];
-  if (s < 0) return;  // invalid length: slice left untouched (error word already set)
+  // r < 0: the slice does not run this call (trigger not met, outlier in place, or a bad length
+  // with the error word already set) and is left as it is; one load decides it
   const double r = a.s_r[z];
-  if (r < 0.0) return;  // trigger not met: slice left as it is
+  if (r < 0.0) return;
+  const int s = a.s_in[z];
+  if (s < 0) return;
   const bool outl = a.mask != nullptr && a.mask[z] != 0;
   if (outl && a.in_place) return;
   if (t == 0) s_misc[0] = (int32_t)atomicAdd(a.ticket + z, 1u);

@@ -33,6 +33,7 @@ constexpr int64_t kItemTarget = 2048;               // work items a call aims fo
 template <int D>
 constexpr int part_width() { return 4 + D; }
 constexpr int kDecThreads = 256;
+constexpr int kCombThreads = 1024;  // dec_combine workgroup
 #ifndef DEC_NS
 #define DEC_NS 3
 #endif
@@ -455,15 +456,16 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
 }
 
 // One workgroup per slice, every head at once, in one pass over the partials: each thread
-// takes 4 output elements of one head and one of 8/G item groups and sums the partials against
-// a running maximum (rescaling its sums when the maximum grows), four independent items per
-// step; the item groups are then merged through LDS against their common maximum and divided.
+// takes 4 output elements of one head and one of kCombThreads / (D / 4 * G) item groups and sums
+// the partials against a running maximum (rescaling its sums when the maximum grows), four
+// independent items per step, so a slice of up to 4 items per group needs one round trip to
+// memory; the item groups are then merged through LDS against their common maximum and divided.
 template <int G, int D>
-__global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
+__global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
   constexpr int PW = part_width<D>();
-  constexpr int CPH = D / 4;      // 4-element columns per head
-  constexpr int COLS = CPH * G;   // columns over the G heads
-  constexpr int IG = 256 / COLS;  // item groups
+  constexpr int CPH = D / 4;               // 4-element columns per head
+  constexpr int COLS = CPH * G;            // columns over the G heads
+  constexpr int IG = kCombThreads / COLS;  // item groups
   __shared__ __attribute__((aligned(16))) float s_acc[IG][G][D];
   __shared__ float s_l[IG][G], s_m[IG][G];
   const int64_t z = blockIdx.x;
@@ -522,7 +524,7 @@ __global__ void __launch_bounds__(256) dec_combine(DecArgs a) {
     s_m[grp][h] = M;
   }
   __syncthreads();
-  for (int i = t; i < G * D; i += 256) {
+  for (int i = t; i < G * D; i += kCombThreads) {
     const int hh = i / D, d = i % D;
     float Mx = NEG_INF;
 #pragma unroll
@@ -559,12 +561,12 @@ static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
 
 template <int D>
 static int launch_combine(const DecArgs &a, int G, hipStream_t st) {
-  const dim3 cg((uint32_t)a.num_slices);
+  const dim3 cg((uint32_t)a.num_slices), ct(kCombThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((dec_combine<1, D>), cg, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((dec_combine<2, D>), cg, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((dec_combine<4, D>), cg, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_combine<8, D>), cg, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((dec_combine<1, D>), cg, ct, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((dec_combine<2, D>), cg, ct, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((dec_combine<4, D>), cg, ct, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_combine<8, D>), cg, ct, 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

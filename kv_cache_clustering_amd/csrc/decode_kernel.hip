@@ -292,26 +292,36 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
   }
 }
 
-// Threads of a dec_split workgroup: G = 8 splits the heads over two sets of four waves that
-// stream the same tokens (heads 0-3 and 4-7), so that every wave holds the registers of four
-// heads (eight spill); the second read of a row is served by the cache.
+// G = 8 splits the heads into two sets (0-3 and 4-7), each served by its own workgroup, so that
+// every wave holds the registers of four heads (eight spill) and a CU still holds two
+// workgroups.  Work unit v = 16k + j takes item 8k + (j mod 8) for head set j / 8: the two
+// halves of an item run in workgroups whose indices differ by 8, which the dispatcher places
+// on the same XCD (workgroups go round-robin over the 8 XCDs), so the second read of a row is
+// served by that XCD's L2.
 template <int G>
 constexpr int dec_head_sets() { return G >= 8 ? 2 : 1; }
-template <int G>
-constexpr int dec_threads() { return kDecThreads * dec_head_sets<G>(); }
+// Work units of a call with `items` items, the item of unit v and its head set.
+template <int HS>
+__host__ __device__ constexpr int64_t dec_units(int64_t items) {
+  return HS == 1 ? items : (items + 7) / 8 * 16;
+}
+template <int HS>
+__device__ __forceinline__ int dec_unit_item(int v) { return HS == 1 ? v : (v >> 4) * 8 + (v & 7); }
+template <int HS>
+__device__ __forceinline__ int dec_unit_set(int v) { return HS == 1 ? 0 : (v >> 3) & 1; }
 
 // INL: the items are found from the lengths in the kernel (calls over at most kInlineSlices
 // slices), else read from the plan kernel's table.
 template <typename T, int G, int D, bool INL>
-__global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_split(DecArgs a) {
-  constexpr int HS = dec_head_sets<G>(), GW = G / HS, NT = dec_threads<G>();
+__global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
+  constexpr int HS = dec_head_sets<G>(), GW = G / HS, NT = kDecThreads;
   using DT = DecTile<T, GW, D>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
   constexpr int PW = part_width<D>();  // (max, sum, pad, pad, o[d]) per head
-  __shared__ float s_part[4][G][PW];
+  __shared__ float s_part[4][GW][PW];
   __shared__ int32_t s_off[kInlineSlices + 1], s_len[kInlineSlices], s_wsum[NT / 64],
       s_wsum2[NT / 64];
-  const int t = threadIdx.x, w = (t >> 6) & 3, hs = t >> 8, l = t & 63;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int sg = l % LPR, rw = l / LPR;
   const int S = (int)a.num_slices;
   const float NEG_INF = -__builtin_inff();
@@ -346,8 +356,8 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
   } else {
     total = a.item_off[S];
   }
-  // one work item: tokens [tok0, tok1) of slice z
-  auto process = [&](int item, int64_t z, int tok0, int tok1) {
+  // one work item: tokens [tok0, tok1) of slice z for the heads of head set hs
+  auto process = [&](int item, int hs, int64_t z, int tok0, int tok1) {
     const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
     const char *Kz = a.K + z * a.cap * ROWB;
     const char *Vz = a.V + z * a.cap * ROWB;
@@ -400,18 +410,18 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
     if (rw == 0) {
 #pragma unroll
       for (int h = 0; h < GW; ++h) {
-        const int hh = hs * GW + h;
         if (sg == 0) {
-          s_part[w][hh][0] = mrun[h];
-          s_part[w][hh][1] = lrun[h];
+          s_part[w][h][0] = mrun[h];
+          s_part[w][h][1] = lrun[h];
         }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_part[w][hh][4 + sg * EPL + e] = o[h][e];
+        for (int e = 0; e < EPL; ++e) s_part[w][h][4 + sg * EPL + e] = o[h][e];
       }
     }
     __syncthreads();
-    float *dst = a.part + (int64_t)item * G * PW;
-    for (int i = t; i < G * PW; i += NT) {
+    // this head set's partials: heads hs * GW .. hs * GW + GW - 1 of the item, contiguous
+    float *dst = a.part + ((int64_t)item * G + hs * GW) * PW;
+    for (int i = t; i < GW * PW; i += NT) {
       const int h = i / PW, k = i % PW;
       float M = NEG_INF;
 #pragma unroll
@@ -437,7 +447,9 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
     // slice is the last z with s_off[z] <= item (slices without items share their offset
     // with the next one).  The LDS values are the same in every lane; readfirstlane keeps
     // the search and the item bounds in scalar registers.
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    for (int v = blockIdx.x; v < dec_units<HS>(total); v += gridDim.x) {
+      const int item = dec_unit_item<HS>(v), hs = dec_unit_set<HS>(v);
+      if (item >= total) continue;
       int lo = 0, hi = S - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -445,12 +457,14 @@ __global__ void __launch_bounds__(dec_threads<G>(), 2 / dec_head_sets<G>()) dec_
       }
       const int p = item - __builtin_amdgcn_readfirstlane(s_off[lo]);
       const int len = __builtin_amdgcn_readfirstlane(s_len[lo]), cnt = (len + ts - 1) / ts;
-      process(item, lo, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
+      process(item, hs, lo, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
     }
   } else {
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    for (int v = blockIdx.x; v < dec_units<HS>(total); v += gridDim.x) {
+      const int item = dec_unit_item<HS>(v), hs = dec_unit_set<HS>(v);
+      if (item >= total) continue;
       const int4 it4 = *reinterpret_cast<const int4 *>(a.item_zp + 4 * (int64_t)item);
-      process(item, it4.x, it4.y, it4.z);
+      process(item, hs, it4.x, it4.y, it4.z);
     }
   }
 }
@@ -547,7 +561,7 @@ static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
     case 1: hipLaunchKernelGGL((dec_split<T, 1, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
     case 2: hipLaunchKernelGGL((dec_split<T, 2, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
     case 4: hipLaunchKernelGGL((dec_split<T, 4, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_split<T, 8, D, INL>), dim3(grid), dim3(dec_threads<8>()), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_split<T, 8, D, INL>), dim3(grid), dim3(kDecThreads), 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
@@ -600,7 +614,10 @@ int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_item
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_items, kMaxSplitGroups));
+  // G = 8: twice the units, in groups of 16 (kMaxSplitGroups is a multiple of 16, so a
+  // workgroup's units keep their partner 8 indices away in every pass)
+  const int64_t units = G >= 8 ? dec_units<2>(max_items) : max_items;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
   if (rc) return rc;
   return d == 64 ? launch_combine<64>(a, G, st) : launch_combine<128>(a, G, st);

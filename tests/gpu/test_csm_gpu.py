@@ -111,7 +111,11 @@ def test_single_head_2k_fp32_workload(lib, dev):
     assert rep.slices == 1
 
 
-def _device_workload(lib, dev, cid, sample, n_outlier_checks=2):
+def _device_workload(lib, dev, cid, sample, n_outlier_checks=2, out_of_place=False):
+    """One round over a whole synthetic workload on the device (the debug launch, in place),
+    sampled slices against the oracle.  out_of_place: first run the round as the benchmark
+    times it (csm_compress_into from the pristine cache into a second one, every slice) and
+    require that output to equal the in-place result bit for bit, slice by slice."""
     w = kvsynth.workload(cid)
     c = kvsynth.make_cache(w, dev, with_appends=False)
     K, V, N, lens, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]
@@ -122,9 +126,21 @@ def _device_workload(lib, dev, cid, sample, n_outlier_checks=2):
     Vin = {z: V[z].cpu() for z in zs}
     Nin = {z: N[z].cpu() for z in zs}
     lin = lens.cpu().numpy().copy()
+    if out_of_place:
+        Ko, Vo, No, Lo = (torch.empty_like(t) for t in (K, V, N, lens))
+        ws = lib.csm_compress_into(K, V, N, lens, Ko, Vo, No, Lo, w.n1, w.n2, w.c, w.r_init,
+                                   mask if maskh.any() else None, max_len=w.ctx)
+        assert lib.read_error(ws) == lib.OK
     best, sel, src, ws = lib.csm_compress_debug(K, V, N, lens, w.n1, w.n2, w.c, w.r_init,
                                                 mask if maskh.any() else None, max_len=w.ctx)
     assert lib.read_error(ws) == lib.OK
+    if out_of_place:
+        assert torch.equal(Lo, lens)
+        for z in range(K.shape[0]):
+            s = int(lin[z]) if maskh[z] else int(lens[z])
+            assert torch.equal(Ko[z, :s], K[z, :s]) and torch.equal(Vo[z, :s], V[z, :s]), z
+            assert torch.equal(No[z, :s], N[z, :s]), z
+        del Ko, Vo, No
     rep = parity.Report()
     for z in zs:
         if maskh[z]:
@@ -154,7 +170,7 @@ def test_llama3_16k_workload_sampled(lib, dev):
 
 
 def test_llama3_64k_outlier_workload_sampled(lib, dev):
-    rep = _device_workload(lib, dev, 4, sample=[0, 13, 99, 180, 255])
+    rep = _device_workload(lib, dev, 4, sample=[0, 13, 99, 180, 255], out_of_place=True)
     print(rep)
     parity.check_report(rep)
 

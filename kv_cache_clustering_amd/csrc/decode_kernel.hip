@@ -9,17 +9,19 @@
 //                 the length bound so that a call has about 2048 items.  Smaller calls plan
 //                 in the split kernel itself, from the total length: about one item per CU
 //                 for a layer's few slices, items of up to 2048 tokens for many slices.
-//   dec_split   : persistent workgroups stride over the work items.  A work item is
-//                 tsplit tokens of one slice, shared by the G query heads of that KV
-//                 head, so K, V and N are read once per step.  Each wave streams a
+//   dec_split   : workgroups stride over the work items (at most 2048 workgroups).  A work
+//                 item is up to tsplit tokens of one slice, shared by the G query heads of
+//                 that KV head (G = 8: two workgroups of four heads each), so K, V and N are
+//                 read from HBM once per step.  Each wave streams a
 //                 quarter of the item: 16 B per lane per row, sub-blocks of 16 tokens
 //                 (bf16) with the next sub-block's loads in flight while the current
 //                 one is computed, q.k by packed bf16 dot products, a 16-lane DPP reduction,
 //                 base-2 online softmax (log2 N added, log2 e folded into the scale),
 //                 P.V accumulated in fp32.  Waves merge in LDS; each item writes one
 //                 (max, sum, 0, 0, o[128]) partial per head.
-//   dec_combine : one workgroup per slice merges the item partials by log-sum-exp
-//                 (max first, then rescaled sums over item groups in parallel).
+//   dec_combine : one 1024-thread workgroup per slice merges the item partials by
+//                 log-sum-exp (a running maximum per thread over item groups in parallel,
+//                 then the groups merged against their common maximum).
 #include <algorithm>
 
 #include "device_common.hpp"

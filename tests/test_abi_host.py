@@ -5,6 +5,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -143,3 +144,43 @@ def test_decode_and_append_validation(lib):
     assert app(FAKE, FAKE, FAKE, None, ctypes.byref(d), FAKE, FAKE, None, None) == lib.EINVAL
     assert app(FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc(lib, dtype=3)), FAKE, FAKE, None, None) == lib.EDTYPE
     assert lib.raw.csmkv_read_error(None, None) == lib.EINVAL
+
+
+def _items_for_lengths(S, max_len, lens):
+    """Work items a decode call lays out for these lengths, by the rule the decode kernel
+    states: calls over at most 1024 slices take an item size of the total length over 256
+    items, rounded up to 16 tokens, within [256, 2048]; larger calls take the smallest of 512,
+    1024 and 2048 tokens that is at least S * max_len / 2048 (else 2048).  A slice of s tokens
+    has ceil(s / item size) items; lengths above the bound count none."""
+    ok = [s for s in lens if 0 <= s <= max_len]
+    if S <= 1024:
+        T = sum(ok)
+        ts = min(max(-(-(-(-T // 256)) // 16) * 16, 256), 2048)
+    else:
+        want, ts = S * max_len // 2048, 512
+        while ts < 2048 and ts < want:
+            ts *= 2
+    return sum(-(-s // ts) for s in ok)
+
+
+def test_decode_workspace_holds_every_item_plan(lib):
+    """The decode workspace must hold one (max, sum, pad, o[d]) fp32 partial per item and head
+    for any lengths within the bound: random geometries (both planning rules), random and
+    extreme length mixes, against the size the library asks for."""
+    rng = np.random.default_rng(5)
+    cases = [(8, 65792), (256, 65792), (1024, 6200), (1025, 6200), (3, 1), (1, 300000),
+             (1000, 2049), (1100, 513)]
+    cases += [(int(rng.integers(1, 1500)), int(rng.integers(1, 70000))) for _ in range(40)]
+    for S, max_len in cases:
+        for d, G in ((128, 4), (64, 8), (128, 1)):
+            H_kv = 1
+            desc = lib.CacheDesc(S, max_len, d, 0, max_len)
+            ws = lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(desc), G * H_kv, H_kv)
+            assert ws > 0
+            part = G * (4 + d) * 4
+            mixes = [[max_len] * S, [1] * S, [0] * (S - 1) + [max_len],
+                     list(rng.integers(0, max_len + 1, size=S)),
+                     list(rng.choice([1, max_len, max_len // 2 + 1, 2049, 257], size=S))]
+            for lens in mixes:
+                items = _items_for_lengths(S, max_len, [int(x) for x in lens])
+                assert items * part + (S + 1) * 4 <= ws, (S, max_len, d, G, items, ws)

@@ -294,14 +294,144 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
   }
 }
 
+// bf16 caches run q.k and P.V on MFMA (16 x 16 tiles, heads padded to 16).  A wave takes
+// 16-token sub-blocks; lane l covers token row l mod 16 and lane group g = l / 16:
+//   K and V rows are loaded as whole rows (non-temporal, the VALU path's pattern) and staged in
+//   per-wave LDS tiles (rows padded by 8 bytes so both read patterns below hit distinct banks);
+//   q.k : v_mfma_f32_16x16x32_bf16 with A = K rows from the tile (lane: row l mod 16, 16 bytes at
+//         64 kk + 16 g) and B = q (lane: head l mod 16, the same bytes), D / 32 steps; lane l
+//         receives the scores of tokens 4g .. 4g + 3 for head l mod 16;
+//   P.V : v_mfma_f32_16x16x16_bf16 with A = P (head l mod 16, tokens 4g .. 4g + 3: the lane's own
+//         scores, so P needs no exchange) and B = V (tokens 4g .. 4g + 3, column l mod 16 of a
+//         16-column block), read across the V tile's rows.  P enters as two bf16 terms, p = hi + lo
+//         (hi = RNE(p), lo = RNE(p - hi)), which keeps it to about 2^-17 relative; the sum of P
+//         is taken in fp32 from p itself.  Lane l holds O rows (heads) 4g .. 4g + 3, column
+//         l mod 16 of each block.
+#ifndef DEC_MFMA
+#define DEC_MFMA 1
+#endif
+template <typename T>
+constexpr bool dec_mfma() { return DEC_MFMA && __is_same(T, __bf16); }
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MfStage {
+  static constexpr int NR = D / 32;  // wave loads per 16-row sub-block (512 / D rows each)
+  u32x4 k[NR], v[NR];
+  int32_t n[4];
+};
+template <int D>
+constexpr int mf_stride() { return 2 * D + 8; }  // LDS bytes per staged row (bank spread)
+
+// Sub-block rows rel .. rel + 15 of the wave's range (relative to its first row).  K and V are
+// read as whole rows, 16 bytes per lane, 512 / D rows per wave load, non-temporal (each row is
+// read once); lane_kv = (l / (D / 8)) * row bytes + 16 (l mod (D / 8)) is the lane's fixed part
+// of the address, and the sub-block's, wave-uniform, goes in the scalar offset, so no address
+// register is rewritten in the loop (one that shared registers with an in-flight load made the
+// loop wait for every load).  The degrees of the tokens 4g .. 4g + 3 the lane scores come as
+// lane_n = 16 g plus 4 i.
+template <int D>
+__device__ __forceinline__ void mf_load(MfStage<D> &st, const DecRows &rs, int rel, int lane_kv,
+                                        int lane_n) {
+  constexpr int ROWB = 2 * D, NR = D / 32, RPW = 512 / D;
+  const int soff = __builtin_amdgcn_readfirstlane(rel * ROWB);
+  const int soff_n = __builtin_amdgcn_readfirstlane(rel * 4);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    st.k[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, lane_kv + i * RPW * ROWB, soff, 2));
+    st.v[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, lane_kv + i * RPW * ROWB, soff, 2));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    st.n[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rs.n, lane_n + 4 * i, soff_n, 0);
+}
+
+// Online-softmax update with one sub-block, base 2.  mrun / lrun: head l mod 16 (lrun over the
+// lane's tokens only); o[eb]: heads 4g .. 4g + 3 of column block eb.  kt, vt: this wave's LDS
+// tiles (16 rows each).
+template <int D>
+__device__ __forceinline__ void mf_compute(const MfStage<D> &st, const bf16x8 *qop,
+                                           float scale_log2, float &mrun, float &lrun,
+                                           f32x4 *o, char *kt, char *vt, int l) {
+  constexpr int NR = D / 32, KK = D / 32, EB = D / 16, ST = mf_stride<D>(), LPR = D / 8;
+  const int g = l >> 4, c = l & 15;
+  // the sub-block's rows into LDS as loaded (row l / LPR + 512 / D * i, segment l mod LPR),
+  // 8 bytes at a time (the padded rows are 8-byte aligned)
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int off = (l / LPR + (512 / D) * i) * ST + 16 * (l % LPR);
+    uint2 *dk = reinterpret_cast<uint2 *>(kt + off);
+    uint2 *dv = reinterpret_cast<uint2 *>(vt + off);
+    dk[0] = make_uint2(st.k[i][0], st.k[i][1]);
+    dk[1] = make_uint2(st.k[i][2], st.k[i][3]);
+    dv[0] = make_uint2(st.v[i][0], st.v[i][1]);
+    dv[1] = make_uint2(st.v[i][2], st.v[i][3]);
+  }
+  // The staged rows are read by other lanes of the wave.  These writes, the reads below and the
+  // next sub-block's writes go through the same pointers and may alias, so they keep their
+  // program order, and a wave's LDS accesses execute in that order: no barrier is needed.
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const uint2 *src = reinterpret_cast<const uint2 *>(kt + c * ST + 64 * kk + 16 * g);
+    const uint2 lo = src[0], hi = src[1];
+    const u32x4 kw = {lo.x, lo.y, hi.x, hi.y};
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qop[kk], sc, 0,
+                                                 0, 0);
+  }
+  // scores: a row past the range has N = 0 (range-checked load), so log2 N = -inf drops it
+  float z[4], mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = fmaf(sc[i], scale_log2, __builtin_amdgcn_logf((float)st.n[i]));
+    mx = fmaxf(mx, z[i]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mn = fmaxf(mrun, mx);
+  const float alpha = fast_exp2(mrun - mn);
+  mrun = mn;
+  float p[4], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = fast_exp2(z[i] - mn);
+    ps += p[i];
+  }
+  lrun = fmaf(lrun, alpha, ps);
+  // rescale factors of the heads this lane's O rows hold (lane h holds head h's factor)
+  float al[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+  bf16x4 ph, pl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ph[i] = (__bf16)p[i];
+    pl[i] = (__bf16)(p[i] - (float)ph[i]);
+  }
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb) {
+    bf16x4 vop;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      vop[j] = *reinterpret_cast<const __bf16 *>(vt + (4 * g + j) * ST + 2 * (16 * eb + c));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[eb][i] *= al[i];
+    o[eb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vop, o[eb], 0, 0, 0);
+    o[eb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vop, o[eb], 0, 0, 0);
+  }
+}
+
 // G = 8 splits the heads into two sets (0-3 and 4-7), each served by its own workgroup, so that
 // every wave holds the registers of four heads (eight spill) and a CU still holds two
 // workgroups.  Work unit v = 16k + j takes item 8k + (j mod 8) for head set j / 8: the two
 // halves of an item run in workgroups whose indices differ by 8, which the dispatcher places
 // on the same XCD (workgroups go round-robin over the 8 XCDs), so the second read of a row is
 // served by that XCD's L2.
-template <int G>
-constexpr int dec_head_sets() { return G >= 8 ? 2 : 1; }
+template <typename T, int G>
+constexpr int dec_head_sets() { return G >= 8 && !dec_mfma<T>() ? 2 : 1; }
 // Work units of a call with `items` items, the item of unit v and its head set.
 template <int HS>
 __host__ __device__ constexpr int64_t dec_units(int64_t items) {
@@ -316,11 +446,14 @@ __device__ __forceinline__ int dec_unit_set(int v) { return HS == 1 ? 0 : (v >> 
 // slices), else read from the plan kernel's table.
 template <typename T, int G, int D, bool INL>
 __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
-  constexpr int HS = dec_head_sets<G>(), GW = G / HS, NT = kDecThreads;
+  constexpr bool MF = dec_mfma<T>();
+  constexpr int HS = dec_head_sets<T, G>(), GW = G / HS, NT = kDecThreads;
   using DT = DecTile<T, GW, D>;
   constexpr int ROWB = DT::ROWB, LPR = DT::LPR, RPW = DT::RPW, SUB = DT::SUB, EPL = DT::EPL;
   constexpr int PW = part_width<D>();  // (max, sum, pad, pad, o[d]) per head
   __shared__ float s_part[4][GW][PW];
+  __shared__ __attribute__((aligned(16))) char s_kt[4][MF ? 16 * mf_stride<D>() : 16];
+  __shared__ __attribute__((aligned(16))) char s_vt[4][MF ? 16 * mf_stride<D>() : 16];
   __shared__ int32_t s_off[kInlineSlices + 1], s_len[kInlineSlices], s_wsum[NT / 64],
       s_wsum2[NT / 64];
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
@@ -369,6 +502,53 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     const int wb = __builtin_amdgcn_readfirstlane(tok0 + w * wq);
     const int we = __builtin_amdgcn_readfirstlane(min(tok1, wb + wq));
     const DecRows rs = dec_rows(Kz, Vz, Nz, ROWB, wb, we);
+    if constexpr (MF) {
+      constexpr int KK = D / 32, EB = D / 16, NS = DEC_NS;
+      const int gq = l >> 4, c = l & 15;
+      // q of head c as the B operand (zeros for the padding heads c >= G), loaded first
+      bf16x8 qop[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        u32x4 qw = {0u, 0u, 0u, 0u};
+        if (c < G) qw = ld16(a.q + ((g * a.H_q + kvh * G + c) * (int64_t)D) * 2 + 64 * kk + 16 * gq);
+        qop[kk] = __builtin_bit_cast(bf16x8, qw);
+      }
+      // each stage's loads are issued as one group, in stage order, ahead of the compute that
+      // precedes their use (sched_barrier keeps the scheduler from interleaving or sinking them:
+      // loads retire in order, so a reordered stage makes the first sub-block wait for all)
+      const int lane_kv = (l / (D / 8)) * ROWB + 16 * (l % (D / 8)), lane_n = 16 * gq;
+      MfStage<D> st[NS];
+#pragma unroll
+      for (int k = 0; k + 1 < NS; ++k) {
+        mf_load<D>(st[k], rs, k * 16, lane_kv, lane_n);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float mrun = NEG_INF, lrun = 0.f;
+      f32x4 o[EB];
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) o[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sb = wb; sb < we; sb += NS * 16) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          const int cur = sb + k * 16;
+          if (cur >= we) break;
+          mf_load<D>(st[(k + NS - 1) % NS], rs, cur + (NS - 1) * 16 - wb, lane_kv, lane_n);
+          __builtin_amdgcn_sched_barrier(0);
+          mf_compute<D>(st[k], qop, a.scale_log2, mrun, lrun, o, s_kt[w], s_vt[w], l);
+        }
+      }
+      lrun += __shfl_xor(lrun, 16);
+      lrun += __shfl_xor(lrun, 32);
+      if (l < G) {
+        s_part[w][l][0] = mrun;
+        s_part[w][l][1] = lrun;
+      }
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * gq + i < G) s_part[w][4 * gq + i][4 + 16 * eb + c] = o[eb][i];
+    } else {
     // this lane's q segment for each head of the wave's head set, loaded first: loads retire in
     // order, so q issued after the stages would make the first sub-block wait for all of them
     u32x4 qv[GW];
@@ -420,6 +600,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
         for (int e = 0; e < EPL; ++e) s_part[w][h][4 + sg * EPL + e] = o[h][e];
       }
     }
+    }  // VALU path
     __syncthreads();
     // this head set's partials: heads hs * GW .. hs * GW + GW - 1 of the item, contiguous
     float *dst = a.part + ((int64_t)item * G + hs * GW) * PW;
@@ -618,7 +799,8 @@ int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_item
   }
   // G = 8: twice the units, in groups of 16 (kMaxSplitGroups is a multiple of 16, so a
   // workgroup's units keep their partner 8 indices away in every pass)
-  const int64_t units = G >= 8 ? dec_units<2>(max_items) : max_items;
+  const bool sets2 = G >= 8 && !(dtype == kDtypeBf16 && DEC_MFMA);  // dec_head_sets<T, G>() == 2
+  const int64_t units = sets2 ? dec_units<2>(max_items) : max_items;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
   if (rc) return rc;

@@ -294,7 +294,8 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
   }
 }
 
-// bf16 caches run q.k and P.V on MFMA (16 x 16 tiles, heads padded to 16).  A wave takes
+// bf16 and fp16 caches run q.k and P.V on MFMA (16 x 16 tiles, heads padded to 16; fp32 caches
+// keep the VALU path below).  A wave takes
 // 16-token sub-blocks; lane l covers token row l mod 16 and lane group g = l / 16:
 //   K and V rows are loaded as whole rows (non-temporal, the VALU path's pattern) and staged in
 //   per-wave LDS tiles (rows padded by 8 bytes so both read patterns below hit distinct banks);
@@ -303,16 +304,20 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
 //         receives the scores of tokens 4g .. 4g + 3 for head l mod 16;
 //   P.V : v_mfma_f32_16x16x16_bf16 with A = P (head l mod 16, tokens 4g .. 4g + 3: the lane's own
 //         scores, so P needs no exchange) and B = V (tokens 4g .. 4g + 3, column l mod 16 of a
-//         16-column block), read across the V tile's rows.  P enters as two bf16 terms, p = hi + lo
-//         (hi = RNE(p), lo = RNE(p - hi)), which keeps it to about 2^-17 relative; the sum of P
-//         is taken in fp32 from p itself.  Lane l holds O rows (heads) 4g .. 4g + 3, column
-//         l mod 16 of each block.
+//         16-column block), read across the V tile's rows.  P enters as two terms of the storage
+//         type, p = hi + lo (hi = RNE(p), lo = RNE(p - hi); fp16 on p * 2^14), which keeps it to
+//         about 2^-17 (bf16) or 2^-22 (fp16) relative; the sum of P is taken in fp32 from p.
+//         Lane l holds O rows (heads) 4g .. 4g + 3, column l mod 16 of each block.
 #ifndef DEC_MFMA
 #define DEC_MFMA 1
 #endif
 template <typename T>
-constexpr bool dec_mfma() { return DEC_MFMA && __is_same(T, __bf16); }
+constexpr bool dec_mfma() { return DEC_MFMA && (__is_same(T, __bf16) || __is_same(T, _Float16)); }
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+// fp16 P terms carry this factor (an exact power of two, removed from O at the end) so that
+// neither term of p = hi + lo falls into fp16's subnormal range for p >= 2^-17
+constexpr float kF16PScale = 16384.f;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
@@ -352,8 +357,8 @@ __device__ __forceinline__ void mf_load(MfStage<D> &st, const DecRows &rs, int r
 // Online-softmax update with one sub-block, base 2.  mrun / lrun: head l mod 16 (lrun over the
 // lane's tokens only); o[eb]: heads 4g .. 4g + 3 of column block eb.  kt, vt: this wave's LDS
 // tiles (16 rows each).
-template <int D>
-__device__ __forceinline__ void mf_compute(const MfStage<D> &st, const bf16x8 *qop,
+template <typename T, int D>
+__device__ __forceinline__ void mf_compute(const MfStage<D> &st, const u32x4 *qop,
                                            float scale_log2, float &mrun, float &lrun,
                                            f32x4 *o, char *kt, char *vt, int l) {
   constexpr int NR = D / 32, KK = D / 32, EB = D / 16, ST = mf_stride<D>(), LPR = D / 8;
@@ -379,8 +384,12 @@ __device__ __forceinline__ void mf_compute(const MfStage<D> &st, const bf16x8 *q
     const uint2 *src = reinterpret_cast<const uint2 *>(kt + c * ST + 64 * kk + 16 * g);
     const uint2 lo = src[0], hi = src[1];
     const u32x4 kw = {lo.x, lo.y, hi.x, hi.y};
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qop[kk], sc, 0,
-                                                 0, 0);
+    if constexpr (__is_same(T, __bf16))
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw),
+                                                   __builtin_bit_cast(bf16x8, qop[kk]), sc, 0, 0, 0);
+    else
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kw),
+                                                  __builtin_bit_cast(f16x8, qop[kk]), sc, 0, 0, 0);
   }
   // scores: a row past the range has N = 0 (range-checked load), so log2 N = -inf drops it
   float z[4], mx = -__builtin_inff();
@@ -405,22 +414,30 @@ __device__ __forceinline__ void mf_compute(const MfStage<D> &st, const bf16x8 *q
   float al[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
-  bf16x4 ph, pl;
+  typedef T tx4 __attribute__((ext_vector_type(4)));
+  constexpr float psc = __is_same(T, __bf16) ? 1.f : kF16PScale;
+  tx4 ph, pl;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ph[i] = (__bf16)p[i];
-    pl[i] = (__bf16)(p[i] - (float)ph[i]);
+    const float ps_i = p[i] * psc;
+    ph[i] = (T)ps_i;
+    pl[i] = (T)(ps_i - (float)ph[i]);
   }
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) {
-    bf16x4 vop;
+    tx4 vop;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      vop[j] = *reinterpret_cast<const __bf16 *>(vt + (4 * g + j) * ST + 2 * (16 * eb + c));
+      vop[j] = *reinterpret_cast<const T *>(vt + (4 * g + j) * ST + 2 * (16 * eb + c));
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[eb][i] *= al[i];
-    o[eb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vop, o[eb], 0, 0, 0);
-    o[eb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vop, o[eb], 0, 0, 0);
+    if constexpr (__is_same(T, __bf16)) {
+      o[eb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vop, o[eb], 0, 0, 0);
+      o[eb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vop, o[eb], 0, 0, 0);
+    } else {
+      o[eb] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vop, o[eb], 0, 0, 0);
+      o[eb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vop, o[eb], 0, 0, 0);
+    }
   }
 }
 
@@ -506,12 +523,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
       constexpr int KK = D / 32, EB = D / 16, NS = DEC_NS;
       const int gq = l >> 4, c = l & 15;
       // q of head c as the B operand (zeros for the padding heads c >= G), loaded first
-      bf16x8 qop[KK];
+      u32x4 qop[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         u32x4 qw = {0u, 0u, 0u, 0u};
         if (c < G) qw = ld16(a.q + ((g * a.H_q + kvh * G + c) * (int64_t)D) * 2 + 64 * kk + 16 * gq);
-        qop[kk] = __builtin_bit_cast(bf16x8, qw);
+        qop[kk] = qw;
       }
       // each stage's loads are issued as one group, in stage order, ahead of the compute that
       // precedes their use (sched_barrier keeps the scheduler from interleaving or sinking them:
@@ -534,7 +551,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
           if (cur >= we) break;
           mf_load<D>(st[(k + NS - 1) % NS], rs, cur + (NS - 1) * 16 - wb, lane_kv, lane_n);
           __builtin_amdgcn_sched_barrier(0);
-          mf_compute<D>(st[k], qop, a.scale_log2, mrun, lrun, o, s_kt[w], s_vt[w], l);
+          mf_compute<T, D>(st[k], qop, a.scale_log2, mrun, lrun, o, s_kt[w], s_vt[w], l);
         }
       }
       lrun += __shfl_xor(lrun, 16);
@@ -543,11 +560,12 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
         s_part[w][l][0] = mrun;
         s_part[w][l][1] = lrun;
       }
+      constexpr float pinv = __is_same(T, __bf16) ? 1.f : 1.f / kF16PScale;
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * gq + i < G) s_part[w][4 * gq + i][4 + 16 * eb + c] = o[eb][i];
+          if (4 * gq + i < G) s_part[w][4 * gq + i][4 + 16 * eb + c] = o[eb][i] * pinv;
     } else {
     // this lane's q segment for each head of the wave's head set, loaded first: loads retire in
     // order, so q issued after the stages would make the first sub-block wait for all of them
@@ -799,7 +817,7 @@ int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_item
   }
   // G = 8: twice the units, in groups of 16 (kMaxSplitGroups is a multiple of 16, so a
   // workgroup's units keep their partner 8 indices away in every pass)
-  const bool sets2 = G >= 8 && !(dtype == kDtypeBf16 && DEC_MFMA);  // dec_head_sets<T, G>() == 2
+  const bool sets2 = G >= 8 && !(dtype != kDtypeF32 && DEC_MFMA);  // dec_head_sets<T, G>() == 2
   const int64_t units = sets2 ? dec_units<2>(max_items) : max_items;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);

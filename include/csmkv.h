@@ -178,7 +178,11 @@ CSMKV_API size_t decode_attn_logn_workspace_bytes(const csmkv_cache *cache, int3
  * q : [groups][H_q][d] in the cache dtype, groups = num_slices / H_kv; query head h of
  *   group g reads slice g * H_kv + h / (H_q / H_kv).
  * O : [groups][H_q][d] fp32 (written for every head; an empty slice gives zeros).
- * Arithmetic in fp32 (exp/log in base 2 with the log2(e) factor folded into the scale).
+ * Arithmetic in fp32 (exp/log in base 2 with the log2(e) factor folded into the scale).  bf16
+ * and fp16 caches take q.k and P.V on matrix cores: the q.k products are exact and summed in
+ * fp32; P enters P.V as two terms of the storage type (hi + lo, fp16 on a 2^14-scaled P), about
+ * 2^-17 (bf16) or 2^-22 (fp16) relative, summed in fp32; the softmax denominator is summed in
+ * fp32 from P itself.
  * H_kv >= 1, H_q a multiple of H_kv with H_q / H_kv in {1, 2, 4, 8};
  * num_slices a multiple of H_kv.  Workspace as for csm_compress (first int32 = error word).
  */

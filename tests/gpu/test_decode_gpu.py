@@ -447,3 +447,28 @@ def test_seeded_sweep_decode_plan_kernel(lib, dev):
     print(worst)
     assert worst[str(torch.float32)] < 2e-5
     assert worst[str(torch.bfloat16)] < 2e-4 and worst[str(torch.float16)] < 2e-4
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("G", [4, 8])
+def test_peaked_and_flat_attention_precision(lib, dev, dtype, G):
+    """The P.V product on matrix cores takes P as two terms of the storage type: queries scaled
+    so the softmax is flat (q = 0), moderate, or peaked on a few tokens (weights down to the
+    fp16 subnormal range and below), values of large magnitude, degrees up to 10^6.  Every head
+    against the oracle, relative to the output's magnitude: 2e-4 (fp32 rounding of scores of a
+    few hundred moves p by ~4e-5; P as a single bf16 term would miss the flat case by ~2e-3)."""
+    H_kv = 2
+    S, cap = 2 * H_kv, 3100
+    lens = [3100, 1, 2049, 777]
+    rng = np.random.default_rng(17 + G)
+    for scale, vmag in ((0.0, 1.0), (3.0, 50.0), (25.0, 1.0), (60.0, 300.0)):
+        K, V, N, L = host_cache(S, cap, lens, dtype=dtype, seed=int(scale) + G, degrees=True)
+        V = (V.float() * vmag).to(dtype)
+        N[N > 0] = torch.from_numpy(rng.integers(1, 10 ** 6, size=int((N > 0).sum())).astype(np.int32))
+        q = (torch.from_numpy(rng.standard_normal((S // H_kv, G * H_kv, 128))).float() * scale).to(dtype)
+        O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), L.to(dev), G * H_kv,
+                                 H_kv).cpu().double().numpy()
+        ref = _oracle_all(q, K, V, N, L, G * H_kv, H_kv)
+        err = float(np.abs(O - ref).max()) / max(float(np.abs(ref).max()), 1e-30)
+        print(dtype, G, scale, vmag, "max err / max |O|", err)
+        assert err < 2e-4, (scale, vmag, err)

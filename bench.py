@@ -209,6 +209,30 @@ def main():
         torch.cuda.synchronize()
         layer_ms.append(e0.elapsed_time(e1))
     assert lib.read_error(ws_l) == lib.OK
+    O_eager = O.clone()
+    # the same 32 calls replayed from one HIP graph: the GPU's own time per layer, without the
+    # host's per-call cost (argument checks, marshalling and two launches per call)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        layer_calls()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    layer_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(layer_graph):
+        layer_calls()
+    layer_graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_eager)
+    layer_graph_ms = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer_graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        layer_graph_ms.append(e0.elapsed_time(e1))
+    del layer_graph
     dec_alg_now = int(Ld.cpu().numpy().sum()) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
 
     # auxiliary: the in-place round.  Before each rep the input is restored and the 256 MB
@@ -358,7 +382,10 @@ def main():
                         "per_layer_calls": {
                             "calls": w.layers, "median_us": median(layer_ms) * 1e3,
                             "min_us": min(layer_ms) * 1e3, "alg_bytes": dec_alg_now,
-                            "GBps": dec_alg_now / (median(layer_ms) * 1e-3) / 1e9},
+                            "GBps": dec_alg_now / (median(layer_ms) * 1e-3) / 1e9,
+                            "hip_graph_median_us": median(layer_graph_ms) * 1e3,
+                            "hip_graph_min_us": min(layer_graph_ms) * 1e3,
+                            "hip_graph_GBps": dec_alg_now / (median(layer_graph_ms) * 1e-3) / 1e9},
                         "traffic": recorded_traffic("dec_split_bf16_g4", DEC_SOURCES)},
         "append_us": app_avg * 1e3,
         "decode_loop_wall_us_per_step": {"eager": eager_us, "hip_graph": graph_us,

@@ -255,7 +255,7 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
   constexpr int EPL = DT::EPL;
   T *tsel = nullptr;
   const float NEG_INF = -__builtin_inff();
-  float zs[DT::NR][G];
+  float zs[DT::NR][G], msf[G];
 #pragma unroll
   for (int i = 0; i < DT::NR; ++i) {
     const bool ok = sb + DT::RPW * i + rw < we;
@@ -274,7 +274,10 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
 #pragma unroll
     for (int o2 = DT::LPR; o2 < 64; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
     const float mn = fmaxf(mrun[h], mx);
-    const float alpha = fast_exp2(mrun[h] - mn);
+    // while every row so far has degree 0 the maximum is -inf: exponentiate against 0 instead,
+    // which gives such rows weight 0 (as log 0 = -inf does) rather than NaN
+    msf[h] = mn == NEG_INF ? 0.f : mn;
+    const float alpha = fast_exp2(mrun[h] - msf[h]);
     mrun[h] = mn;
     lrun[h] *= alpha;
 #pragma unroll
@@ -286,7 +289,7 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
     seg_to_f32(st.v[i], vf, tsel);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float pr = fast_exp2(zs[i][h] - mrun[h]);
+      const float pr = fast_exp2(zs[i][h] - msf[h]);
       lrun[h] += pr;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pr, vf[e], o[h][e]);
@@ -401,12 +404,15 @@ __device__ __forceinline__ void mf_compute(const MfStage<D> &st, const u32x4 *qo
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mn = fmaxf(mrun, mx);
-  const float alpha = fast_exp2(mrun - mn);
+  // while every row so far has degree 0 the maximum is -inf: exponentiate against 0 instead,
+  // which gives such rows weight 0 (as log 0 = -inf does) rather than NaN
+  const float msf = mn == -__builtin_inff() ? 0.f : mn;
+  const float alpha = fast_exp2(mrun - msf);
   mrun = mn;
   float p[4], ps = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    p[i] = fast_exp2(z[i] - mn);
+    p[i] = fast_exp2(z[i] - msf);
     ps += p[i];
   }
   lrun = fmaf(lrun, alpha, ps);

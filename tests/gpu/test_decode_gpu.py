@@ -472,3 +472,28 @@ def test_peaked_and_flat_attention_precision(lib, dev, dtype, G):
         err = float(np.abs(O - ref).max()) / max(float(np.abs(ref).max()), 1e-30)
         print(dtype, G, scale, vmag, "max err / max |O|", err)
         assert err < 2e-4, (scale, vmag, err)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_rows_of_degree_zero_weigh_nothing(lib, dev, dtype):
+    """A row of degree 0 inside the length adds log 0 = -inf to its score, so it weighs nothing;
+    whole leading runs of such rows (more than a wave's first sub-blocks, and a whole slice but
+    one row) must not turn the output into NaN.  Every head against the oracle."""
+    H_kv, G = 2, 4
+    S, cap = 2 * H_kv, 3000
+    lens = [3000, 2500, 700, 65]
+    K, V, N, L = host_cache(S, cap, lens, dtype=dtype, seed=23, degrees=True)
+    N[0, :1500] = 0                # the first half of slice 0
+    N[1, :2499] = 0                # all but the last row of slice 1
+    N[2, 100:400] = 0              # a run in the middle
+    N[3, ::2] = 0                  # every other row
+    rng = np.random.default_rng(29)
+    q = torch.from_numpy(rng.standard_normal((S // H_kv, G * H_kv, 128))).float().to(dtype)
+    O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), L.to(dev), G * H_kv,
+                             H_kv).cpu().double().numpy()
+    assert np.all(np.isfinite(O))
+    with np.errstate(divide="ignore"):  # the oracle's log 0 = -inf is the intended weight
+        ref = _oracle_all(q, K, V, N, L, G * H_kv, H_kv)
+    err = float(np.abs(O - ref).max())
+    print(dtype, "max abs", err)
+    assert err < (2e-5 if dtype == torch.float32 else 2e-4)

@@ -11,14 +11,14 @@
 //                 for a layer's few slices, items of up to 2048 tokens for many slices.
 //   dec_split   : workgroups stride over the work items (at most 2048 workgroups).  A work
 //                 item is up to tsplit tokens of one slice, shared by the G query heads of
-//                 that KV head (G = 8: two workgroups of four heads each), so K, V and N are
-//                 read from HBM once per step.  Each wave streams a
-//                 quarter of the item: 16 B per lane per row, sub-blocks of 16 tokens
-//                 (bf16) with the next sub-block's loads in flight while the current
-//                 one is computed, q.k by packed bf16 dot products, a 16-lane DPP reduction,
-//                 base-2 online softmax (log2 N added, log2 e folded into the scale),
-//                 P.V accumulated in fp32.  Waves merge in LDS; each item writes one
-//                 (max, sum, 0, 0, o[128]) partial per head.
+//                 that KV head, so K, V and N are read from HBM once per step.  Each wave
+//                 streams a quarter of the item: 16 B per lane per row, 16-token sub-blocks
+//                 with the next two sub-blocks' loads in flight while the current one is
+//                 computed; base-2 online softmax (log2 N added, log2 e folded into the
+//                 scale).  bf16 / fp16: q.k and P.V on MFMA tiles (described below); fp32:
+//                 FMAs with a DPP reduction over the lanes of a row, and at G = 8 two
+//                 workgroups of four heads each.  Waves merge in LDS; each item writes one (max, sum, 0, 0, o[d])
+//                 partial per head.
 //   dec_combine : one 1024-thread workgroup per slice merges the item partials by
 //                 log-sum-exp (a running maximum per thread over item groups in parallel,
 //                 then the groups merged against their common maximum).
@@ -298,8 +298,8 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
 }
 
 // bf16 and fp16 caches run q.k and P.V on MFMA (16 x 16 tiles, heads padded to 16; fp32 caches
-// keep the VALU path below).  A wave takes
-// 16-token sub-blocks; lane l covers token row l mod 16 and lane group g = l / 16:
+// keep the VALU path above).  A wave takes 16-token sub-blocks; lane l covers token row l mod 16
+// and lane group g = l / 16:
 //   K and V rows are loaded as whole rows (non-temporal, the VALU path's pattern) and staged in
 //   per-wave LDS tiles (rows padded by 8 bytes so both read patterns below hit distinct banks);
 //   q.k : v_mfma_f32_16x16x32_bf16 with A = K rows from the tile (lane: row l mod 16, 16 bytes at

@@ -311,11 +311,8 @@ __device__ __forceinline__ void dec_compute(const DecStage<DecTile<T, G, D>::NR>
 //         type, p = hi + lo (hi = RNE(p), lo = RNE(p - hi); fp16 on p * 2^14), which keeps it to
 //         about 2^-17 (bf16) or 2^-22 (fp16) relative; the sum of P is taken in fp32 from p.
 //         Lane l holds O rows (heads) 4g .. 4g + 3, column l mod 16 of each block.
-#ifndef DEC_MFMA
-#define DEC_MFMA 1
-#endif
 template <typename T>
-constexpr bool dec_mfma() { return DEC_MFMA && (__is_same(T, __bf16) || __is_same(T, _Float16)); }
+constexpr bool dec_mfma() { return __is_same(T, __bf16) || __is_same(T, _Float16); }
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 // fp16 P terms carry this factor (an exact power of two, removed from O at the end) so that
@@ -823,7 +820,7 @@ int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_item
   }
   // G = 8: twice the units, in groups of 16 (kMaxSplitGroups is a multiple of 16, so a
   // workgroup's units keep their partner 8 indices away in every pass)
-  const bool sets2 = G >= 8 && !(dtype != kDtypeF32 && DEC_MFMA);  // dec_head_sets<T, G>() == 2
+  const bool sets2 = G >= 8 && dtype == kDtypeF32;  // dec_head_sets<T, G>() == 2
   const int64_t units = sets2 ? dec_units<2>(max_items) : max_items;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);

@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-slices", type=int, default=32)
+    ap.add_argument("--cpu-slices", type=int, default=246,
+                    help="compressible slices the oracle baseline clusters (all 246 by default)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--workloads", default="1,2,3,5,4:f16,4:d64,4:c512,4:g8",
@@ -93,6 +94,11 @@ def main():
     import torch
 
     import kvsynth
+    # the oracle baseline forks its host workers first, before anything (the HIP library
+    # included) touches the GPU, so that they start from a process with no GPU state
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(kvsynth.workload(4), args.cpu_slices)
     from kv_cache_clustering_amd import _lib as lib
     from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
 
@@ -335,11 +341,6 @@ def main():
         del g, h
     del a, b
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, K0, V0, N0, L0, Kd, Vd, Nd, Ld, q_all[W + K - 1], maskh,
-                           args.cpu_slices)
-
     others = []
     wl = [x.strip() for x in args.workloads.split(",") if x.strip()]
     if wl:
@@ -413,6 +414,11 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
     import torch
 
     import kvsynth
+    # the oracle baseline forks its host workers first, before anything (the HIP library
+    # included) touches the GPU, so that they start from a process with no GPU state
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(kvsynth.workload(4), args.cpu_slices)
     from kv_cache_clustering_amd import _lib as lib
     from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
 
@@ -489,45 +495,92 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
     return out
 
 
-def cpu_baseline(w, K0, V0, N0, L0, Kd, Vd, Nd, Ld, q, maskh, nslices):
-    """The fp64 oracle on the host: one CSM round on a sample of slices (slice-tokens/s) and
-    one full decode step over every slice of the serving cache (us/step)."""
+def _oracle_worker(cid, zs, csm_zs, barrier, queue):
+    """One host worker of the oracle baseline: generates its slices of the workload on the host
+    (the workload's per-slice seeds, AR(1) parameters and bf16 rounding; the host's random
+    streams, so the same distribution but not the device's bits), then, between barriers shared
+    with the other workers, times one CSM round on its compressible slices and one decode step
+    (every query head of its slices at their serving lengths)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
 
+    import kvsynth
+    from kvsynth import gen as kg
+    from kv_cache_clustering_amd.schedule import Algorithm1
     from oracle import attention as oatt
-    from oracle import bf16 as obf16
     from oracle import csm as ocsm
 
-    def f64(t):
-        return obf16.bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
-
-    pick = [z for z in range(K0.shape[0]) if not maskh[z]]
-    rng = np.random.default_rng(0)
-    pick = sorted(rng.choice(pick, size=min(nslices, len(pick)), replace=False).tolist())
-    inputs = [(f64(K0[z, :w.ctx]), f64(V0[z, :w.ctx]), N0[z, :w.ctx].cpu().numpy().astype(np.int64))
-              for z in pick]
-    lens = Ld.cpu().numpy()
-    dec_in = [(f64(Kd[z, :lens[z]]), f64(Vd[z, :lens[z]]), Nd[z, :lens[z]].cpu().numpy().astype(np.int64))
-              for z in range(Kd.shape[0])]
-    qh = f64(q)
+    w = kvsynth.workload(cid)
+    mask = kg.outlier_mask(w)
+    sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
+    sched.prefill_rounds()
+    serve_len = sched.s  # the compressed slices' length after the annealed prefill rounds
+    data = []
+    for z in zs:
+        b, layer, head = kg._slice_coords(w, z)
+        rho, sigma, mu = kg.slice_params(w, z)
+        rng = np.random.default_rng(kg.seed_of(cid, b, layer, head, "K"))
+        k = kg.ar1_numpy(rng, w.ctx, w.d, rho, sigma, mu)
+        v = np.random.default_rng(kg.seed_of(cid, b, layer, head, "V")).standard_normal((w.ctx, w.d))
+        k = torch.from_numpy(k).float().to(torch.bfloat16).double().numpy()
+        v = torch.from_numpy(v).float().to(torch.bfloat16).double().numpy()
+        data.append((z, k, v))
+    q = np.random.default_rng(kg.seed_of(cid, 0, 0, 0, "q")).standard_normal((w.G, w.d))
+    ones = np.ones(w.ctx, dtype=np.int64)
     with threadpool_limits(1):
+        barrier.wait()
         t0 = time.perf_counter()
-        for (k, v, n) in inputs:
-            ocsm.csm_round_slice(k, v, n, w.ctx, w.n1, w.n2, w.c, w.r_init, "bf16", "f64")
-        t_csm = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        for z, (k, v, n) in enumerate(dec_in):
-            g, kvh = divmod(z, w.H_kv)
+        for z, k, v in data:
+            if z in csm_zs:
+                ocsm.csm_round_slice(k, v, ones, w.ctx, w.n1, w.n2, w.c, w.r_init, "bf16", "f64")
+        t1 = time.perf_counter()
+        barrier.wait()
+        t2 = time.perf_counter()
+        for z, k, v in data:
+            s = w.ctx if mask[z] else serve_len
             for h in range(w.G):
-                oatt.logn_attention_one(qh[g, kvh * w.G + h], k, v, n)
-        t_dec = time.perf_counter() - t0
-    return {"value": len(inputs) * w.ctx / t_csm, "unit": "slice-tokens/s", "cores": 1,
+                oatt.logn_attention_one(q[h], k[:s], v[:s], ones[:s])
+        t3 = time.perf_counter()
+    queue.put((t0, t1, t2, t3))
+
+
+def cpu_baseline(w, nslices):
+    """The fp64 oracle on the host cores, one worker process per core (at most 16): one CSM
+    round over nslices of the workload's compressible slices (slice-tokens/s) and one decode
+    step over every slice at the serving lengths (us/step).  Wall time from the first worker's
+    start to the last one's end of each phase.  Must run before anything touches the GPU: the
+    workers are forked."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    from kvsynth import gen as kg
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    mask = kg.outlier_mask(w)
+    comp = [z for z in range(w.slices) if not mask[z]]
+    csm_zs = set(comp[:: max(1, len(comp) // max(1, nslices))][:nslices])
+    ctx = mp.get_context("fork")
+    barrier, queue = ctx.Barrier(cores), ctx.Queue()
+    shares = [list(range(i, w.slices, cores)) for i in range(cores)]
+    procs = [ctx.Process(target=_oracle_worker, args=(w.cid, zs, csm_zs, barrier, queue))
+             for zs in shares]
+    for p in procs:
+        p.start()
+    stamps = [queue.get() for _ in procs]
+    for p in procs:
+        p.join()
+        if p.exitcode != 0:
+            raise RuntimeError(f"oracle worker failed with exit code {p.exitcode}")
+    t_csm = max(s[1] for s in stamps) - min(s[0] for s in stamps)
+    t_dec = max(s[3] for s in stamps) - min(s[2] for s in stamps)
+    return {"value": len(csm_zs) * w.ctx / t_csm, "unit": "slice-tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"CSM round on {len(inputs)} of {int((maskh == 0).sum())} compressible "
-                      f"64K slices (fp64 numpy, 1 thread); decode: one full step over all "
-                      f"{Kd.shape[0]} slices",
+            "sample": f"CSM round on {len(csm_zs)} of {len(comp)} compressible 64K slices and a "
+                      f"decode step over all {w.slices} slices at the serving lengths (fp64 "
+                      f"numpy, {cores} worker processes, one thread each; slices generated on "
+                      f"the host with the workload's seeds and recipe)",
             "csm_s": t_csm, "decode_us_per_step": t_dec * 1e6,
             "host_cpus": len(os.sched_getaffinity(0))}
 

@@ -414,11 +414,6 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
     import torch
 
     import kvsynth
-    # the oracle baseline forks its host workers first, before anything (the HIP library
-    # included) touches the GPU, so that they start from a process with no GPU state
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(kvsynth.workload(4), args.cpu_slices)
     from kv_cache_clustering_amd import _lib as lib
     from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
 

@@ -572,7 +572,7 @@ def cpu_baseline(w, nslices):
     t_dec = max(s[3] for s in stamps) - min(s[2] for s in stamps)
     return {"value": len(csm_zs) * w.ctx / t_csm, "unit": "slice-tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"CSM round on {len(csm_zs)} of {len(comp)} compressible 64K slices and a "
+            "sample": f"CSM round on {len(csm_zs)} of {len(comp)} compressible {w.ctx // 1024}K slices and a "
                       f"decode step over all {w.slices} slices at the serving lengths (fp64 "
                       f"numpy, {cores} worker processes, one thread each; slices generated on "
                       f"the host with the workload's seeds and recipe)",

@@ -491,19 +491,31 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
 
 
 def _oracle_worker(cid, zs, csm_zs, barrier, queue):
+    """Runs _oracle_work and reports its stamps, or the error that stopped it (after which the
+    barrier is broken, so that no other worker waits for this one)."""
+    try:
+        queue.put(("ok", _oracle_work(cid, zs, csm_zs, barrier)))
+    except BaseException as e:  # reported to the parent, which raises
+        barrier.abort()
+        queue.put(("error", f"{type(e).__name__}: {e}"))
+
+
+def _oracle_work(cid, zs, csm_zs, barrier):
     """One host worker of the oracle baseline: generates its slices of the workload on the host
     (the workload's per-slice seeds, AR(1) parameters and bf16 rounding; the host's random
     streams, so the same distribution but not the device's bits), then, between barriers shared
     with the other workers, times one CSM round on its compressible slices and one decode step
     (every query head of its slices at their serving lengths)."""
+    # numpy only: torch's OpenMP pool is not safe to use in a forked child of a process that
+    # has already run it (as a test process may have)
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_limits
 
     import kvsynth
     from kvsynth import gen as kg
     from kv_cache_clustering_amd.schedule import Algorithm1
     from oracle import attention as oatt
+    from oracle import bf16 as obf16
     from oracle import csm as ocsm
 
     w = kvsynth.workload(cid)
@@ -518,26 +530,27 @@ def _oracle_worker(cid, zs, csm_zs, barrier, queue):
         rng = np.random.default_rng(kg.seed_of(cid, b, layer, head, "K"))
         k = kg.ar1_numpy(rng, w.ctx, w.d, rho, sigma, mu)
         v = np.random.default_rng(kg.seed_of(cid, b, layer, head, "V")).standard_normal((w.ctx, w.d))
-        k = torch.from_numpy(k).float().to(torch.bfloat16).double().numpy()
-        v = torch.from_numpy(v).float().to(torch.bfloat16).double().numpy()
+        # generated in fp64, stored as the device stores it: fp32, then bf16 (nearest even)
+        k = obf16.round_to_bf16(k.astype(np.float32).astype(np.float64))
+        v = obf16.round_to_bf16(v.astype(np.float32).astype(np.float64))
         data.append((z, k, v))
     q = np.random.default_rng(kg.seed_of(cid, 0, 0, 0, "q")).standard_normal((w.G, w.d))
     ones = np.ones(w.ctx, dtype=np.int64)
     with threadpool_limits(1):
-        barrier.wait()
+        barrier.wait(timeout=900)
         t0 = time.perf_counter()
         for z, k, v in data:
             if z in csm_zs:
                 ocsm.csm_round_slice(k, v, ones, w.ctx, w.n1, w.n2, w.c, w.r_init, "bf16", "f64")
         t1 = time.perf_counter()
-        barrier.wait()
+        barrier.wait(timeout=900)
         t2 = time.perf_counter()
         for z, k, v in data:
             s = w.ctx if mask[z] else serve_len
             for h in range(w.G):
                 oatt.logn_attention_one(q[h], k[:s], v[:s], ones[:s])
         t3 = time.perf_counter()
-    queue.put((t0, t1, t2, t3))
+    return t0, t1, t2, t3
 
 
 def cpu_baseline(w, nslices):
@@ -563,11 +576,19 @@ def cpu_baseline(w, nslices):
              for zs in shares]
     for p in procs:
         p.start()
-    stamps = [queue.get() for _ in procs]
-    for p in procs:
-        p.join()
-        if p.exitcode != 0:
-            raise RuntimeError(f"oracle worker failed with exit code {p.exitcode}")
+    results = []
+    try:
+        for _ in procs:
+            results.append(queue.get(timeout=900))
+    finally:
+        for p in procs:
+            p.join(timeout=60)
+            if p.is_alive():
+                p.terminate()
+    errors = [r[1] for r in results if r[0] != "ok"]
+    if errors or len(results) != len(procs):
+        raise RuntimeError(f"oracle baseline workers failed: {errors or 'no report'}")
+    stamps = [r[1] for r in results]
     t_csm = max(s[1] for s in stamps) - min(s[0] for s in stamps)
     t_dec = max(s[3] for s in stamps) - min(s[2] for s in stamps)
     return {"value": len(csm_zs) * w.ctx / t_csm, "unit": "slice-tokens/s", "cores": cores,

@@ -541,7 +541,7 @@ def _oracle_work(cid, zs, csm_zs, barrier):
         t0 = time.perf_counter()
         for z, k, v in data:
             if z in csm_zs:
-                ocsm.csm_round_slice(k, v, ones, w.ctx, w.n1, w.n2, w.c, w.r_init, "bf16", "f64")
+                ocsm.csm_round_slice(k, v, ones, w.ctx, w.n1, w.n2, w.c, w.r_init, "bf16")
         t1 = time.perf_counter()
         barrier.wait(timeout=900)
         t2 = time.perf_counter()

@@ -25,10 +25,10 @@ Readings taken where the pages are silent (each also listed in the design doc):
   * Compaction keeps the original order; a centroid occupies its target's slot.
   * Outlier (masked) slices are left untouched.
 
-Decision precision: ``precision='f64'`` scores in fp64 (the definition); ``'f32'``
-scores in binary32 (dot products and norms rounded to fp32, then the dot product scaled
-by the two rounded reciprocal norms), which is the precision and form a GPU kernel
-decides in.
+Decisions are taken on the definition in fp64: every dot product is summed in one fixed
+order for every pair of rows (so two identical rows score identically and exact ties
+stay exact ties), norms likewise, and the cosine is the dot product over the product of
+the two floored norms.
 
 Pins (tests/oracle/): Theorem 6.1 brute force for the partition; argmax / ranking
 properties on every chunk; r = 0 identity; sum of N conserved; first moments
@@ -69,27 +69,20 @@ def partition(L):
     return np.arange(0, L, 2), np.arange(1, L, 2)
 
 
-def cosine_matrix(Ka, Kb, precision="f64"):
-    """Cosine similarity S[i, j] of rows a_i and b_j, norms floored at eps.
+def cosine_matrix(Ka, Kb):
+    """Cosine similarity S[i, j] = <a_i, b_j> / (max(|a_i|, eps) * max(|b_j|, eps)), fp64.
 
-    'f64': <a_i, b_j> / (max(|a_i|, eps) * max(|b_j|, eps)), the definition.
-    'f32': binary32 throughout, evaluated as (<a_i, b_j> * (1 / max(|b_j|, eps))) *
-    (1 / max(|a_i|, eps)) with each reciprocal rounded once: the form the GPU kernel
-    decides with, so that both sides take the same decision up to summation order.
+    The dot products are evaluated element by element in the same summation order for every
+    (i, j) (einsum's own loop, not a blocked matrix product whose order can depend on where
+    a row sits in the block), so rows with equal values give bit-identical scores.
     """
-    dt = {"f64": np.float64, "f32": np.float32}[precision]
-    a = np.asarray(Ka).astype(dt)
-    b = np.asarray(Kb).astype(dt)
-    dots = a @ b.T
-    na = np.sqrt(np.sum(a * a, axis=1, dtype=dt))
-    nb = np.sqrt(np.sum(b * b, axis=1, dtype=dt))
-    floor = dt(NORM_FLOOR)
-    if precision == "f64":
-        den = np.maximum(na, floor)[:, None] * np.maximum(nb, floor)[None, :]
-        return dots / den
-    inv_a = dt(1) / np.maximum(na, floor)
-    inv_b = dt(1) / np.maximum(nb, floor)
-    return ((dots * inv_b[None, :]) * inv_a[:, None]).astype(dt)
+    a = np.asarray(Ka, dtype=np.float64)
+    b = np.asarray(Kb, dtype=np.float64)
+    dots = np.einsum("ik,jk->ij", a, b)
+    na = np.sqrt(np.einsum("ik,ik->i", a, a))
+    nb = np.sqrt(np.einsum("jk,jk->j", b, b))
+    den = np.maximum(na, NORM_FLOOR)[:, None] * np.maximum(nb, NORM_FLOOR)[None, :]
+    return dots / den
 
 
 def match(S):
@@ -107,7 +100,7 @@ def select_top(score, m):
     return sel
 
 
-def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64", forced=None):
+def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", forced=None):
     """One CSM round over one slice.
 
     K, V : [cap, d] fp64 arrays holding the stored values; N : [cap] integer degrees;
@@ -116,9 +109,9 @@ def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64", f
     forced : optional {chunk start: (best_b, selected)} replacing the match and selection
     decisions of those chunks (used to follow another implementation's decisions where
     they differ only at a near-tie, so that merging and compaction can still be compared).
-    Returns (K', V', N', s', taps) where taps is a list with one dict per chunk
-    (start, L, m, best_b, score, selected) and 'src_pos' maps every output row < s'
-    to the input row it came from.
+    Returns (K', V', N', s', taps) where taps['chunks'] holds one dict per chunk
+    (start, L, m, best_b, score, selected, and S, the chunk's similarity matrix) and
+    taps['src_pos'] maps every output row < s' to the input row it came from.
     """
     K = np.array(K, dtype=np.float64)
     V = np.array(V, dtype=np.float64)
@@ -137,14 +130,14 @@ def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64", f
             keep_rows.extend(range(start, end))
             taps.append(tap)
             continue
-        S = cosine_matrix(K[rows_a], K[rows_b], precision)
+        S = cosine_matrix(K[rows_a], K[rows_b])
         best_b, score = match(S)
         m = merge_count(r, L)
         sel = select_top(score, m)
         if forced is not None and start in forced:
             best_b = np.asarray(forced[start][0], dtype=np.int64)
             sel = np.asarray(forced[start][1], dtype=bool)
-        tap.update(m=m, best_b=best_b, score=score, selected=sel)
+        tap.update(m=m, best_b=best_b, score=score, selected=sel, S=S)
         taps.append(tap)
         # Degree-weighted merge: every selected A row folds into its matched B row.
         numk = {}
@@ -182,8 +175,7 @@ def csm_round_slice(K, V, N, s, n1, n2, c, r, storage="bf16", precision="f64", f
     return K2, V2, N2, s_new, {"chunks": taps, "src_pos": src_pos}
 
 
-def csm_compress(K, V, N, lens, n1, n2, c, r, outlier_mask=None, storage="bf16",
-                 precision="f64"):
+def csm_compress(K, V, N, lens, n1, n2, c, r, outlier_mask=None, storage="bf16"):
     """One CSM round over every slice of a cache.
 
     K, V : [S, cap, d]; N : [S, cap]; lens : [S]; outlier_mask : [S] (nonzero = skip).
@@ -201,7 +193,7 @@ def csm_compress(K, V, N, lens, n1, n2, c, r, outlier_mask=None, storage="bf16",
             taps.append(None)
             continue
         k, v, n, s2, t = csm_round_slice(K[z], V[z], N[z], int(lens[z]), n1, n2, c, r,
-                                         storage, precision)
+                                         storage)
         K2[z], V2[z], N2[z], lens2[z] = k, v, n, s2
         taps.append(t)
     return K2, V2, N2, lens2, taps

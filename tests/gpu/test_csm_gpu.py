@@ -55,7 +55,7 @@ def test_small_caches_bf16(lib, dev, c, r, n1, n2):
     mask[3] = 1
     rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
     print(rep)
-    parity.check_report(rep, near_bar=5e-3)
+    parity.check_report(rep)
 
 
 @pytest.mark.parametrize("c,r,n1,n2", [(256, 0.5, 16, 64), (256, 1.0, 16, 64), (64, 0.77, 3, 5),
@@ -68,7 +68,7 @@ def test_small_caches_fp16(lib, dev, c, r, n1, n2):
     mask[6] = 1
     rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
     print(rep)
-    parity.check_report(rep, near_bar=5e-3)
+    parity.check_report(rep)
 
 
 def test_fp16_in_place_equals_out_of_place_and_decode(lib, dev):
@@ -99,7 +99,7 @@ def test_small_caches_fp32(lib, dev):
     K, V, N, lens = host_cache(len(LENS), 2100, LENS, dtype=torch.float32, seed=3, degrees=True)
     rep = run_and_compare(lib, dev, K, V, N, lens, 16, 64, 256, 0.5)
     print(rep)
-    parity.check_report(rep, near_bar=5e-3)
+    parity.check_report(rep)
 
 
 def test_single_head_2k_fp32_workload(lib, dev):
@@ -163,16 +163,24 @@ def _device_workload(lib, dev, cid, sample, n_outlier_checks=2, out_of_place=Fal
     return rep
 
 
-def test_llama3_16k_workload_sampled(lib, dev):
-    rep = _device_workload(lib, dev, 2, sample=[0, 1, 77, 130, 201, 255])
-    print(rep)
+def test_llama3_16k_workload_every_slice(lib, dev):
+    """The 16K workload (256 slices, keys with a per-head mean offset): every slice against the
+    oracle; near-tie mismatches under 0.1% of the A edges."""
+    rep = _device_workload(lib, dev, 2, sample=range(256))
+    print("16K workload, all slices:", rep)
     parity.check_report(rep)
+    assert rep.slices == 256
 
 
 def test_llama3_64k_outlier_workload_sampled(lib, dev):
-    rep = _device_workload(lib, dev, 4, sample=[0, 13, 99, 180, 255], out_of_place=True)
-    print(rep)
+    """The 64K workload: 24 compressed slices spread over all layers and heads, and all 10
+    outlier slices, against the oracle; the out-of-place round equals the in-place one on
+    every slice."""
+    rep = _device_workload(lib, dev, 4, sample=range(0, 256, 11), n_outlier_checks=10,
+                           out_of_place=True)
+    print("64K workload, sampled slices:", rep)
     parity.check_report(rep)
+    assert rep.slices >= 20
 
 
 def test_in_place_equals_out_of_place_and_is_deterministic(lib, dev):
@@ -285,7 +293,7 @@ def test_small_caches_head_dim_64(lib, dev, dtype, c, r, n1, n2):
     mask[1] = 1
     rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
     print(rep)
-    parity.check_report(rep, near_bar=5e-3)
+    parity.check_report(rep)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
@@ -320,7 +328,7 @@ def test_wide_chunks(lib, dev, dtype, d, c, r, n1, n2):
     mask[4] = 1
     rep = run_and_compare(lib, dev, K, V, N, lens, n1, n2, c, r, mask)
     print(rep)
-    parity.check_report(rep, near_bar=5e-3)
+    parity.check_report(rep)
 
 
 def test_wide_chunks_in_place_equals_out_of_place(lib, dev):
@@ -394,10 +402,6 @@ def test_seeded_sweep_of_shapes_and_parameters(lib, dev):
                                 int(rng.integers(0, cap + 1))])) for _ in range(S)]
         K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=1000 + case, degrees=True)
         mask = (rng.random(S) < 0.25).astype(np.uint8)
-        rep = run_and_compare(lib, dev, K, V, N, L, n1, n2, c, r, mask)
-        for f in ("edges", "match_near", "match_hard", "sel_near", "sel_hard", "followed_chunks",
-                  "abs_floor_used", "slices"):
-            setattr(total, f, getattr(total, f) + getattr(rep, f))
-        total.max_ulp = max(total.max_ulp, rep.max_ulp)
+        total.add(run_and_compare(lib, dev, K, V, N, L, n1, n2, c, r, mask))
     print(total)
-    parity.check_report(total, near_bar=5e-3)
+    parity.check_report(total)

@@ -25,42 +25,53 @@ def test_hand_worked_cases(golden_dir):
         N = np.array(case["N"], dtype=np.int64)
         s = K.shape[0]
         exp = case["expect"]
-        for precision in ("f64", "f32"):
-            K2, V2, N2, s2, taps = csm.csm_round_slice(K, V, N, s, case["n1"], case["n2"],
-                                                       case["c"], case["r"], storage="f64",
-                                                       precision=precision)
-            name = (case["name"], precision)
-            assert s2 == exp["s"], name
-            assert taps["src_pos"].tolist() == exp["src_pos"], name
-            assert N2[:s2].tolist() == exp["N"], name
-            np.testing.assert_allclose(K2[:s2], np.array(exp["K"]), rtol=0, atol=1e-12, err_msg=str(name))
-            np.testing.assert_allclose(V2[:s2], np.array(exp["V"]), rtol=0, atol=1e-12, err_msg=str(name))
-            got_b = [t["best_b"].tolist() for t in taps["chunks"] if "best_b" in t]
-            got_sel = [t["selected"].tolist() for t in taps["chunks"] if "selected" in t]
-            assert got_b == exp["best_b"], name
-            assert got_sel == exp["selected"], name
+        K2, V2, N2, s2, taps = csm.csm_round_slice(K, V, N, s, case["n1"], case["n2"],
+                                                   case["c"], case["r"], storage="f64")
+        name = case["name"]
+        assert s2 == exp["s"], name
+        assert taps["src_pos"].tolist() == exp["src_pos"], name
+        assert N2[:s2].tolist() == exp["N"], name
+        np.testing.assert_allclose(K2[:s2], np.array(exp["K"]), rtol=0, atol=1e-12, err_msg=str(name))
+        np.testing.assert_allclose(V2[:s2], np.array(exp["V"]), rtol=0, atol=1e-12, err_msg=str(name))
+        got_b = [t["best_b"].tolist() for t in taps["chunks"] if "best_b" in t]
+        got_sel = [t["selected"].tolist() for t in taps["chunks"] if "selected" in t]
+        assert got_b == exp["best_b"], name
+        assert got_sel == exp["selected"], name
 
 
 def test_cosine_matches_scipy():
     rng = np.random.default_rng(1)
     a = rng.standard_normal((37, 16))
     b = rng.standard_normal((29, 16))
-    S = csm.cosine_matrix(a, b, "f64")
+    S = csm.cosine_matrix(a, b)
     np.testing.assert_allclose(S, 1.0 - cdist(a, b, metric="cosine"), atol=1e-13)
-    S32 = csm.cosine_matrix(a.astype(np.float32), b.astype(np.float32), "f32")
-    assert S32.dtype == np.float32
-    np.testing.assert_allclose(S32, S, atol=2e-6)
+
+
+def test_equal_rows_score_identically():
+    """The similarity depends on the two rows' values only, so rows with equal values score
+    bit-identically against everything (ties in the definition stay exact ties), whatever
+    their position and the block shapes (fp32-valued data, whose products are not exact)."""
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        nA, nB, d = int(rng.integers(2, 257)), int(rng.integers(2, 257)), int(rng.choice([64, 128]))
+        a = rng.standard_normal((nA, d)).astype(np.float32).astype(np.float64)
+        b = rng.standard_normal((nB, d)).astype(np.float32).astype(np.float64)
+        j, j2 = sorted(rng.choice(nB, 2, replace=False))
+        i, i2 = sorted(rng.choice(nA, 2, replace=False))
+        b[j2], a[i2] = b[j], a[i]
+        S = csm.cosine_matrix(a, b)
+        assert np.array_equal(S[:, j], S[:, j2]) and np.array_equal(S[i], S[i2])
 
 
 def test_cosine_special_values_and_scale_invariance():
     e = np.eye(4)
-    S = csm.cosine_matrix(e, np.vstack([e[0] * 3.0, -e[0], e[1]]), "f64")
+    S = csm.cosine_matrix(e, np.vstack([e[0] * 3.0, -e[0], e[1]]))
     assert S[0, 0] == pytest.approx(1.0) and S[0, 1] == pytest.approx(-1.0)
     assert S[0, 2] == 0.0 and S[1, 2] == pytest.approx(1.0)
     rng = np.random.default_rng(2)
     a, b = rng.standard_normal((8, 5)), rng.standard_normal((6, 5))
-    np.testing.assert_allclose(csm.cosine_matrix(a * 7.5, b * 0.01, "f64"),
-                               csm.cosine_matrix(a, b, "f64"), atol=1e-14)
+    np.testing.assert_allclose(csm.cosine_matrix(a * 7.5, b * 0.01),
+                               csm.cosine_matrix(a, b), atol=1e-14)
 
 
 def test_merge_count_guard():
@@ -133,31 +144,63 @@ def test_degree_sum_first_moments_and_compaction(r):
         assert (x - start) % 2 == 0
 
 
+def _check_match_and_rank(K, taps):
+    """best_b is the lowest B attaining the row maximum; the selected set is the first m by
+    (score descending, A index ascending)."""
+    ties = 0
+    for t in taps["chunks"]:
+        if "best_b" not in t:
+            continue
+        A, B = csm.partition(t["L"])
+        S = csm.cosine_matrix(K[t["start"] + A], K[t["start"] + B])
+        for i, b in enumerate(t["best_b"]):
+            assert S[i, b] == S[i].max()
+            assert np.all(S[i, :b] < S[i, b])          # lowest index among maxima
+            assert t["score"][i] == S[i, b]
+            ties += int(np.sum(S[i] == S[i, b]) > 1)
+        sel = t["selected"]
+        if sel.any() and (~sel).any():
+            lo_sel = t["score"][sel].min()
+            hi_uns = t["score"][~sel].max()
+            assert lo_sel >= hi_uns
+            # at an exact tie the lower A index is the selected one
+            for i in np.nonzero(~sel)[0]:
+                if t["score"][i] == lo_sel:
+                    ties += 1
+                    assert np.nonzero(sel & (t["score"] == lo_sel))[0].max() < i
+    return ties
+
+
 def test_match_and_rank_properties():
     rng = np.random.default_rng(5)
     s, n1, n2, c = 2000, 16, 64, 256
     K, V, N = _random_slice(rng, s, 32, rho=0.97)
     K = bf16.round_to_bf16(K)
-    for precision in ("f64", "f32"):
-        _, _, _, _, taps = csm.csm_round_slice(K, V, N, s, n1, n2, c, 0.5, precision=precision)
-        for t in taps["chunks"]:
-            if "best_b" not in t:
-                continue
-            A, B = csm.partition(t["L"])
-            S = csm.cosine_matrix(K[t["start"] + A], K[t["start"] + B], precision)
-            for i, b in enumerate(t["best_b"]):
-                assert S[i, b] == S[i].max()
-                assert np.all(S[i, :b] < S[i, b])          # lowest index among maxima
-                assert t["score"][i] == S[i, b]
-            sel = t["selected"]
-            if sel.any() and (~sel).any():
-                lo_sel = t["score"][sel].min()
-                hi_uns = t["score"][~sel].max()
-                assert lo_sel >= hi_uns
-                # at an exact tie the lower A index is the selected one
-                for i in np.nonzero(~sel)[0]:
-                    if t["score"][i] == lo_sel:
-                        assert np.nonzero(sel & (t["score"] == lo_sel))[0].max() < i
+    _, _, _, _, taps = csm.csm_round_slice(K, V, N, s, n1, n2, c, 0.5)
+    _check_match_and_rank(K, taps)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_planted_exact_ties_follow_the_rules(dt):
+    """Copies of B rows make an A row tie two B rows exactly (the lower B must win); copies
+    of A rows give equal best scores, some straddling the selection cut (the lower A must be
+    selected).  Checked on fp32-valued data (inexact products) and bf16-valued data."""
+    rng = np.random.default_rng(13)
+    s, n1, n2, c = 3000, 16, 64, 128
+    K, V, N = _random_slice(rng, s, 64, rho=0.9)
+    K = K.astype(np.float32).astype(np.float64) if dt == "f32" else bf16.round_to_bf16(K)
+    for start in range(n1, s - n2 - c, c):
+        for _ in range(6):                     # B copies (odd offsets) inside the chunk
+            j, j2 = sorted(rng.choice(c // 2, 2, replace=False))
+            K[start + 2 * j2 + 1] = K[start + 2 * j + 1]
+        for _ in range(6):                     # A copies (even offsets)
+            i, i2 = sorted(rng.choice(c // 2, 2, replace=False))
+            K[start + 2 * i2] = K[start + 2 * i]
+    total = 0
+    for r in (0.5, 0.3, 0.77):
+        _, _, _, _, taps = csm.csm_round_slice(K, V, N, s, n1, n2, c, r)
+        total += _check_match_and_rank(K, taps)
+    assert total > 50
 
 
 def test_centroids_are_means_of_their_members_over_rounds():

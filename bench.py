@@ -125,14 +125,13 @@ def main():
     # serving cache: compressed to the budget by Algorithm 1's prefill rounds (untimed)
     Kd, Vd, Nd, Ld = K0.clone(), V0.clone(), N0.clone(), L0.clone()
     sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
-    ws_c = torch.empty(lib.csm_workspace_bytes(K0, w.n1, w.n2, w.c, max_len=w.ctx),
-                       dtype=torch.uint8, device=dev)
+    ws_c = lib.new_workspace(lib.csm_workspace_bytes(K0, w.n1, w.n2, w.c, max_len=w.ctx), dev)
     s_pre = w.ctx
     for r in sched.prefill_rounds():  # in place: the bound covers the compressed slices only
         lib.csm_compress(Kd, Vd, Nd, Ld, w.n1, w.n2, w.c, r, mask, max_len=s_pre, workspace=ws_c)
         s_pre = round_output_length(s_pre, w.n1, w.n2, w.c, r)
     assert lib.read_error(ws_c) == lib.OK
-    ws_d = torch.empty(lib.decode_workspace_bytes(Kd, w.H_q, w.H_kv), dtype=torch.uint8, device=dev)
+    ws_d = lib.new_workspace(lib.decode_workspace_bytes(Kd, w.H_q, w.H_kv), dev)
     O = torch.empty((w.groups, w.H_q, d), dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
@@ -195,8 +194,8 @@ def main():
     for layer in range(w.layers):
         sl = slice(layer * hk, (layer + 1) * hk)
         layer_views.append((Kd[sl], Vd[sl], Nd[sl], Ld[sl], O[layer:layer + 1]))
-    ws_l = torch.empty(lib.decode_workspace_bytes(layer_views[0][0], w.H_q, w.H_kv, max_len=w.ctx),
-                       dtype=torch.uint8, device=dev)
+    ws_l = lib.new_workspace(lib.decode_workspace_bytes(layer_views[0][0], w.H_q, w.H_kv,
+                                                        max_len=w.ctx), dev)
     q_last = q_all[W + K - 1]
 
     def layer_calls():
@@ -296,8 +295,7 @@ def main():
         ridx = torch.full((S,), len(sched.rounds), dtype=torch.int32, device=dev)
         s_now = int(Ld[int(np.argmin(maskh))].item())
         bound = min(cap, max(thr_v, s_now) + tsteps)
-        ws_t = torch.empty(lib.csm_workspace_bytes(Kd, w.n1, w.n2, w.c, max_len=bound),
-                           dtype=torch.uint8, device=dev)
+        ws_t = lib.new_workspace(lib.csm_workspace_bytes(Kd, w.n1, w.n2, w.c, max_len=bound), dev)
         tq = q_all[0].clone()
         tk = torch.stack([app_k[base + loop_steps + gsteps + 1 + i] for i in range(25)])
         tv = torch.stack([app_v[base + loop_steps + gsteps + 1 + i] for i in range(25)])
@@ -433,8 +431,7 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
     maskh = mask.cpu().numpy()
     S, cap, d = K.shape
     row = 2 * d * K.element_size() + 4
-    ws = torch.empty(lib.csm_workspace_bytes(K, w.n1, w.n2, w.c, max_len=w.ctx), dtype=torch.uint8,
-                     device=dev)
+    ws = lib.new_workspace(lib.csm_workspace_bytes(K, w.n1, w.n2, w.c, max_len=w.ctx), dev)
     if w.R is None:
         rs = [w.r_init]
     else:
@@ -465,7 +462,7 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
            "prefill": {"rounds": len(rounds), "len": s, "ms": sum(x["ms"] for x in rounds),
                        "GBps": sum(n_comp * ((x["s_in"] - w.n1) + (x["s_out"] - w.n1)) * row
                                    for x in rounds) / sum(x["ms"] for x in rounds) / 1e6}}
-    ws_d = torch.empty(lib.decode_workspace_bytes(K, w.H_q, w.H_kv), dtype=torch.uint8, device=dev)
+    ws_d = lib.new_workspace(lib.decode_workspace_bytes(K, w.H_q, w.H_kv), dev)
     q = kvsynth.make_queries(w, dev, steps=min(w.steps, 8))
     O = torch.empty((w.groups, w.H_q, d), dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)

@@ -23,7 +23,12 @@
  *     K and V must be 16-byte aligned.  Rows at or beyond lens[] are ignored.
  *   - Device-side errors (a lens[] entry above max_len or cap) are reported through an
  *     int32 error word in device memory, read with csmkv_read_error().  The affected
- *     slice is left unchanged (compress, append) or produces zeros (attention).
+ *     slice is left unchanged (compress, append) or produces zeros (attention).  The word
+ *     is sticky: kernels only ever set it (to CSMKV_EDEVICE), never clear it, so a loop or a
+ *     graph replay of many calls reports an error from any of them.  It must hold 0 before
+ *     the first call (allocate the workspace zeroed, or call csmkv_clear_error) and is
+ *     cleared only by csmkv_clear_error.
+ *   - Workspaces: apart from that first int32 (the error word), any prior contents.
  *   - Calls that share a workspace must not overlap in time (use one stream).
  */
 #ifndef CSMKV_H
@@ -100,8 +105,8 @@ CSMKV_API size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t 
  *   similarity tile grows to 256 x 256 and the key tile to c * d * 2 bytes of LDS);
  *   0 <= r <= 1 (not NaN); outlier_mask is a device
  *   [num_slices] uint8 array or NULL (no outliers); workspace: device memory of at least
- *   csm_compress_workspace_bytes() bytes, 256-byte aligned.  Its first int32 is the error
- *   word of this call.
+ *   csm_compress_workspace_bytes() bytes, 256-byte aligned.  Its first int32 is the sticky
+ *   error word.
  * Returns CSMKV_OK or a negative csmkv_status.
  */
 CSMKV_API int csm_compress(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
@@ -184,7 +189,8 @@ CSMKV_API size_t decode_attn_logn_workspace_bytes(const csmkv_cache *cache, int3
  * 2^-17 (bf16) or 2^-22 (fp16) relative, summed in fp32; the softmax denominator is summed in
  * fp32 from P itself.
  * H_kv >= 1, H_q a multiple of H_kv with H_q / H_kv in {1, 2, 4, 8};
- * num_slices a multiple of H_kv.  Workspace as for csm_compress (first int32 = error word).
+ * num_slices a multiple of H_kv.  Workspace as for csm_compress (first int32 = sticky error
+ * word).
  */
 CSMKV_API int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t *N,
                      const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
@@ -202,8 +208,13 @@ CSMKV_API int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv
 
 /* Synchronise `stream` and return CSMKV_OK if the device error word is 0, CSMKV_EDEVICE if
  * a kernel set it, or CSMKV_EHIP if the copy failed.  error_word is the first int32 of a
- * workspace or the word given to kv_append. */
+ * workspace or the word given to kv_append.  The word is not changed. */
 CSMKV_API int csmkv_read_error(const int32_t *error_word, void *stream);
+
+/* Enqueue on `stream` a reset of a device error word to 0 (a one-thread kernel, so it can be
+ * captured in a graph).  error_word: device int32, 4-byte aligned.  Returns CSMKV_OK,
+ * CSMKV_EINVAL (NULL or misaligned) or CSMKV_EHIP. */
+CSMKV_API int csmkv_clear_error(int32_t *error_word, void *stream);
 
 #ifdef __cplusplus
 }

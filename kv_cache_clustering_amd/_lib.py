@@ -52,6 +52,7 @@ _SIGS = {
     "decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _sz, _p]),
     "kv_append": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p]),
     "csmkv_read_error": (ctypes.c_int, [_p, _p]),
+    "csmkv_clear_error": (ctypes.c_int, [_p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -116,9 +117,14 @@ def _check_mask(mask, S):
         raise ValueError("outlier_mask must be a contiguous uint8 GPU tensor [num_slices]")
 
 
+def new_workspace(nbytes, device):
+    """A workspace of at least nbytes with its (sticky) error word at 0."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes, device, ws):
     if ws is None:
-        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        return new_workspace(nbytes, device)
     if ws.dtype != torch.uint8 or not ws.is_cuda or ws.numel() < nbytes:
         raise ValueError(f"workspace must be a uint8 GPU tensor of at least {nbytes} bytes")
     return ws
@@ -251,8 +257,14 @@ def kv_append(K, V, N, lens, k_new, v_new, error_word=None):
 
 
 def read_error(word):
-    """Synchronise and read a device error word (first int32 of a workspace, or an append word)."""
+    """Synchronise and read a device error word (first int32 of a workspace, or an append word).
+    The word is sticky: it stays set until clear_error."""
     return _lib.csmkv_read_error(_ptr(word), _stream(word.device))
+
+
+def clear_error(word):
+    """Enqueue a reset of a device error word (first int32 of a workspace, or an append word)."""
+    _raise(_lib.csmkv_clear_error(_ptr(word), _stream(word.device)), "csmkv_clear_error")
 
 
 # Host-only entry points for argument-validation tests (no GPU work is enqueued on errors).

@@ -8,7 +8,7 @@
 // averaging of K and V; degrees accumulate over rounds).
 //
 // Launch structure (all on the caller's stream):
-//   csm_prep   : resets the error word, validates every lens[] entry, decides which
+//   csm_prep   : validates every lens[] entry (a bad one sets the sticky error word), decides which
 //                slices run (all, or those at their trigger threshold) and with which r,
 //                records each slice's input and output length, resets the per-slice
 //                ticket counters and clears the per-chunk "source consumed" flags.
@@ -54,8 +54,6 @@ namespace csmkv {
 
 __global__ void csm_prep(CsmArgs a) {
   if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) *a.err = 0;
-    __syncthreads();
     for (int64_t z = threadIdx.x; z < a.num_slices; z += blockDim.x) {
       const int s = a.lens_in[z];
       const bool outl = a.mask != nullptr && a.mask[z] != 0;

@@ -167,7 +167,7 @@ const char *csmkv_status_string(int status) {
   }
 }
 
-int csmkv_version(void) { return 103; }
+int csmkv_version(void) { return 104; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
   if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 512) return 0;
@@ -285,6 +285,11 @@ int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *ca
   a.rowb = cache->d * elem_bytes(cache->dtype);
   const int e = csmkv::launch_append(a, static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+int csmkv_clear_error(int32_t *error_word, void *stream) {
+  if (error_word == nullptr || !aligned(error_word, 4)) return CSMKV_EINVAL;
+  return csmkv::launch_clear(error_word, static_cast<hipStream_t>(stream)) ? CSMKV_EHIP : CSMKV_OK;
 }
 
 int csmkv_read_error(const int32_t *error_word, void *stream) {

@@ -29,6 +29,7 @@
 
 namespace csmkv {
 
+
 constexpr int kTSplitMin = 512, kTSplitMax = 2048;  // tokens per work item
 constexpr int64_t kItemTarget = 2048;               // work items a call aims for
 // floats per (item, head) partial: (max, sum, 0, 0, o[d]), 16-byte aligned rows
@@ -106,8 +107,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
 __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
   __shared__ int32_t wsum[16];
   const int t = threadIdx.x;
-  if (t == 0) *a.err = 0;
-  __syncthreads();
   const int64_t S = a.num_slices;
   const int64_t per = (S + 1023) / 1024;
   const int64_t z0 = t * per, z1 = min(S, z0 + per);
@@ -483,7 +482,8 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
   int total, ts = a.tsplit;
   if constexpr (INL) {
     // item counts of all slices, scanned into LDS (a bad length counts 0 items).  Workgroup
-    // 0 also stores the offsets for the combine kernel and sets the error word.
+    // 0 also stores the offsets for the combine kernel and, for a bad length, sets the
+    // (sticky) error word.
     const int per = (S + NT - 1) / NT, z0 = t * per, z1 = min(S, z0 + per);
     int sum = 0, bad = 0;
     for (int z = z0; z < z1; ++z) {
@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     }
     if (blockIdx.x == 0 && t == 0) a.item_off[S] = total;
     const int any_bad = __syncthreads_or(bad);
-    if (blockIdx.x == 0 && t == 0) *a.err = any_bad ? kDeviceError : 0;
+    if (blockIdx.x == 0 && t == 0 && any_bad) atomicExch(a.err, kDeviceError);
   } else {
     total = a.item_off[S];
   }
@@ -854,6 +854,15 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppArgs a) {
       atomicExch(a.err, kDeviceError);
     }
   }
+}
+
+// Resets an error word to 0 (a kernel rather than a memset node, so that it can be captured in
+// a graph and replayed).
+__global__ void clear_word_kernel(int32_t *w) { *w = 0; }
+
+int launch_clear(int32_t *word, hipStream_t st) {
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, word);
+  return (int)hipGetLastError();
 }
 
 int launch_append(const AppArgs &a, hipStream_t st) {

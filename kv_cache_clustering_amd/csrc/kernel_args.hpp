@@ -22,7 +22,7 @@ struct CsmArgs {
   int32_t *round_idx;   // [num_slices] rounds run so far; r = max(r_init - j * r_delta, r_min)
   double r_init, r_delta, r_min;
   // workspace
-  int32_t *err;      // device error word of this call
+  int32_t *err;      // sticky device error word (set on a bad length, never cleared here)
   uint32_t *ticket;  // [num_slices] unit ticket counters
   int32_t *s_in;     // [num_slices] validated input length, -1 = skip the slice
   int32_t *s_out;    // [num_slices] output length
@@ -42,7 +42,7 @@ struct DecArgs {
   int32_t max_len, H_q, H_kv;
   int32_t tsplit;     // tokens per work item of the plan kernel (dec_split_tokens)
   float scale_log2;   // log2(e) / sqrt(d)
-  int32_t *err;       // device error word of this call
+  int32_t *err;       // sticky device error word (set on a bad length, never cleared here)
   int32_t *item_off;  // [num_slices + 1] first work item of each slice (plan kernel only)
   int32_t *item_zp;   // [items][4] (slice, first token, end token, 0) of every work item
   int32_t inline_items;  // 1: the split and combine kernels derive the items from lens
@@ -65,6 +65,7 @@ constexpr int kDtypeBf16 = 0, kDtypeF32 = 1, kDtypeF16 = 2;
 int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream);
 int launch_decode(const DecArgs &a, int dtype, int d, int G, int64_t max_items, hipStream_t st);
 int launch_append(const AppArgs &a, hipStream_t st);
+int launch_clear(int32_t *word, hipStream_t st);
 // Tokens per decode work item for a geometry, and the upper bound on work items (sizes the
 // partial buffer).  Both depend only on the slice count and the host-known length bound.
 int32_t dec_split_tokens(int64_t num_slices, int32_t max_len);

@@ -42,10 +42,8 @@ class ClusteredKVCache:
         self.outlier_len = n
         dev = K.device
         cap = K.shape[1]
-        self.ws_csm = torch.empty(lib.csm_workspace_bytes(K, n1, n2, c, max_len=cap),
-                                  dtype=torch.uint8, device=dev)
-        self.ws_dec = torch.empty(lib.decode_workspace_bytes(K, H_q, H_kv, max_len=cap),
-                                  dtype=torch.uint8, device=dev)
+        self.ws_csm = lib.new_workspace(lib.csm_workspace_bytes(K, n1, n2, c, max_len=cap), dev)
+        self.ws_dec = lib.new_workspace(lib.decode_workspace_bytes(K, H_q, H_kv, max_len=cap), dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         groups = K.shape[0] // H_kv
         self.out = torch.empty((groups, H_q, K.shape[2]), dtype=torch.float32, device=dev)
@@ -228,7 +226,8 @@ class ClusteredKVCache:
         return self.loop_out, rounds
 
     def check_errors(self):
-        """Synchronise and raise if a kernel flagged a bad length."""
+        """Synchronise and raise if a kernel flagged a bad length since the cache was built
+        (the error words are sticky)."""
         for word in (self.ws_csm, self.ws_dec, self.err):
             rc = lib.read_error(word)
             if rc != lib.OK:

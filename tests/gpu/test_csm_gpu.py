@@ -405,3 +405,32 @@ def test_seeded_sweep_of_shapes_and_parameters(lib, dev):
         total.add(run_and_compare(lib, dev, K, V, N, L, n1, n2, c, r, mask))
     print(total)
     parity.check_report(total)
+
+
+def test_error_word_is_sticky_until_cleared(lib, dev):
+    """A bad length flagged by one call stays visible after later clean calls on the same
+    workspace (as in a loop or a graph replay of many calls) until csmkv_clear_error; the
+    clear is a kernel, so it can sit inside a captured graph."""
+    lens = [3000, 3000]
+    K, V, N, L = (t.to(dev) for t in host_cache(2, 3100, lens, seed=12))
+    ws = lib.new_workspace(lib.csm_workspace_bytes(K, 16, 64, 256, max_len=3100), dev)
+    L[1] = 3050
+    lib.csm_compress(K, V, N, L, 16, 64, 256, 0.5, max_len=3000, workspace=ws)   # 3050 > 3000
+    L[1] = 2900
+    lib.csm_compress(K, V, N, L, 16, 64, 256, 0.5, max_len=3000, workspace=ws)   # clean
+    assert lib.read_error(ws) == lib.EDEVICE
+    lib.clear_error(ws)
+    assert lib.read_error(ws) == lib.OK
+    # clear + round captured in a graph: each replay starts clean and reports its own status
+    Kg, Vg, Ng, Lg = (t.to(dev) for t in host_cache(2, 3100, lens, seed=13))
+    Lg[0] = 3100
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.clear_error(ws)
+        lib.csm_compress(Kg, Vg, Ng, Lg, 16, 64, 256, 0.0, max_len=3000, workspace=ws)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert lib.read_error(ws) == (lib.EDEVICE if rep == 0 else lib.OK), rep
+        Lg[0] = 2000                       # r = 0 leaves the lengths as they are

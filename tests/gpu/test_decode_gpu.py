@@ -253,17 +253,23 @@ def test_bad_length_gives_zeros_and_error(lib, dev):
     Ld = L.to(dev)
     Ld[1] = 800
     q = torch.randn((2, 1, 128)).to(torch.bfloat16)
-    ws = torch.empty(lib.decode_workspace_bytes(K, 1, 1, max_len=700), dtype=torch.uint8, device=dev)
+    ws = torch.full((lib.decode_workspace_bytes(K, 1, 1, max_len=700),), 0x77, dtype=torch.uint8,
+                    device=dev)
+    lib.clear_error(ws)                       # only the error word must start at 0
     O = lib.decode_attn_logn(q.to(dev), K.to(dev), V.to(dev), N.to(dev), Ld, 1, 1, max_len=700,
                              workspace=ws)
     assert lib.read_error(ws) == lib.EDEVICE
     assert torch.all(O[1] == 0) and torch.any(O[0] != 0)
-    # the error word belongs to one call: the next call on the same workspace is clean
+    # the error word is sticky: a clean call after the bad one leaves it set until cleared
     Kd, Vd, Nd = K.to(dev), V.to(dev), N.to(dev)
     Ld[1] = 650
     O2 = lib.decode_attn_logn(q.to(dev), Kd, Vd, Nd, Ld, 1, 1, max_len=700, workspace=ws)
-    assert lib.read_error(ws) == lib.OK
+    assert lib.read_error(ws) == lib.EDEVICE
     assert torch.equal(O2[0], O[0]) and torch.any(O2[1] != 0)
+    lib.clear_error(ws)
+    O3 = lib.decode_attn_logn(q.to(dev), Kd, Vd, Nd, Ld, 1, 1, max_len=700, workspace=ws)
+    assert lib.read_error(ws) == lib.OK
+    assert torch.equal(O3, O2)
 
 
 def test_item_plan_kernel_and_inline_plan_agree(lib, dev):
@@ -289,6 +295,7 @@ def test_item_plan_kernel_and_inline_plan_agree(lib, dev):
     q = torch.randn((S, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
     ws = torch.full((lib.decode_workspace_bytes(K, H_q, 1, max_len=cap),), 0x5A,
                     dtype=torch.uint8, device=dev)
+    lib.clear_error(ws)
     O_plan = lib.decode_attn_logn(q, K, V, N, L, H_q, 1, max_len=cap, workspace=ws)
     assert lib.read_error(ws) == lib.EDEVICE
     O_inl = torch.empty_like(O_plan)
@@ -296,6 +303,7 @@ def test_item_plan_kernel_and_inline_plan_agree(lib, dev):
     for lo, hi in ((0, half), (half, S)):
         wsh = torch.full((lib.decode_workspace_bytes(K[lo:hi], H_q, 1, max_len=cap),), 0x5A,
                          dtype=torch.uint8, device=dev)
+        lib.clear_error(wsh)
         lib.decode_attn_logn(q[lo:hi], K[lo:hi], V[lo:hi], N[lo:hi], L[lo:hi], H_q, 1,
                              out=O_inl[lo:hi], max_len=cap, workspace=wsh)
         errs.append(lib.read_error(wsh))
@@ -335,6 +343,7 @@ def test_inline_plan_with_more_items_than_workgroups(lib, dev):
     q = torch.randn((S // H_kv, H_q, 128), generator=gen, device=dev).to(torch.bfloat16)
     ws = torch.full((lib.decode_workspace_bytes(K, H_q, H_kv, max_len=cap),), 0x33,
                     dtype=torch.uint8, device=dev)
+    lib.clear_error(ws)
     O = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, max_len=cap, workspace=ws)
     assert lib.read_error(ws) == lib.OK
     O = O.cpu().double().numpy()
@@ -363,6 +372,7 @@ def test_workspace_reused_across_calls_and_geometries(lib, dev):
     L = torch.randint(0, cap + 1, (S,), generator=gen, device=dev, dtype=torch.int32)
     ws = torch.full((lib.decode_workspace_bytes(K, 16, 4, max_len=cap),), 0xA5, dtype=torch.uint8,
                     device=dev)
+    lib.clear_error(ws)
     for call, (n, ml) in enumerate([(64, cap), (8, cap), (64, 3000), (4, 900), (64, cap)]):
         Lc = torch.clamp(L[:n], max=ml)
         q = torch.randn((n // 4, 16, 128), generator=gen, device=dev).to(torch.bfloat16)

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.version() == 103
+    assert lib.version() == 104
     for code in range(-6, 1):
         assert lib.status_string(code).startswith("CSMKV_")
     assert "unknown" in lib.status_string(-99)
@@ -144,6 +144,7 @@ def test_decode_and_append_validation(lib):
     assert app(FAKE, FAKE, FAKE, None, ctypes.byref(d), FAKE, FAKE, None, None) == lib.EINVAL
     assert app(FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc(lib, dtype=3)), FAKE, FAKE, None, None) == lib.EDTYPE
     assert lib.raw.csmkv_read_error(None, None) == lib.EINVAL
+    assert lib.raw.csmkv_clear_error(None, None) == lib.EINVAL
 
 
 def _items_for_lengths(S, max_len, lens):

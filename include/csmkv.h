@@ -196,6 +196,31 @@ CSMKV_API int decode_attn_logn(const void *q, const void *K, const void *V, cons
                      const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
                      float *O, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Size of the fixed device scratch array decode_attn_logn_noalloc works in (per GPU). */
+#define CSMKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * decode_attn_logn_noalloc -- decode_attn_logn for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid allocation.
+ * Same computation, same kernels and bit-identical output; the workspace is replaced by a fixed
+ * scratch array inside the library (CSMKV_DECODE_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends), so this call allocates and frees nothing.  Its first call on a device (with that
+ * device current) looks up that device's array; later calls only launch kernels.
+ * error_word : device int32 owned by the caller (4-byte aligned, not NULL): the sticky error
+ *   word of the call (see the conventions above).
+ * Geometries whose decode_attn_logn_workspace_bytes() exceed CSMKV_DECODE_NOALLOC_SCRATCH_BYTES
+ *   are rejected with CSMKV_EWORKSPACE before anything is enqueued (e.g. 256 slices of up to
+ *   64K tokens at G = 4 need about 18 MB; 8192 slices of 32K tokens at G = 1 do not fit).
+ * Every call on one GPU uses that GPU's single array: calls that may overlap in time on one GPU
+ * (different streams without ordering) race on it and must not be made.  The array keeps the
+ * last call's contents; nothing in it needs to start at zero.
+ * Other arguments, layout and status codes as decode_attn_logn.
+ */
+CSMKV_API int decode_attn_logn_noalloc(const void *q, const void *K, const void *V,
+                                       const int32_t *N, const int32_t *lens,
+                                       const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                                       float *O, int32_t *error_word, void *stream);
+
 /*
  * kv_append -- Algorithm 1 decode update for every slice (Chelsea review, section 三,
  * Algorithm 1: K = [K, k], V = [V, v], N = [N, 1], s = s + 1).

@@ -50,6 +50,7 @@ _SIGS = {
                                               _d, _d, _p, _p, _sz, _p]),
     "decode_attn_logn_workspace_bytes": (_sz, [_desc, _i32, _i32]),
     "decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _sz, _p]),
+    "decode_attn_logn_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _p]),
     "kv_append": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p]),
     "csmkv_read_error": (ctypes.c_int, [_p, _p]),
     "csmkv_clear_error": (ctypes.c_int, [_p, _p]),
@@ -240,6 +241,30 @@ def decode_attn_logn(q, K, V, N, lens, H_q, H_kv, out=None, max_len=None, worksp
     rc = _lib.decode_attn_logn(_ptr(q), _ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc),
                                H_q, H_kv, _ptr(out), _ptr(ws), ws.numel(), _stream(K.device))
     _raise(rc, "decode_attn_logn")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_attn_logn_noalloc(q, K, V, N, lens, H_q, H_kv, out, error_word, max_len=None):
+    """decode_attn_logn without a workspace and without allocating anything: the library's fixed
+    per-GPU scratch array holds the partials.  out (fp32 [groups, H_q, d]) and error_word (int32
+    GPU tensor, sticky) are the caller's.  Calls that overlap on one GPU must not be made."""
+    _check_cache(K, V, N, lens)
+    S, cap, d = K.shape
+    groups = S // H_kv if H_kv > 0 else 0
+    if q.shape != (groups, H_q, d) or q.dtype != K.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
+    if out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [groups, H_q, d]")
+    if error_word.dtype != torch.int32 or not error_word.is_cuda:
+        raise ValueError("error_word must be an int32 GPU tensor")
+    desc = cache_desc(K, max_len)
+    rc = _lib.decode_attn_logn_noalloc(_ptr(q), _ptr(K), _ptr(V), _ptr(N), _ptr(lens),
+                                       ctypes.byref(desc), H_q, H_kv, _ptr(out), _ptr(error_word),
+                                       _stream(K.device))
+    _raise(rc, "decode_attn_logn_noalloc")
     return out
 
 

@@ -264,6 +264,50 @@ int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t 
   return e ? CSMKV_EHIP : CSMKV_OK;
 }
 
+int decode_attn_logn_noalloc(const void *q, const void *K, const void *V, const int32_t *N,
+                             const int32_t *lens, const csmkv_cache *cache, int32_t H_q,
+                             int32_t H_kv, float *O, int32_t *error_word, void *stream) {
+  static_assert(csmkv::kNoAllocScratchBytes == CSMKV_DECODE_NOALLOC_SCRATCH_BYTES,
+                "scratch size in the header and the library agree");
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  rc = check_heads(cache, H_q, H_kv);
+  if (rc) return rc;
+  if (!q || !K || !V || !N || !lens || !O || !error_word) return CSMKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(error_word, 4))
+    return CSMKV_EINVAL;
+  const int G = H_q / H_kv;
+  const DecLayout lay = dec_layout(cache, G);
+  if (lay.total > CSMKV_DECODE_NOALLOC_SCRATCH_BYTES) return CSMKV_EWORKSPACE;
+  const int64_t items = csmkv::dec_max_items(cache->num_slices, cache->max_len);
+  if (items > (int64_t)INT32_MAX / 2) return CSMKV_EUNSUPPORTED;
+  if (cache->num_slices == 0) return CSMKV_OK;
+  void *scr = nullptr;
+  if (csmkv::noalloc_scratch(&scr) != 0) return CSMKV_EHIP;
+  char *w = static_cast<char *>(scr);
+  csmkv::DecArgs a;
+  a.q = static_cast<const char *>(q);
+  a.K = static_cast<const char *>(K);
+  a.V = static_cast<const char *>(V);
+  a.N = N;
+  a.lens = lens;
+  a.O = O;
+  a.num_slices = cache->num_slices;
+  a.cap = cache->cap;
+  a.max_len = cache->max_len;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.tsplit = csmkv::dec_split_tokens(cache->num_slices, cache->max_len);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cache->d));
+  a.err = error_word;
+  a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
+  a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
+  a.part = reinterpret_cast<float *>(w + lay.part);
+  const int e = csmkv::launch_decode(a, cache->dtype, cache->d, G, items,
+                                     static_cast<hipStream_t>(stream));
+  return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
 int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
               const void *k_new, const void *v_new, int32_t *error_word, void *stream) {
   int rc = check_cache(cache);

@@ -23,12 +23,18 @@
 //                 log-sum-exp (a running maximum per thread over item groups in parallel,
 //                 then the groups merged against their common maximum).
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.hpp"
 #include "kernel_args.hpp"
 
 namespace csmkv {
 
+// Scratch memory of the allocation-free decode entry point: what a caller's workspace holds
+// for decode_attn_logn (item offsets, item table, per-item partials), in one fixed array.
+// Each GPU the library runs on holds its own copy until the process ends; host code reaches
+// it only through the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 constexpr int kTSplitMin = 512, kTSplitMax = 2048;  // tokens per work item
 constexpr int64_t kItemTarget = 2048;               // work items a call aims for
@@ -808,6 +814,25 @@ int64_t dec_max_items(int64_t num_slices, int32_t max_len) {
   if (dec_inline(num_slices, max_len)) return dec_inline_items(num_slices, max_len);
   const int32_t ts = dec_split_tokens(num_slices, max_len);
   return num_slices * (int64_t)((max_len + ts - 1) / ts);
+}
+
+int noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_items, hipStream_t st) {

@@ -58,6 +58,9 @@ struct AppArgs {
   int32_t rowb;
 };
 
+// Bytes of the fixed device scratch array behind decode_attn_logn_noalloc (one per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
 // Storage codes of the C ABI (csmkv_dtype).
 constexpr int kDtypeBf16 = 0, kDtypeF32 = 1, kDtypeF16 = 2;
 
@@ -70,5 +73,8 @@ int launch_clear(int32_t *word, hipStream_t st);
 // partial buffer).  Both depend only on the slice count and the host-known length bound.
 int32_t dec_split_tokens(int64_t num_slices, int32_t max_len);
 int64_t dec_max_items(int64_t num_slices, int32_t max_len);
+// Device address of this GPU's scratch array (the current device's), looked up once per
+// device; 0 or a hipError_t value.
+int noalloc_scratch(void **ptr);
 
 }  // namespace csmkv

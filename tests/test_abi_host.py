@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -145,6 +145,20 @@ def test_decode_and_append_validation(lib):
     assert app(FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc(lib, dtype=3)), FAKE, FAKE, None, None) == lib.EDTYPE
     assert lib.raw.csmkv_read_error(None, None) == lib.EINVAL
     assert lib.raw.csmkv_clear_error(None, None) == lib.EINVAL
+
+
+def test_noalloc_decode_validation(lib):
+    """The allocation-free decode rejects a missing error word and any geometry whose partials
+    would not fit its fixed scratch array, before touching the GPU."""
+    noa = lib.raw.decode_attn_logn_noalloc
+    d = _desc(lib, S=256, cap=65792, max_len=65792)            # 64K workload, G = 4: fits
+    assert lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(d), 32, 8) <= lib.NOALLOC_SCRATCH_BYTES
+    assert noa(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 32, 8, FAKE, None, None) == lib.EINVAL
+    assert noa(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 6, 4, FAKE, FAKE, None) == lib.EINVAL
+    big = _desc(lib, S=8192, cap=32896, max_len=32896)          # 8192 slices of 32K, G = 1
+    assert lib.raw.decode_attn_logn_workspace_bytes(ctypes.byref(big), 32, 32) > lib.NOALLOC_SCRATCH_BYTES
+    assert noa(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(big), 32, 32, FAKE, FAKE, None) == lib.EWORKSPACE
+    assert lib.raw.csmkv_clear_error(ctypes.c_void_p(FAKE.value + 2), None) == lib.EINVAL
 
 
 def _items_for_lengths(S, max_len, lens):

@@ -5,15 +5,18 @@ bf16, batch 1, 65536-token context, 4% of (layer, kv-head) slices flagged outlie
 AR(1) with rho ~ U[0.8, 0.99] per head, values N(0, 1), queries N(0, 1).
 
 One step = one pass of the whole hot path:
-  1. csm_compress_into: one CSM round (r = 0.5, c = 256, n1 = 16, n2 = 64) over the
-     pristine 64K cache, written to a second cache (the prefill -> serving-cache round);
+  1. csm_compress: one CSM round (r = 0.5, c = 256, n1 = 16, n2 = 64) in place over the
+     64K cache (its input is restored from a pristine copy and the 256 MB last-level cache is
+     flushed before every step, outside the round's timed events);
   2. kv_append: one decode token appended to every slice of the serving cache, which was
      compressed beforehand (untimed) to the 20% budget by the annealed Algorithm 1 rounds;
   3. decode_attn_logn: GQA log-N attention for all 32 query heads of all 32 layers.
 Inputs are resident in HBM before timing.  `value` is the CSM round's throughput in
-slice-tokens/s (input tokens of the compressed slices per second of the csm call, timed
-with HIP events on the stream the library launches on); the decode figures are reported
-beside it.  Roofline: algorithmic bytes (what the round must read and write) / duration.
+slice-tokens/s (input tokens of the compressed slices per second of the csm_compress call,
+timed with HIP events on the stream the library launches on); the decode figures are
+reported beside it.  Roofline: algorithmic bytes (what the round must read and write: every
+compressed slice reads its rows after the sinks once and writes its kept rows once; outlier
+slices are not touched) / duration.
 """
 
 import argparse
@@ -69,17 +72,19 @@ def recorded_traffic(key, sources):
     return rec["traffic_bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
-def csm_bytes(lens_in, lens_out, mask, n1, out_of_place):
-    """Algorithmic HBM bytes of one round: every compressed slice reads its rows once and
-    writes its kept rows once; out of place, protected rows and outlier slices are copied."""
+def csm_bytes(lens_in, lens_out, mask, n1):
+    """Algorithmic HBM bytes of one round: every compressed slice reads its rows after the n1
+    sinks once and writes its kept rows once; outlier slices are not read or written."""
+    return sum(((s - n1) + (s2 - n1)) * ROW_BYTES
+               for s, s2, m in zip(lens_in, lens_out, mask) if not m)
+
+
+def csm_copy_bytes(lens_in, lens_out, mask):
+    """Bytes the out-of-place round moves besides the algorithmic ones: the sink rows of every
+    compressed slice (read and written) and whole outlier slices (read and written)."""
     total = 0
     for s, s2, m in zip(lens_in, lens_out, mask):
-        if m:
-            total += 2 * s * ROW_BYTES if out_of_place else 0
-        elif out_of_place:
-            total += (s + s2) * ROW_BYTES
-        else:
-            total += ((s - n1) + (s2 - n1)) * ROW_BYTES
+        total += 2 * s * ROW_BYTES if m else 0
     return total
 
 
@@ -119,9 +124,9 @@ def main():
     q_all = kvsynth.make_queries(w, dev, steps=K + W)
     S, cap, d = K0.shape
     maskh = mask.cpu().numpy()
-    # output cache of the timed round
-    Kw, Vw = torch.empty_like(K0), torch.empty_like(V0)
-    Nw, Lw = torch.empty_like(N0), torch.empty_like(L0)
+    # the timed round works in place on a copy restored from the pristine cache every step
+    Ki, Vi, Ni, Li = (torch.empty_like(t) for t in (K0, V0, N0, L0))
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     # serving cache: compressed to the budget by Algorithm 1's prefill rounds (untimed)
     Kd, Vd, Nd, Ld = K0.clone(), V0.clone(), N0.clone(), L0.clone()
     sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
@@ -136,22 +141,36 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
+    stream = torch.cuda.current_stream(dev)
+    # auxiliary: the decode-time round of Algorithm 1 (step 110 of this workload: the serving
+    # cache, 13081 tokens after the prefill rounds, reaches B + g after 110 appended tokens and
+    # one round at r = 0.1 runs), in place, input restored and cache flushed before each rep;
+    # measured on a copy of the serving cache before the timed steps append to it
+    trig = trigger_round(lib, w, sched, Kd, Vd, Nd, Ld, app_k, app_v, mask, maskh, flush, stream,
+                         dev)
 
     r0 = w.r_init
     s_out = round_output_length(w.ctx, w.n1, w.n2, w.c, r0)
     lens_in = [w.ctx] * S
     lens_out = [w.ctx if m else s_out for m in maskh]
-    csm_alg = csm_bytes(lens_in, lens_out, maskh, w.n1, out_of_place=True)
+    csm_alg = csm_bytes(lens_in, lens_out, maskh, w.n1)
     slice_tokens = int(sum(w.ctx for m in maskh if not m))
 
-    stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
 
+    def restore(i):
+        """The round's input back to the pristine cache, then the last-level cache flushed."""
+        Ki.copy_(K0)
+        Vi.copy_(V0)
+        Ni.copy_(N0)
+        Li.copy_(L0)
+        flush.fill_(i & 0xFF)
+
     def step(i, evs=None):
+        restore(i)
         if evs:
             evs[0].record(stream)
-        lib.csm_compress_into(K0, V0, N0, L0, Kw, Vw, Nw, Lw, w.n1, w.n2, w.c, r0, mask,
-                              max_len=w.ctx, workspace=ws_c)
+        lib.csm_compress(Ki, Vi, Ni, Li, w.n1, w.n2, w.c, r0, mask, max_len=w.ctx, workspace=ws_c)
         if evs:
             evs[1].record(stream)
         lib.kv_append(Kd, Vd, Nd, Ld, app_k[i], app_v[i], err)
@@ -182,7 +201,7 @@ def main():
     lens_d = Ld.cpu().numpy()
     dec_lens_mid = lens_d - (K // 2)  # lengths grow by one per step; use the mid-run length
     dec_alg = int(dec_lens_mid.sum()) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
-    assert np.all(Lw.cpu().numpy() == np.array(lens_out))
+    assert np.all(Li.cpu().numpy() == np.array(lens_out))
 
     csm_gbps = csm_alg / (csm_avg * 1e-3) / 1e9
     dec_gbps = dec_alg / (dec_avg * 1e-3) / 1e9
@@ -194,14 +213,17 @@ def main():
     for layer in range(w.layers):
         sl = slice(layer * hk, (layer + 1) * hk)
         layer_views.append((Kd[sl], Vd[sl], Nd[sl], Ld[sl], O[layer:layer + 1]))
+    # host-known bound on every length: the outlier slices are never compressed and have grown
+    # by one token per step
+    dec_bound = w.ctx + W + K
     ws_l = lib.new_workspace(lib.decode_workspace_bytes(layer_views[0][0], w.H_q, w.H_kv,
-                                                        max_len=w.ctx), dev)
+                                                        max_len=dec_bound), dev)
     q_last = q_all[W + K - 1]
 
     def layer_calls():
         for layer, (Kl, Vl, Nl, Ll, Ol) in enumerate(layer_views):
             lib.decode_attn_logn(q_last[layer:layer + 1], Kl, Vl, Nl, Ll, w.H_q, w.H_kv, out=Ol,
-                                 max_len=w.ctx, workspace=ws_l)
+                                 max_len=dec_bound, workspace=ws_l)
 
     layer_calls()
     torch.cuda.synchronize()
@@ -240,35 +262,45 @@ def main():
     del layer_graph
     dec_alg_now = int(Ld.cpu().numpy().sum()) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
 
-    # auxiliary: the in-place round.  Before each rep the input is restored and the 256 MB
-    # last-level cache (MALL) is flushed by writing a 512 MB buffer, both untimed.
-    Ki, Vi, Ni, Li = torch.empty_like(K0), torch.empty_like(V0), torch.empty_like(N0), torch.empty_like(L0)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    inplace_ms = []
+    # auxiliary: the out-of-place round (csm_compress_into, pristine cache -> a second cache).
+    # Its algorithmic bytes are the in-place round's; it also copies the sinks of every slice and
+    # the whole outlier slices, reported apart.
+    Kw, Vw, Nw, Lw = (torch.empty_like(t) for t in (K0, V0, N0, L0))
+    oop_ms = []
     for rep in range(5):
-        Ki.copy_(K0); Vi.copy_(V0); Ni.copy_(N0); Li.copy_(L0)
         flush.fill_(rep & 0xFF)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        lib.csm_compress(Ki, Vi, Ni, Li, w.n1, w.n2, w.c, r0, mask, max_len=w.ctx, workspace=ws_c)
+        lib.csm_compress_into(K0, V0, N0, L0, Kw, Vw, Nw, Lw, w.n1, w.n2, w.c, r0, mask,
+                              max_len=w.ctx, workspace=ws_c)
         e1.record(stream)
         torch.cuda.synchronize()
-        inplace_ms.append(e0.elapsed_time(e1))
-    assert torch.equal(Li, Lw)
-    inplace_alg = csm_bytes(lens_in, lens_out, maskh, w.n1, out_of_place=False)
-    inplace_avg = sum(inplace_ms) / len(inplace_ms)
-    del Ki, Vi, Ni, Li, flush
+        oop_ms.append(e0.elapsed_time(e1))
+    assert lib.read_error(ws_c) == lib.OK
+    assert torch.equal(Lw, Li)
+    oop_avg = sum(oop_ms) / len(oop_ms)
+    oop_copy = csm_copy_bytes(lens_in, lens_out, maskh) + 2 * w.n1 * ROW_BYTES * int((maskh == 0).sum())
+    del Kw, Vw, Nw, Lw
 
-    # decode loop wall time per step: eager calls vs one HIP graph replay per step
+    # decode as the serving loop runs it (append + attention, step after step): wall time per
+    # step, and HIP events around every attention call (its steady-state time, not preceded by
+    # a 64K round as in the timed step)
     loop_steps = min(50, w.steps - K - W - 1)
     base = W + K
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(loop_steps)]
     t0 = time.perf_counter()
     for i in range(loop_steps):
         lib.kv_append(Kd, Vd, Nd, Ld, app_k[base + i], app_v[base + i], err)
+        lev[i][0].record(stream)
         lib.decode_attn_logn(q_all[i % (K + W)], Kd, Vd, Nd, Ld, w.H_q, w.H_kv, out=O,
                              max_len=cap, workspace=ws_d)
+        lev[i][1].record(stream)
     torch.cuda.synchronize()
     eager_us = (time.perf_counter() - t0) * 1e6 / loop_steps
+    steady_ms = [a.elapsed_time(b) for a, b in lev[1:]]
+    steady_avg = sum(steady_ms) / len(steady_ms)
+    steady_alg = int(Ld.cpu().numpy().sum() - loop_steps // 2 * S) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
     q_in, k_in, v_in = q_all[0].clone(), app_k[0].clone(), app_v[0].clone()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -342,7 +374,7 @@ def main():
     others = []
     wl = [x.strip() for x in args.workloads.split(",") if x.strip()]
     if wl:
-        del K0, V0, N0, Kw, Vw, Nw, Kd, Vd, Nd, app_k, app_v, c
+        del K0, V0, N0, Ki, Vi, Ni, Kd, Vd, Nd, app_k, app_v, c, flush
         torch.cuda.empty_cache()
         for spec in wl:  # "<id>[:<dtype>][:d<head dim>][:c<chunk>][:g<q heads per kv head>]"
             cid, *mods = spec.split(":")
@@ -357,6 +389,8 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": ms_per_step,
+        "ms_per_step_includes": "per step: restore of the round's 8.6 GB input and a 512 MB "
+                                "cache flush (untimed by the events), the round, append, decode",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -367,17 +401,32 @@ def main():
                    "outlier_slices": int(maskh.sum()), "c": w.c, "n1": w.n1, "n2": w.n2,
                    "r": r0, "round_out_len": s_out, "budget": sched.budget,
                    "decode_len": int(sched.s), "prefill_rounds": len(sched.rounds)},
-        "csm": {"ms": csm_avg, "median_ms": csm_med, "min_ms": min(csm_ms),
+        "csm": {"call": "csm_compress (in place; input restored and last-level cache flushed "
+                        "before each step, outside the events)",
+                "ms": csm_avg, "median_ms": csm_med, "min_ms": min(csm_ms),
                 "alg_bytes": csm_alg, "GBps": csm_gbps, "frac": csm_gbps / PEAK_GBPS,
                 "slice_tokens": slice_tokens,
                 "model_tokens_per_s": w.ctx / (csm_avg * 1e-3),
                 "whole_step_slice_tokens_per_s": slice_tokens / (ms_per_step * 1e-3),
-                "in_place_ms": inplace_avg, "in_place_median_ms": median(inplace_ms),
-                "in_place_min_ms": min(inplace_ms), "in_place_alg_bytes": inplace_alg,
-                "in_place_GBps": inplace_alg / (inplace_avg * 1e-3) / 1e9},
-        "decode_attn": {"us": dec_avg * 1e3, "median_us": dec_med * 1e3,
-                        "min_us": min(dec_ms) * 1e3, "alg_bytes": dec_alg, "GBps": dec_gbps,
-                        "frac": dec_gbps / PEAK_GBPS, "layers": w.layers,
+                "out_of_place": {"call": "csm_compress_into", "ms": oop_avg,
+                                 "median_ms": median(oop_ms), "min_ms": min(oop_ms),
+                                 "alg_bytes": csm_alg,
+                                 "GBps": csm_alg / (oop_avg * 1e-3) / 1e9,
+                                 "frac": csm_alg / (oop_avg * 1e-3) / 1e9 / PEAK_GBPS,
+                                 "copy_bytes": oop_copy,
+                                 "GBps_with_copies": (csm_alg + oop_copy) / (oop_avg * 1e-3) / 1e9},
+                "trigger_round": trig},
+        "decode_attn": {"us": steady_avg * 1e3, "median_us": median(steady_ms) * 1e3,
+                        "min_us": min(steady_ms) * 1e3, "alg_bytes": steady_alg,
+                        "GBps": steady_alg / (steady_avg * 1e-3) / 1e9,
+                        "timing": "events around each call of a run of append + attention "
+                                  f"steps ({len(steady_ms)} timed)",
+                        "in_step": {"us": dec_avg * 1e3, "median_us": dec_med * 1e3,
+                                    "min_us": min(dec_ms) * 1e3, "alg_bytes": dec_alg,
+                                    "GBps": dec_gbps, "frac": dec_gbps / PEAK_GBPS,
+                                    "note": "the step's own call, right after the 64K round"},
+                        "frac": steady_alg / (steady_avg * 1e-3) / 1e9 / PEAK_GBPS,
+                        "layers": w.layers,
                         "per_layer_calls": {
                             "calls": w.layers, "median_us": median(layer_ms) * 1e3,
                             "min_us": min(layer_ms) * 1e3, "alg_bytes": dec_alg_now,
@@ -393,7 +442,7 @@ def main():
                                          "device_trigger_steps": tsteps,
                                          "device_trigger_rounds_fired": trig_rounds},
         "hbm_copy_GBps": copy_gbps,
-        "roofline": {"bound": "hbm", "kernel": "csm_round<bf16> (csm_compress_into)",
+        "roofline": {"bound": "hbm", "kernel": "csm_round_bf16 (csm_compress, in place)",
                      "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": csm_gbps / PEAK_GBPS,
                      "traffic": recorded_traffic("csm_round_bf16", CSM_SOURCES)},
@@ -402,6 +451,57 @@ def main():
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
+
+
+def trigger_round(lib, w, sched, Kd, Vd, Nd, Ld, app_k, app_v, mask, maskh, flush, stream, dev):
+    """Time the first decode-time round of Algorithm 1 on this workload by itself: a copy of the
+    serving cache gets appended tokens until the compressed slices reach B + g, then the round
+    runs in place at the schedule's r (input restored and cache flushed before each rep)."""
+    import math
+
+    import torch
+
+    from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
+    probe = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
+    probe.prefill_rounds()
+    steps = 0
+    while not probe.over_budget():
+        probe.append()
+        steps += 1
+    j = len(probe.rounds)
+    r = probe.next_round(steps)
+    s_in, s_out = probe.rounds[-1][2], probe.rounds[-1][3]
+    Kt, Vt, Nt, Lt = Kd.clone(), Vd.clone(), Nd.clone(), Ld.clone()
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for i in range(steps):
+        lib.kv_append(Kt, Vt, Nt, Lt, app_k[i], app_v[i], err)
+    Kr, Vr, Nr, Lr = Kt.clone(), Vt.clone(), Nt.clone(), Lt.clone()
+    ws = lib.new_workspace(lib.csm_workspace_bytes(Kt, w.n1, w.n2, w.c, max_len=s_in), dev)
+    ms = []
+    for rep in range(5):
+        Kr.copy_(Kt)
+        Vr.copy_(Vt)
+        Nr.copy_(Nt)
+        Lr.copy_(Lt)
+        flush.fill_(rep & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.csm_compress(Kr, Vr, Nr, Lr, w.n1, w.n2, w.c, r, mask, max_len=s_in, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    assert lib.read_error(ws) == lib.OK and lib.read_error(err) == lib.OK
+    comp = int((maskh == 0).sum())
+    assert int(Lr[int(maskh.argmin())]) == s_out == round_output_length(s_in, w.n1, w.n2, w.c, r)
+    alg = comp * ((s_in - w.n1) + (s_out - w.n1)) * ROW_BYTES
+    avg = sum(ms) / len(ms)
+    del Kt, Vt, Nt, Lt, Kr, Vr, Nr, Lr
+    torch.cuda.empty_cache()
+    return {"decode_step": steps, "round_index": j, "r": r, "s_in": s_in, "s_out": s_out,
+            "threshold": math.ceil(sched.budget + sched.g), "ms": avg, "median_ms": median(ms),
+            "min_ms": min(ms), "alg_bytes": alg, "GBps": alg / (avg * 1e-3) / 1e9,
+            "frac": alg / (avg * 1e-3) / 1e9 / PEAK_GBPS,
+            "slice_tokens_per_s": comp * s_in / (avg * 1e-3)}
 
 
 def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
@@ -592,8 +692,10 @@ def cpu_baseline(w, nslices):
             "kind": "oracle",
             "sample": f"CSM round on {len(csm_zs)} of {len(comp)} compressible {w.ctx // 1024}K slices and a "
                       f"decode step over all {w.slices} slices at the serving lengths (fp64 "
-                      f"numpy, {cores} worker processes, one thread each; slices generated on "
-                      f"the host with the workload's seeds and recipe)",
+                      f"numpy, {cores} worker processes (one per host core, at most 16), one "
+                      f"thread each; slices drawn on the host from the workload's seeds and "
+                      f"recipe, so the same distribution but not the device's bits; the decode "
+                      f"leg attends with every degree 1)",
             "csm_s": t_csm, "decode_us_per_step": t_dec * 1e6,
             "host_cpus": len(os.sched_getaffinity(0))}
 

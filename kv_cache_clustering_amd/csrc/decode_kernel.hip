@@ -368,21 +368,18 @@ __device__ __forceinline__ void mf_compute(const MfStage<D> &st, const u32x4 *qo
                                            f32x4 *o, char *kt, char *vt, int l) {
   constexpr int NR = D / 32, KK = D / 32, EB = D / 16, ST = mf_stride<D>(), LPR = D / 8;
   const int g = l >> 4, c = l & 15;
-  // the sub-block's rows into LDS as loaded (row l / LPR + 512 / D * i, segment l mod LPR),
-  // 8 bytes at a time (the padded rows are 8-byte aligned)
+  // the sub-block's K rows into LDS as loaded (row l / LPR + 512 / D * i, segment l mod LPR),
+  // 8 bytes at a time (the padded rows are 8-byte aligned).  The staged rows are read by other
+  // lanes of the wave: each fence keeps a tile's writes before its reads (and the one at the end
+  // keeps this sub-block's reads before the next one's writes); a wave's LDS accesses then
+  // execute in that order, so no barrier or wait is needed.
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const int off = (l / LPR + (512 / D) * i) * ST + 16 * (l % LPR);
-    uint2 *dk = reinterpret_cast<uint2 *>(kt + off);
-    uint2 *dv = reinterpret_cast<uint2 *>(vt + off);
+    uint2 *dk = reinterpret_cast<uint2 *>(kt + (l / LPR + (512 / D) * i) * ST + 16 * (l % LPR));
     dk[0] = make_uint2(st.k[i][0], st.k[i][1]);
     dk[1] = make_uint2(st.k[i][2], st.k[i][3]);
-    dv[0] = make_uint2(st.v[i][0], st.v[i][1]);
-    dv[1] = make_uint2(st.v[i][2], st.v[i][3]);
   }
-  // The staged rows are read by other lanes of the wave.  These writes, the reads below and the
-  // next sub-block's writes go through the same pointers and may alias, so they keep their
-  // program order, and a wave's LDS accesses execute in that order: no barrier is needed.
+  wave_lds_order();
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
@@ -396,6 +393,14 @@ __device__ __forceinline__ void mf_compute(const MfStage<D> &st, const u32x4 *qo
       sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kw),
                                                   __builtin_bit_cast(f16x8, qop[kk]), sc, 0, 0, 0);
   }
+  // the V rows into their tile while the score MFMAs run
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    uint2 *dv = reinterpret_cast<uint2 *>(vt + (l / LPR + (512 / D) * i) * ST + 16 * (l % LPR));
+    dv[0] = make_uint2(st.v[i][0], st.v[i][1]);
+    dv[1] = make_uint2(st.v[i][2], st.v[i][3]);
+  }
+  wave_lds_order();
   // scores: a row past the range has N = 0 (range-checked load), so log2 N = -inf drops it
   float z[4], mx = -__builtin_inff();
 #pragma unroll
@@ -447,6 +452,7 @@ __device__ __forceinline__ void mf_compute(const MfStage<D> &st, const u32x4 *qo
       o[eb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vop, o[eb], 0, 0, 0);
     }
   }
+  wave_lds_order();  // every read of this sub-block's tiles before the next one's writes
 }
 
 // G = 8 splits the heads into two sets (0-3 and 4-7), each served by its own workgroup, so that

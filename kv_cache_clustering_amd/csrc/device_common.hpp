@@ -80,6 +80,12 @@ __device__ __forceinline__ float lanes_sum(float x) {
 
 __device__ __forceinline__ void wait_vm_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Orders this wave's LDS accesses before and after it for the compiler (acquire-release fence at
+// wavefront scope: no instruction and no wait is emitted, since a wave's LDS operations execute in
+// program order, but no load or store is moved across it).  Used where lanes of one wave read what
+// other lanes of it wrote.
+__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Number of set bits of `mask` below this lane.

@@ -147,11 +147,31 @@ class ClusteredKVCache:
             self.round_idx = torch.full((S,), self.sched.j, dtype=torch.int32, device=dev)
         return self.thr, self.round_idx
 
-    def _triggered_round(self, max_len):
+    def _triggered_round(self, max_len, observe=True):
+        """One csm_compress_triggered call: every slice at its threshold runs a round with its
+        own annealed r.  An observer with before_device_round(cache) / after_device_round(cache)
+        sees the cache around the call (not while a graph is being captured)."""
         thr, idx = self._device_schedule()
+        obs = self.observer if observe and hasattr(self.observer, "before_device_round") else None
+        if obs is not None:
+            obs.before_device_round(self)
         lib.csm_compress_triggered(self.K, self.V, self.N, self.lens, thr, idx, self.n1, self.n2,
                                    self.c, self.sched.r_init, self.sched.delta, self.sched.r_min,
                                    self.mask, max_len=max_len, workspace=self.ws_csm)
+        if obs is not None:
+            obs.after_device_round(self)
+
+    def prefill_device(self):
+        """prefill with the trigger and r decided on the device: one triggered call for each
+        round the host bookkeeping predicts (each slice runs when its length is at the threshold,
+        with r from its own round counter).  Returns the r the host expects of each round."""
+        self._device_schedule()  # the device's round counters start at the rounds run so far
+        rs = []
+        while self.sched.over_budget():
+            s_before = self.sched.s
+            rs.append(self.sched.next_round(0))
+            self._triggered_round(s_before)
+        return rs
 
     def _host_step(self):
         """Advance the host bookkeeping by one decode step (append, then the trigger)."""
@@ -205,7 +225,7 @@ class ClusteredKVCache:
                 lib.decode_attn_logn(self.loop_q[i], self.K, self.V, self.N, self.lens, self.H_q,
                                      self.H_kv, out=self.loop_out[i], max_len=cap,
                                      workspace=self.ws_dec)
-                self._triggered_round(round_bound)
+                self._triggered_round(round_bound, observe=False)
         self.loop_graph = graph
         self.loop_steps = steps
 

@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=246,
                     help="compressible slices the oracle baseline clusters (all 246 by default)")
+    ap.add_argument("--offload-slices", type=int, default=32,
+                    help="compressible slices the CPU-offloaded round is timed on")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--workloads", default="1,2,3,5,4:f16,4:d64,4:c512,4:g8",
@@ -148,6 +150,9 @@ def main():
     # measured on a copy of the serving cache before the timed steps append to it
     trig = trigger_round(lib, w, sched, Kd, Vd, Nd, Ld, app_k, app_v, mask, maskh, flush, stream,
                          dev)
+    # the CPU-offloaded variant: the same round on the host's cores over a host copy of a sample
+    # of the slices, and the upload of its result
+    offload = host_offload(lib, w, K0, V0, N0, L0, maskh, stream, dev, args.offload_slices)
 
     r0 = w.r_init
     s_out = round_output_length(w.ctx, w.n1, w.n2, w.c, r0)
@@ -446,11 +451,51 @@ def main():
                      "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": csm_gbps / PEAK_GBPS,
                      "traffic": recorded_traffic("csm_round_bf16", CSM_SOURCES)},
+        "cpu_offload": offload,
         "cpu_baseline": cpu,
         "workloads": others,
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
+
+
+def host_offload(lib, w, K0, V0, N0, L0, maskh, stream, dev, nslices):
+    """The CPU-offloaded round (csm_compress_host) on `nslices` compressible slices of the workload
+    copied to pinned host memory, one host thread per core, then csm_upload_rows of its result
+    (rows from n1 on, and the lengths) into a device cache of those slices, timed with events."""
+    import torch
+
+    comp = [int(z) for z in range(len(maskh)) if not maskh[z]]
+    zs = comp[:: max(1, len(comp) // nslices)][:nslices]
+    Kh, Vh, Nh, Lh = (torch.empty((len(zs),) + tuple(t.shape[1:]), dtype=t.dtype, pin_memory=True)
+                      for t in (K0, V0, N0, L0))
+    for h, t in ((Kh, K0), (Vh, V0), (Nh, N0), (Lh, L0)):
+        h.copy_(t[zs])
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    lib.csm_compress_host(Kh, Vh, Nh, Lh, w.n1, w.n2, w.c, w.r_init, threads=threads)
+    round_s = time.perf_counter() - t0
+    Kd, Vd, Nd, Ld = (t[zs].clone() for t in (K0, V0, N0, L0))
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.csm_upload_rows(Kh, Vh, Nh, Lh, Kd, Vd, Nd, Ld, row_begin=w.n1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    assert torch.equal(Ld.cpu(), Lh)
+    up_bytes = int(sum(int(s) - w.n1 for s in Lh)) * ROW_BYTES + 4 * len(zs)
+    rate = len(zs) * w.ctx / round_s
+    del Kh, Vh, Nh, Lh, Kd, Vd, Nd, Ld
+    torch.cuda.empty_cache()
+    return {"call": "csm_compress_host + csm_upload_rows", "isa": lib.host_isa(),
+            "threads": threads, "slices": len(zs), "round_s": round_s,
+            "slice_tokens_per_s": rate,
+            "round_s_all_compressible_slices": len(comp) * w.ctx / rate,
+            "upload_ms": min(ms), "upload_bytes": up_bytes,
+            "upload_GBps": up_bytes / (min(ms) * 1e-3) / 1e9}
 
 
 def trigger_round(lib, w, sched, Kd, Vd, Nd, Ld, app_k, app_v, mask, maskh, flush, stream, dev):

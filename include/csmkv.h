@@ -231,6 +231,52 @@ CSMKV_API int decode_attn_logn_noalloc(const void *q, const void *K, const void 
 CSMKV_API int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
               const void *k_new, const void *v_new, int32_t *error_word, void *stream);
 
+/* ---------------------------------------------------------------- CPU-offloaded clustering
+ * CentroidKV page, 它做不到的事（局限性） → 仍留在 GPU 上 and 技术摘要 → 作者注明的局限性: the
+ * grouping could run on the CPU with only its result sent to the GPU.  These two entry points do
+ * that: a CSM round over a cache held in HOST memory, on the host's cores, and an asynchronous
+ * copy of the compacted rows into the device cache.
+ */
+
+/* Vector unit csm_compress_host uses on this CPU (chosen at run time). */
+#define CSMKV_HOST_ISA_SCALAR 0
+#define CSMKV_HOST_ISA_AVX2 1   /* AVX2 + FMA */
+#define CSMKV_HOST_ISA_AVX512 2 /* AVX-512F */
+CSMKV_API int csm_host_isa(void);
+
+/*
+ * csm_compress_host -- csm_compress's round (same arguments, rules and readings) on a cache in
+ * HOST memory, in place, on num_threads host threads (0 = one per hardware thread), one slice per
+ * thread at a time.  K, V, N, lens and outlier_mask (NULL = none) are host pointers in the device
+ * layout.  Similarities in fp32 (exact bf16 / fp16 products), merges accumulated in fp32 and
+ * rounded to nearest even, like the device round; results agree with it up to near-ties.
+ * Optional host taps as csm_compress_debug (best_b and selected both or neither; units from
+ * cache->max_len, which must then bound every slice that runs; src_pos [num_slices][cap]).
+ * Every lens[] entry is checked against cap first: CSMKV_EINVAL and nothing changed if one is
+ * out of range.  Blocks until done.  Returns CSMKV_OK or a negative csmkv_status.
+ */
+CSMKV_API int csm_compress_host(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *cache,
+                                int32_t n1, int32_t n2, int32_t c, double r,
+                                const uint8_t *outlier_mask, int32_t num_threads, int32_t *best_b,
+                                uint8_t *selected, int32_t *src_pos);
+
+/*
+ * csm_upload_rows -- enqueue on `stream` the copy of a host cache's rows [row_begin, lens_host[z])
+ * (K, V, N) and lens_host[z] into the device cache, for every slice z with outlier_mask[z] == 0
+ * (outlier_mask: host pointer or NULL = every slice).  After csm_compress_host the rows from n1
+ * on are the ones a round changed, so row_begin = n1 sends only the round's result.  Consecutive
+ * slices go as one strided copy each for K, V, N and lens (rows between a slice's length and its
+ * group's longest may be copied too; they lie past its length).  Host buffers must stay
+ * unchanged until the stream has run the copies, and should be pinned (hipHostMalloc) for the
+ * copies to be asynchronous.  Both caches share `cache`'s geometry.  Returns CSMKV_OK,
+ * CSMKV_EINVAL (NULL pointer, row_begin < 0, a lens_host entry out of [0, cap]) with nothing
+ * enqueued, or CSMKV_EHIP.
+ */
+CSMKV_API int csm_upload_rows(const void *K_host, const void *V_host, const int32_t *N_host,
+                              const int32_t *lens_host, void *K, void *V, int32_t *N,
+                              int32_t *lens, const csmkv_cache *cache, int32_t row_begin,
+                              const uint8_t *outlier_mask, void *stream);
+
 /* Synchronise `stream` and return CSMKV_OK if the device error word is 0, CSMKV_EDEVICE if
  * a kernel set it, or CSMKV_EHIP if the copy failed.  error_word is the first int32 of a
  * workspace or the word given to kv_append.  The word is not changed. */

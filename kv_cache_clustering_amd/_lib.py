@@ -52,6 +52,10 @@ _SIGS = {
     "decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _sz, _p]),
     "decode_attn_logn_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _p]),
     "kv_append": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p]),
+    "csm_host_isa": (ctypes.c_int, []),
+    "csm_compress_host": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _d, _p, _i32, _p,
+                                         _p, _p]),
+    "csm_upload_rows": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _desc, _i32, _p, _p]),
     "csmkv_read_error": (ctypes.c_int, [_p, _p]),
     "csmkv_clear_error": (ctypes.c_int, [_p, _p]),
 }
@@ -279,6 +283,63 @@ def kv_append(K, V, N, lens, k_new, v_new, error_word=None):
     rc = _lib.kv_append(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), _ptr(k_new),
                         _ptr(v_new), _ptr(error_word), _stream(K.device))
     _raise(rc, "kv_append")
+
+
+HOST_ISA = {0: "scalar", 1: "avx2", 2: "avx512"}
+
+
+def host_isa():
+    """Vector unit the host round uses on this CPU: 'avx512', 'avx2' or 'scalar'."""
+    return HOST_ISA[_lib.csm_host_isa()]
+
+
+def _check_host(*ts):
+    for t in ts:
+        if t is not None and (t.is_cuda or not t.is_contiguous()):
+            raise ValueError("host-round tensors must be contiguous CPU tensors")
+
+
+def csm_compress_host(K, V, N, lens, n1=16, n2=64, c=256, r=0.5, outlier_mask=None, threads=0,
+                      taps=False, max_len=None):
+    """One CSM round in place over a cache in host memory (CPU tensors), on `threads` host
+    threads (0 = all).  With taps=True returns (best_b, selected, src_pos) host tensors laid out
+    as csm_compress_debug's; else None."""
+    _check_host(K, V, N, lens, outlier_mask)
+    if K.shape != V.shape or K.dtype != V.dtype or N.shape != K.shape[:2] or N.dtype != torch.int32:
+        raise ValueError("K, V [num_slices, cap, d] of one dtype; N int32 [num_slices, cap]")
+    if lens.shape != K.shape[:1] or lens.dtype != torch.int32:
+        raise ValueError("lens must be int32 [num_slices]")
+    if outlier_mask is not None and (outlier_mask.dtype != torch.uint8 or outlier_mask.shape != K.shape[:1]):
+        raise ValueError("outlier_mask must be uint8 [num_slices]")
+    desc = cache_desc(K, max_len)
+    best = sel = src = None
+    if taps:
+        S, cap = K.shape[0], K.shape[1]
+        units = _lib.csm_compress_units(ctypes.byref(desc), n1, n2, c)
+        W = 128 if c <= 256 else 256
+        best = torch.full((S, max(units, 1), W), -1, dtype=torch.int32)
+        sel = torch.zeros((S, max(units, 1), W), dtype=torch.uint8)
+        src = torch.full((S, cap), -1, dtype=torch.int32)
+    rc = _lib.csm_compress_host(_ptr(K), _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), n1, n2, c,
+                                float(r), _ptr(outlier_mask), int(threads), _ptr(best), _ptr(sel),
+                                _ptr(src))
+    _raise(rc, "csm_compress_host")
+    return (best, sel, src) if taps else None
+
+
+def csm_upload_rows(K_host, V_host, N_host, lens_host, K, V, N, lens, row_begin=16,
+                    outlier_mask=None):
+    """Enqueue the copy of the host cache's rows [row_begin, lens) (K, V, N) and lens into the
+    device cache, for every slice not flagged in outlier_mask (a CPU uint8 tensor or None)."""
+    _check_host(K_host, V_host, N_host, lens_host, outlier_mask)
+    _check_cache(K, V, N, lens)
+    if K_host.shape != K.shape or K_host.dtype != K.dtype or N_host.shape != N.shape:
+        raise ValueError("host and device caches must share their geometry")
+    desc = cache_desc(K)
+    rc = _lib.csm_upload_rows(_ptr(K_host), _ptr(V_host), _ptr(N_host), _ptr(lens_host), _ptr(K),
+                              _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), int(row_begin),
+                              _ptr(outlier_mask), _stream(K.device))
+    _raise(rc, "csm_upload_rows")
 
 
 def read_error(word):

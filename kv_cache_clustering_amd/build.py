@@ -9,6 +9,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsmkv.so")
 SOURCES = ["csm_kernel.hip", "decode_kernel.hip", "csmkv_abi.cpp"]
+HOST_SOURCES = ["csm_host.cpp"]  # host-only C++ (no GPU code), built with the host compiler
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread",
+              "-I", os.path.join(ROOT, "include")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -30,8 +34,12 @@ def build(verbose=False):
             cmd.insert(1, "-xhip")
         _run(cmd, verbose)
         objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
+        _run([CXX, *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

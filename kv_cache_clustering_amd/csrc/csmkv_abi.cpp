@@ -2,6 +2,7 @@
 // and launches on the caller's stream.  No entry point allocates or frees memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -329,6 +330,46 @@ int kv_append(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_cache *ca
   a.rowb = cache->d * elem_bytes(cache->dtype);
   const int e = csmkv::launch_append(a, static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+int csm_upload_rows(const void *K_host, const void *V_host, const int32_t *N_host,
+                    const int32_t *lens_host, void *K, void *V, int32_t *N, int32_t *lens,
+                    const csmkv_cache *cache, int32_t row_begin, const uint8_t *outlier_mask,
+                    void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (!K_host || !V_host || !N_host || !lens_host || !K || !V || !N || !lens || row_begin < 0)
+    return CSMKV_EINVAL;
+  const int64_t S = cache->num_slices, cap = cache->cap;
+  for (int64_t z = 0; z < S; ++z)
+    if (lens_host[z] < 0 || (int64_t)lens_host[z] > cap) return CSMKV_EINVAL;
+  const size_t rowb = (size_t)cache->d * elem_bytes(cache->dtype);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char *Kh = static_cast<const char *>(K_host), *Vh = static_cast<const char *>(V_host);
+  char *Kd = static_cast<char *>(K), *Vd = static_cast<char *>(V);
+  for (int64_t z0 = 0; z0 < S;) {
+    if (outlier_mask && outlier_mask[z0]) {
+      ++z0;
+      continue;
+    }
+    int64_t z1 = z0;  // a run of consecutive slices to upload
+    int64_t hi = 0;
+    while (z1 < S && !(outlier_mask && outlier_mask[z1])) hi = std::max<int64_t>(hi, lens_host[z1++]);
+    const size_t run = (size_t)(z1 - z0);
+    if (hi > row_begin) {
+      const size_t rows = (size_t)(hi - row_begin);
+      const size_t off = ((size_t)z0 * cap + row_begin) * rowb, pitch = (size_t)cap * rowb;
+      const size_t noff = (size_t)z0 * cap + row_begin, npitch = (size_t)cap * 4;
+      if (hipMemcpy2DAsync(Kd + off, pitch, Kh + off, pitch, rows * rowb, run, hipMemcpyHostToDevice, st) != hipSuccess ||
+          hipMemcpy2DAsync(Vd + off, pitch, Vh + off, pitch, rows * rowb, run, hipMemcpyHostToDevice, st) != hipSuccess ||
+          hipMemcpy2DAsync(N + noff, npitch, N_host + noff, npitch, rows * 4, run, hipMemcpyHostToDevice, st) != hipSuccess)
+        return CSMKV_EHIP;
+    }
+    if (hipMemcpyAsync(lens + z0, lens_host + z0, run * 4, hipMemcpyHostToDevice, st) != hipSuccess)
+      return CSMKV_EHIP;
+    z0 = z1;
+  }
+  return CSMKV_OK;
 }
 
 int csmkv_clear_error(int32_t *error_word, void *stream) {

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 17
     raw = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(raw, n), n
@@ -145,6 +145,21 @@ def test_decode_and_append_validation(lib):
     assert app(FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc(lib, dtype=3)), FAKE, FAKE, None, None) == lib.EDTYPE
     assert lib.raw.csmkv_read_error(None, None) == lib.EINVAL
     assert lib.raw.csmkv_clear_error(None, None) == lib.EINVAL
+
+
+def test_upload_validation(lib):
+    """csm_upload_rows checks its pointers, row_begin and every host length before enqueuing."""
+    import numpy as np
+    up = lib.raw.csm_upload_rows
+    d = _desc(lib, S=3, cap=100, max_len=100)
+    lens = np.array([100, 50, 101], np.int32)
+    lp = ctypes.c_void_p(lens.ctypes.data)
+    assert up(FAKE, FAKE, FAKE, lp, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 0, None, None) == lib.EINVAL
+    lens[2] = 7
+    assert up(FAKE, FAKE, FAKE, lp, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), -1, None, None) == lib.EINVAL
+    assert up(None, FAKE, FAKE, lp, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 0, None, None) == lib.EINVAL
+    assert up(FAKE, FAKE, FAKE, lp, FAKE, FAKE, FAKE, FAKE, ctypes.byref(_desc(lib, d=96)), 0, None,
+              None) == lib.EUNSUPPORTED
 
 
 def test_noalloc_decode_validation(lib):

@@ -150,6 +150,9 @@ def main():
     # measured on a copy of the serving cache before the timed steps append to it
     trig = trigger_round(lib, w, sched, Kd, Vd, Nd, Ld, app_k, app_v, mask, maskh, flush, stream,
                          dev)
+    # the hierarchical centroid index over the serving cache: build, and decode over the rows
+    # it keeps with the workload's queries
+    hier = index_decode(lib, w, Kd, Vd, Nd, Ld, q_all[0], stream, dev)
     # the CPU-offloaded variant: the same round on the host's cores over a host copy of a sample
     # of the slices, and the upload of its result
     offload = host_offload(lib, w, K0, V0, N0, L0, maskh, stream, dev, args.offload_slices)
@@ -452,11 +455,116 @@ def main():
                      "frac": csm_gbps / PEAK_GBPS,
                      "traffic": recorded_traffic("csm_round_bf16", CSM_SOURCES)},
         "cpu_offload": offload,
+        "hierarchical_index": hier,
         "cpu_baseline": cpu,
         "workloads": others,
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
+
+
+def index_decode(lib, w, Kd, Vd, Nd, Ld, q, stream, dev, B=64, tau=8.0):
+    """The hierarchical centroid index over the serving cache (blocks of B rows): build time,
+    then decode_attn_logn_pruned with the workload's queries (time, fraction of rows kept)
+    beside the plain call, both timed with events over 10 calls."""
+    import torch
+
+    index = lib.new_index(Kd, B)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib.index_build(Kd, Nd, Ld, index, err, B)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    lib.index_build(Kd, Nd, Ld, index, err, B)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    O, kept, ws = lib.decode_attn_logn_pruned(q, Kd, Vd, Nd, Ld, w.H_q, w.H_kv, index, tau, w.n1,
+                                              w.n2, B, kept=True)
+    O_full = lib.decode_attn_logn(q, Kd, Vd, Nd, Ld, w.H_q, w.H_kv)
+    times = {}
+    for name in ("pruned", "plain"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            if name == "pruned":
+                lib.decode_attn_logn_pruned(q, Kd, Vd, Nd, Ld, w.H_q, w.H_kv, index, tau, w.n1,
+                                            w.n2, B, out=O, workspace=ws)
+            else:
+                lib.decode_attn_logn(q, Kd, Vd, Nd, Ld, w.H_q, w.H_kv, out=O_full)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / 10 * 1e3
+    assert lib.read_error(err) == lib.OK and lib.read_error(ws) == lib.OK
+    clustered = index_decode_clustered(lib, w, stream, dev, B, tau)
+    lens = Ld.cpu().numpy()
+    kh = kept.cpu().numpy()
+    kept_rows = 0
+    for z in range(len(lens)):
+        for b in range(-(-int(lens[z]) // B)):
+            kept_rows += min(B, int(lens[z]) - b * B) if kh[z, b] else 0
+    out = {"block_rows": B, "tau": tau, "index_bytes": index.numel(), "build_ms": build_ms,
+           "pruned_decode_us": times["pruned"], "plain_decode_us": times["plain"],
+           "rows_kept_frac": kept_rows / float(lens.sum()),
+           "max_abs_vs_plain": float((O - O_full).abs().max()),
+           "queries": "the workload's (N(0, I)); on AR(1) keys the ball bounds drop little",
+           "clustered_keys": clustered}
+    del index, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def index_decode_clustered(lib, w, stream, dev, B, tau, S=64, s=13081):
+    """The same index path on keys the ball bounds can separate: S slices of s rows whose blocks
+    of B rows are tight clusters (centre of norm sqrt(d) in a random direction, spread 0.05 per
+    element), queries aligned with one key of their slice (norm 6 d^(1/4)), fp32 -> bf16; values
+    N(0, 1), degrees 1.  Time of the pruned and the plain call (events over 10 calls each),
+    fraction of rows kept, largest difference of the outputs."""
+    import torch
+    gen = torch.Generator(device=dev).manual_seed(404)
+    d, cap = w.d, s + 64
+    nb = -(-s // B)
+    C = torch.randn((S, nb, d), generator=gen, device=dev)
+    C = C * (d ** 0.5) / C.norm(dim=2, keepdim=True)
+    K = torch.zeros((S, cap, d), dtype=torch.bfloat16, device=dev)
+    K[:, :s] = (C.repeat_interleave(B, dim=1)[:, :s]
+                + 0.05 * torch.randn((S, s, d), generator=gen, device=dev)).to(torch.bfloat16)
+    V = torch.randn((S, cap, d), generator=gen, device=dev).to(torch.bfloat16)
+    N = torch.ones((S, cap), dtype=torch.int32, device=dev)
+    L = torch.full((S,), s, dtype=torch.int32, device=dev)
+    H_kv, H_q = w.H_kv, w.H_q
+    j = torch.randint(0, s, (S // H_kv, H_q), generator=gen, device=dev)
+    zs = (torch.arange(S // H_kv, device=dev)[:, None] * H_kv
+          + torch.arange(H_q, device=dev)[None, :] // (H_q // H_kv))
+    kq = K[zs, j].float()
+    q = (6.0 * d ** 0.25 * kq / kq.norm(dim=2, keepdim=True)).to(torch.bfloat16)
+    index = lib.new_index(K, B)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib.index_build(K, N, L, index, err, B)
+    O, kept, ws = lib.decode_attn_logn_pruned(q, K, V, N, L, H_q, H_kv, index, tau, w.n1, w.n2, B,
+                                              kept=True)
+    O_full = lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv)
+    times = {}
+    for name in ("pruned", "plain"):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            if name == "pruned":
+                lib.decode_attn_logn_pruned(q, K, V, N, L, H_q, H_kv, index, tau, w.n1, w.n2, B,
+                                            out=O, workspace=ws)
+            else:
+                lib.decode_attn_logn(q, K, V, N, L, H_q, H_kv, out=O_full)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / 10 * 1e3
+    assert lib.read_error(err) == lib.OK and lib.read_error(ws) == lib.OK
+    kept_rows = int(kept[:, :nb - 1].sum()) * B + int(kept[:, nb - 1].sum()) * (s - (nb - 1) * B)
+    out = {"slices": S, "rows": s, "pruned_decode_us": times["pruned"],
+           "plain_decode_us": times["plain"], "rows_kept_frac": kept_rows / float(S * s),
+           "max_abs_vs_plain": float((O - O_full).abs().max())}
+    del K, V, N, index, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def host_offload(lib, w, K0, V0, N0, L0, maskh, stream, dev, nslices):

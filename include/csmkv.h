@@ -277,6 +277,57 @@ CSMKV_API int csm_upload_rows(const void *K_host, const void *V_host, const int3
                               int32_t *lens, const csmkv_cache *cache, int32_t row_begin,
                               const uint8_t *outlier_mask, void *stream);
 
+/* ---------------------------------------------------------------- hierarchical centroid index
+ * LycheeCluster page, 方法论 §2 层次 KV 索引 and §3 流式懒更新: block centroids in a binary tree
+ * whose distances obey the triangle inequality, walked by the query to drop whole subtrees, and
+ * refreshed lazily as tokens are appended.  Here, over the cache CSM leaves: per slice a ball tree
+ * over blocks of block_rows consecutive rows (a leaf: centre = degree-weighted mean of its keys,
+ * radius = farthest key; an inner node: centre = degree-weighted mean of its children's centres,
+ * radius covering both child balls), in heap order over P leaf slots, P = the power of two that
+ * holds cap / block_rows blocks (at most 65536).  block_rows: 16, 32, 64, 128 or 256.
+ * Index memory (device, caller-owned, 256-byte aligned): csm_index_bytes() bytes, laid out as
+ * centres [num_slices][2P][d] fp32, radii, largest log2 degree and degree totals [num_slices][2P].
+ */
+CSMKV_API size_t csm_index_bytes(const csmkv_cache *cache, int32_t block_rows);
+
+/* Build every slice's tree over its rows [0, lens[z]) (after a CSM round, or any change of the
+ * rows).  error_word: device int32 (sticky), set for a lens[] entry above max_len or cap (that
+ * slice's tree is left empty).  Returns CSMKV_OK or a negative csmkv_status. */
+CSMKV_API int csm_index_build(const void *K, const int32_t *N, const int32_t *lens,
+                              const csmkv_cache *cache, int32_t block_rows, void *index,
+                              size_t index_bytes, int32_t *error_word, void *stream);
+
+/* Take in the row lens[z] - 1 just appended to every slice (after kv_append), lazily: the row
+ * joins its leaf (or opens a new one centred on it); the leaf's and every ancestor's radius grow
+ * to cover it; centres move only at the next build.  Bounds stay valid. */
+CSMKV_API int csm_index_append(const void *K, const int32_t *N, const int32_t *lens,
+                               const csmkv_cache *cache, int32_t block_rows, void *index,
+                               size_t index_bytes, int32_t *error_word, void *stream);
+
+/* Workspace bytes of decode_attn_logn_pruned (first int32: the sticky error word). */
+CSMKV_API size_t decode_attn_logn_pruned_workspace_bytes(const csmkv_cache *cache, int32_t H_q,
+                                                         int32_t H_kv, int32_t block_rows);
+
+/*
+ * decode_attn_logn_pruned -- decode_attn_logn over the rows the index keeps.  Per slice (its G
+ * query heads together): every key k in a node's ball satisfies q.k <= q.mu + |q| rho, so
+ * U = (q.mu + |q| rho) log2(e) / sqrt(d) + max log2 N bounds the base-2 logit of all its rows.
+ * m_low = the largest exact logit among the protected rows (the first n1, the last n2) and the
+ * first row of every block.  The tree is walked from the root, a node's children visited only if
+ * U >= m_low - tau log2(e) for one of the G heads; blocks that pass, and blocks holding a
+ * protected row, are kept, and O is the log-N attention over their rows.  tau = +inf keeps every
+ * block.  A dropped row weighs at most e^-tau of the largest, which is always kept.
+ * kept: optional device [num_slices][P] uint8 tap (1 = block kept).  Other arguments as
+ * decode_attn_logn; the index must describe the current rows (built, and appended to after each
+ * kv_append).
+ */
+CSMKV_API int decode_attn_logn_pruned(const void *q, const void *K, const void *V, const int32_t *N,
+                                      const int32_t *lens, const csmkv_cache *cache, int32_t H_q,
+                                      int32_t H_kv, int32_t n1, int32_t n2, int32_t block_rows,
+                                      const void *index, size_t index_bytes, double tau, float *O,
+                                      uint8_t *kept, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
 /* Synchronise `stream` and return CSMKV_OK if the device error word is 0, CSMKV_EDEVICE if
  * a kernel set it, or CSMKV_EHIP if the copy failed.  error_word is the first int32 of a
  * workspace or the word given to kv_append.  The word is not changed. */

@@ -56,6 +56,12 @@ _SIGS = {
     "csm_compress_host": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _d, _p, _i32, _p,
                                          _p, _p]),
     "csm_upload_rows": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _desc, _i32, _p, _p]),
+    "csm_index_bytes": (_sz, [_desc, _i32]),
+    "csm_index_build": (ctypes.c_int, [_p, _p, _p, _desc, _i32, _p, _sz, _p, _p]),
+    "csm_index_append": (ctypes.c_int, [_p, _p, _p, _desc, _i32, _p, _sz, _p, _p]),
+    "decode_attn_logn_pruned_workspace_bytes": (_sz, [_desc, _i32, _i32, _i32]),
+    "decode_attn_logn_pruned": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _i32, _i32,
+                                               _i32, _p, _sz, _d, _p, _p, _p, _sz, _p]),
     "csmkv_read_error": (ctypes.c_int, [_p, _p]),
     "csmkv_clear_error": (ctypes.c_int, [_p, _p]),
 }
@@ -340,6 +346,66 @@ def csm_upload_rows(K_host, V_host, N_host, lens_host, K, V, N, lens, row_begin=
                               _ptr(V), _ptr(N), _ptr(lens), ctypes.byref(desc), int(row_begin),
                               _ptr(outlier_mask), _stream(K.device))
     _raise(rc, "csm_upload_rows")
+
+
+def index_leaf_slots(cap, block_rows):
+    """Leaf slots P of a slice's tree: the power of two holding cap / block_rows blocks."""
+    leaves = -(-int(cap) // int(block_rows))
+    P = 1
+    while P < leaves:
+        P *= 2
+    return P
+
+
+def new_index(K, block_rows=64):
+    """Zeroed device memory for the hierarchical index of cache K."""
+    n = _lib.csm_index_bytes(ctypes.byref(cache_desc(K)), block_rows)
+    if n == 0:
+        raise ValueError("unsupported index geometry")
+    return torch.zeros(n, dtype=torch.uint8, device=K.device)
+
+
+def _index_call(fn, K, N, lens, index, block_rows, error_word, max_len):
+    if error_word is None or error_word.dtype != torch.int32 or not error_word.is_cuda:
+        raise ValueError("error_word must be an int32 GPU tensor")
+    desc = cache_desc(K, max_len)
+    rc = fn(_ptr(K), _ptr(N), _ptr(lens), ctypes.byref(desc), int(block_rows), _ptr(index),
+            index.numel(), _ptr(error_word), _stream(K.device))
+    _raise(rc, fn.__name__)
+
+
+def index_build(K, N, lens, index, error_word, block_rows=64, max_len=None):
+    """Build every slice's ball tree over its rows [0, lens)."""
+    _index_call(_lib.csm_index_build, K, N, lens, index, block_rows, error_word, max_len)
+
+
+def index_append(K, N, lens, index, error_word, block_rows=64):
+    """Take in the row each slice just appended (lazy update)."""
+    _index_call(_lib.csm_index_append, K, N, lens, index, block_rows, error_word, None)
+
+
+def decode_attn_logn_pruned(q, K, V, N, lens, H_q, H_kv, index, tau, n1=16, n2=64, block_rows=64,
+                            out=None, kept=False, max_len=None, workspace=None):
+    """decode_attn_logn over the rows the index keeps.  Returns (O, kept [num_slices, P] uint8 or
+    None)."""
+    _check_cache(K, V, N, lens)
+    S, cap, d = K.shape
+    groups = S // H_kv if H_kv > 0 else 0
+    if q.shape != (groups, H_q, d) or q.dtype != K.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
+    if out is None:
+        out = torch.empty((groups, H_q, d), dtype=torch.float32, device=K.device)
+    desc = cache_desc(K, max_len)
+    ws = _workspace(_lib.decode_attn_logn_pruned_workspace_bytes(ctypes.byref(desc), H_q, H_kv,
+                                                                 block_rows), K.device, workspace)
+    tap = (torch.zeros((S, index_leaf_slots(cap, block_rows)), dtype=torch.uint8, device=K.device)
+           if kept else None)
+    rc = _lib.decode_attn_logn_pruned(_ptr(q), _ptr(K), _ptr(V), _ptr(N), _ptr(lens),
+                                      ctypes.byref(desc), H_q, H_kv, int(n1), int(n2),
+                                      int(block_rows), _ptr(index), index.numel(), float(tau),
+                                      _ptr(out), _ptr(tap), _ptr(ws), ws.numel(), _stream(K.device))
+    _raise(rc, "decode_attn_logn_pruned")
+    return out, tap, ws
 
 
 def read_error(word):

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsmkv.so")
-SOURCES = ["csm_kernel.hip", "decode_kernel.hip", "csmkv_abi.cpp"]
+SOURCES = ["csm_kernel.hip", "decode_kernel.hip", "index_kernel.hip", "csmkv_abi.cpp"]
 HOST_SOURCES = ["csm_host.cpp"]  # host-only C++ (no GPU code), built with the host compiler
 CXX = os.environ.get("CXX", "g++")
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-pthread",

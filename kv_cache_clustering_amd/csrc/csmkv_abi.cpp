@@ -372,6 +372,189 @@ int csm_upload_rows(const void *K_host, const void *V_host, const int32_t *N_hos
   return CSMKV_OK;
 }
 
+// ---------------------------------------------------------------- hierarchical centroid index
+namespace {
+
+// Leaf slots of a slice's tree: the smallest power of two holding cap / B blocks; 0 if invalid.
+int64_t index_leaf_slots(const csmkv_cache *c, int32_t B) {
+  if (B != 16 && B != 32 && B != 64 && B != 128 && B != 256) return 0;
+  const int64_t leaves = (c->cap + B - 1) / B;
+  int64_t P = 1;
+  while (P < leaves) P *= 2;
+  return P <= csmkv::kPruneMaxLeaves ? P : 0;
+}
+
+struct IdxLayout {
+  size_t mu, rho, lmax, wt, total;
+};
+IdxLayout idx_layout(const csmkv_cache *c, int64_t P) {
+  IdxLayout L;
+  const size_t nodes = (size_t)c->num_slices * 2 * (size_t)P;
+  L.mu = 0;
+  L.rho = align_up(nodes * (size_t)c->d * 4);
+  L.lmax = L.rho + align_up(nodes * 4);
+  L.wt = L.lmax + align_up(nodes * 4);
+  L.total = L.wt + align_up(nodes * 4);
+  return L;
+}
+
+int index_common(const void *K, const int32_t *N, const int32_t *lens, const csmkv_cache *cache,
+                 int32_t B, void *index, size_t index_bytes, int32_t *error_word, void *stream,
+                 int op) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  const int64_t P = index_leaf_slots(cache, B);
+  if (P == 0) return CSMKV_EUNSUPPORTED;
+  if (!K || !N || !lens || !index || !error_word) return CSMKV_EINVAL;
+  if (!aligned(K, 16) || !aligned(index, kAlign) || !aligned(error_word, 4)) return CSMKV_EINVAL;
+  const IdxLayout lay = idx_layout(cache, P);
+  if (index_bytes < lay.total) return CSMKV_EWORKSPACE;
+  char *x = static_cast<char *>(index);
+  csmkv::IdxArgs a = {};
+  a.K = static_cast<const char *>(K);
+  a.N = N;
+  a.lens = lens;
+  a.err = error_word;
+  a.mu = reinterpret_cast<float *>(x + lay.mu);
+  a.rho = reinterpret_cast<float *>(x + lay.rho);
+  a.lmax = reinterpret_cast<float *>(x + lay.lmax);
+  a.wt = reinterpret_cast<int32_t *>(x + lay.wt);
+  a.num_slices = cache->num_slices;
+  a.cap = cache->cap;
+  a.max_len = cache->max_len;
+  a.d = cache->d;
+  a.P = (int32_t)P;
+  a.B = B;
+  const int e = csmkv::launch_index(a, cache->dtype, cache->d, op, static_cast<hipStream_t>(stream));
+  return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+struct PruneLayout {
+  size_t item_off, item_zp, part, runs, nruns, total;
+  int64_t items, max_runs;
+};
+PruneLayout prune_layout(const csmkv_cache *c, int G, int64_t P) {
+  PruneLayout L;
+  const int32_t ts = csmkv::dec_split_tokens(c->num_slices, c->max_len);
+  L.max_runs = P / 2 + 1;
+  L.items = c->num_slices * (L.max_runs + (c->max_len + ts - 1) / ts);
+  L.item_off = kAlign;
+  L.item_zp = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
+  L.part = L.item_zp + align_up((size_t)L.items * 16);
+  L.runs = L.part + align_up((size_t)L.items * G * (4 + c->d) * 4);
+  L.nruns = L.runs + align_up((size_t)c->num_slices * L.max_runs * 8);
+  L.total = L.nruns + align_up((size_t)c->num_slices * 4);
+  return L;
+}
+
+}  // namespace
+
+size_t csm_index_bytes(const csmkv_cache *cache, int32_t block_rows) {
+  if (check_cache(cache)) return 0;
+  const int64_t P = index_leaf_slots(cache, block_rows);
+  return P ? idx_layout(cache, P).total : 0;
+}
+
+int csm_index_build(const void *K, const int32_t *N, const int32_t *lens, const csmkv_cache *cache,
+                    int32_t block_rows, void *index, size_t index_bytes, int32_t *error_word,
+                    void *stream) {
+  return index_common(K, N, lens, cache, block_rows, index, index_bytes, error_word, stream, 0);
+}
+
+int csm_index_append(const void *K, const int32_t *N, const int32_t *lens, const csmkv_cache *cache,
+                     int32_t block_rows, void *index, size_t index_bytes, int32_t *error_word,
+                     void *stream) {
+  return index_common(K, N, lens, cache, block_rows, index, index_bytes, error_word, stream, 1);
+}
+
+size_t decode_attn_logn_pruned_workspace_bytes(const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                                               int32_t block_rows) {
+  if (check_cache(cache) || check_heads(cache, H_q, H_kv)) return 0;
+  const int64_t P = index_leaf_slots(cache, block_rows);
+  return P ? prune_layout(cache, H_q / H_kv, P).total : 0;
+}
+
+int decode_attn_logn_pruned(const void *q, const void *K, const void *V, const int32_t *N,
+                            const int32_t *lens, const csmkv_cache *cache, int32_t H_q,
+                            int32_t H_kv, int32_t n1, int32_t n2, int32_t block_rows,
+                            const void *index, size_t index_bytes, double tau, float *O,
+                            uint8_t *kept, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  rc = check_heads(cache, H_q, H_kv);
+  if (rc) return rc;
+  const int64_t P = index_leaf_slots(cache, block_rows);
+  if (P == 0) return CSMKV_EUNSUPPORTED;
+  if (!q || !K || !V || !N || !lens || !O || !index || n1 < 0 || n2 < 0 || !(tau >= 0.0))
+    return CSMKV_EINVAL;  // tau may be +inf (nothing dropped); NaN is rejected
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(index, kAlign))
+    return CSMKV_EINVAL;
+  const IdxLayout il = idx_layout(cache, P);
+  if (index_bytes < il.total) return CSMKV_EWORKSPACE;
+  const int G = H_q / H_kv;
+  const PruneLayout lay = prune_layout(cache, G, P);
+  if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < lay.total)
+    return CSMKV_EWORKSPACE;
+  if (lay.items > (int64_t)INT32_MAX / 2) return CSMKV_EUNSUPPORTED;
+  if (cache->num_slices == 0) return CSMKV_OK;
+  char *w = static_cast<char *>(workspace);
+  char *x = const_cast<char *>(static_cast<const char *>(index));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cache->d));
+  const int32_t ts = csmkv::dec_split_tokens(cache->num_slices, cache->max_len);
+  csmkv::IdxArgs a = {};
+  a.K = static_cast<const char *>(K);
+  a.q = static_cast<const char *>(q);
+  a.N = N;
+  a.lens = lens;
+  a.err = reinterpret_cast<int32_t *>(w);
+  a.mu = reinterpret_cast<float *>(x + il.mu);
+  a.rho = reinterpret_cast<float *>(x + il.rho);
+  a.lmax = reinterpret_cast<float *>(x + il.lmax);
+  a.wt = reinterpret_cast<int32_t *>(x + il.wt);
+  a.num_slices = cache->num_slices;
+  a.cap = cache->cap;
+  a.max_len = cache->max_len;
+  a.d = cache->d;
+  a.P = (int32_t)P;
+  a.B = block_rows;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.n1 = n1;
+  a.n2 = n2;
+  a.scale_log2 = scale_log2;
+  a.tau_log2 = std::isinf(tau) ? INFINITY : (float)(tau * 1.4426950408889634);
+  a.runs = reinterpret_cast<int32_t *>(w + lay.runs);
+  a.nruns = reinterpret_cast<int32_t *>(w + lay.nruns);
+  a.max_runs = (int32_t)lay.max_runs;
+  a.tsplit = ts;
+  a.kept_tap = kept;
+  a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
+  a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
+  int e = csmkv::launch_prune(a, cache->dtype, cache->d, G, st);
+  if (e) return CSMKV_EHIP;
+  csmkv::DecArgs da = {};
+  da.q = static_cast<const char *>(q);
+  da.K = static_cast<const char *>(K);
+  da.V = static_cast<const char *>(V);
+  da.N = N;
+  da.lens = lens;
+  da.O = O;
+  da.num_slices = cache->num_slices;
+  da.cap = cache->cap;
+  da.max_len = cache->max_len;
+  da.H_q = H_q;
+  da.H_kv = H_kv;
+  da.tsplit = ts;
+  da.scale_log2 = scale_log2;
+  da.err = a.err;
+  da.item_off = a.item_off;
+  da.item_zp = a.item_zp;
+  da.part = reinterpret_cast<float *>(w + lay.part);
+  e = csmkv::launch_decode_table(da, cache->dtype, cache->d, G, lay.items, st);
+  return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
 int csmkv_clear_error(int32_t *error_word, void *stream) {
   if (error_word == nullptr || !aligned(error_word, 4)) return CSMKV_EINVAL;
   return csmkv::launch_clear(error_word, static_cast<hipStream_t>(stream)) ? CSMKV_EHIP : CSMKV_OK;

@@ -841,6 +841,18 @@ int noalloc_scratch(void **ptr) {
   return 0;
 }
 
+int launch_decode_table(const DecArgs &args, int dtype, int d, int G, int64_t max_items,
+                        hipStream_t st) {
+  DecArgs a = args;
+  a.inline_items = 0;
+  const bool sets2 = G >= 8 && dtype == kDtypeF32;  // dec_head_sets<T, G>() == 2
+  const int64_t units = sets2 ? dec_units<2>(max_items) : max_items;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
+  int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
+  if (rc) return rc;
+  return d == 64 ? launch_combine<64>(a, G, st) : launch_combine<128>(a, G, st);
+}
+
 int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_items, hipStream_t st) {
   DecArgs a = args;
   a.inline_items = dec_inline(a.num_slices, a.max_len);

@@ -61,6 +61,29 @@ struct AppArgs {
 // Bytes of the fixed device scratch array behind decode_attn_logn_noalloc (one per GPU).
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 
+// Hierarchical centroid index (ball tree per slice, heap order over P leaf slots) and the
+// selection of the rows decode attention keeps.
+constexpr int kPruneMaxLeaves = 65536;  // largest P (the walk keeps a bit per node of a level)
+
+struct IdxArgs {
+  const char *K, *q;
+  const int32_t *N, *lens;
+  int32_t *err;
+  float *mu, *rho, *lmax;  // [num_slices][2P][d], [num_slices][2P] x 2
+  int32_t *wt;             // [num_slices][2P] degree totals (0 = empty node)
+  int64_t num_slices, cap;
+  int32_t max_len, d, P, B;
+  // pruned decode
+  int32_t H_q, H_kv, n1, n2;
+  float scale_log2, tau_log2;
+  int32_t *runs;      // [num_slices][max_runs][2] kept row runs [first, end)
+  int32_t *nruns;     // [num_slices]
+  int32_t max_runs, tsplit;
+  uint8_t *kept_tap;  // [num_slices][P] or null
+  int32_t *item_off;  // [num_slices + 1]
+  int32_t *item_zp;   // [items][4]
+};
+
 // Storage codes of the C ABI (csmkv_dtype).
 constexpr int kDtypeBf16 = 0, kDtypeF32 = 1, kDtypeF16 = 2;
 
@@ -68,6 +91,13 @@ constexpr int kDtypeBf16 = 0, kDtypeF32 = 1, kDtypeF16 = 2;
 int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream);
 int launch_decode(const DecArgs &a, int dtype, int d, int G, int64_t max_items, hipStream_t st);
 int launch_append(const AppArgs &a, hipStream_t st);
+// op 0: build the index over each slice's rows; op 1: take in the row just appended.
+int launch_index(const IdxArgs &a, int dtype, int d, int op, hipStream_t st);
+// Thresholds, walk and runs per slice, then the item table (the decode split and combine kernels
+// follow with launch_decode_table).
+int launch_prune(const IdxArgs &a, int dtype, int d, int G, hipStream_t st);
+// The decode split and combine kernels over an item table already in args (item_off, item_zp).
+int launch_decode_table(const DecArgs &a, int dtype, int d, int G, int64_t max_items, hipStream_t st);
 int launch_clear(int32_t *word, hipStream_t st);
 // Tokens per decode work item for a geometry, and the upper bound on work items (sizes the
 // partial buffer).  Both depend only on the slice count and the host-known length bound.

@@ -20,10 +20,12 @@ Modules:
   attention  -- log-N decode attention, plain softmax attention, cache append.
   schedule   -- Algorithm 1 budget / trigger / annealing as plain integer loops.
   theorem    -- Theorem 6.1 objective and brute-force maximiser search.
+  index      -- hierarchical centroid index (ball tree) over a clustered cache and attention
+                over the rows it keeps (LycheeCluster page, 层次 KV 索引 / 流式懒更新).
 
 Parity status per function is stated in each module header.  Values of merged
 centroids at specific inputs are "parity unpinned" beyond the invariants listed in
 ``csm``: the pages print no worked example with numbers.
 """
 
-from . import bf16, csm, attention, schedule, theorem  # noqa: F401
+from . import bf16, csm, attention, schedule, theorem, index  # noqa: F401

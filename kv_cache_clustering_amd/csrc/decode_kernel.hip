@@ -492,7 +492,38 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
   const int S = (int)a.num_slices;
   const float NEG_INF = -__builtin_inff();
   int total, ts = a.tsplit;
-  if constexpr (INL) {
+  // Calls over at most 64 slices (a layer's KV heads) plan inside every wave, in registers: lane
+  // z holds slice z's length and its inclusive item offset, so neither the plan nor the search
+  // for an item's slice needs a barrier or LDS.
+  const bool wave_plan = INL && S <= 64;
+  int w_len = 0, w_incl = 0;
+  if (INL && wave_plan) {
+    const int sl = l < S ? a.lens[l] : 0;
+    const bool ok = l >= S || len_ok(a, sl);
+    w_len = ok ? sl : 0;
+    int incl = w_len;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (l >= o) incl += y;
+    }
+    ts = __builtin_amdgcn_readfirstlane(inline_split_tokens(__builtin_amdgcn_readlane(incl, 63)));
+    const int cnt = (w_len + ts - 1) / ts;
+    incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (l >= o) incl += y;
+    }
+    w_incl = incl;
+    total = __builtin_amdgcn_readlane(incl, 63);
+    if (blockIdx.x == 0 && w == 0) {  // offsets for the combine kernel; a bad length is sticky
+      if (l < S) a.item_off[l] = incl - cnt;
+      if (l == 0) a.item_off[S] = total;
+      const uint64_t badm = __ballot(!ok);
+      if (l == 0 && badm != 0) atomicExch(a.err, kDeviceError);
+    }
+  } else if constexpr (INL) {
     // item counts of all slices, scanned into LDS (a bad length counts 0 items).  Workgroup
     // 0 also stores the offsets for the combine kernel and, for a bad length, sets the
     // (sticky) error word.
@@ -666,14 +697,24 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     for (int v = blockIdx.x; v < dec_units<HS>(total); v += gridDim.x) {
       const int item = dec_unit_item<HS>(v), hs = dec_unit_set<HS>(v);
       if (item >= total) continue;
-      int lo = 0, hi = S - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= item) lo = mid; else hi = mid - 1;
+      int z, first, len;
+      if (wave_plan) {
+        // the item's slice: the number of slices whose items all lie before it
+        z = __popcll(__ballot(w_incl <= item));
+        len = __builtin_amdgcn_readlane(w_len, z);
+        first = __builtin_amdgcn_readlane(w_incl, z) - (len + ts - 1) / ts;
+      } else {
+        int lo = 0, hi = S - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (__builtin_amdgcn_readfirstlane(s_off[mid]) <= item) lo = mid; else hi = mid - 1;
+        }
+        z = lo;
+        first = __builtin_amdgcn_readfirstlane(s_off[lo]);
+        len = __builtin_amdgcn_readfirstlane(s_len[lo]);
       }
-      const int p = item - __builtin_amdgcn_readfirstlane(s_off[lo]);
-      const int len = __builtin_amdgcn_readfirstlane(s_len[lo]), cnt = (len + ts - 1) / ts;
-      process(item, hs, lo, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
+      const int p = item - first, cnt = (len + ts - 1) / ts;
+      process(item, hs, z, item_bound(p, len, cnt), item_bound(p + 1, len, cnt));
     }
   } else {
     for (int v = blockIdx.x; v < dec_units<HS>(total); v += gridDim.x) {

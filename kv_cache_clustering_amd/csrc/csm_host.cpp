@@ -106,15 +106,18 @@ inline void f32_to_row(const float *src, int dtype, int d, char *dst) {
 }
 
 // ------------------------------------------------------------------ dot products
-// S[i * nB + j] = <A_i, B_j> for fp32 rows of length d (a multiple of 16), row-major.
-using DotsFn = void (*)(const float *, const float *, int, int, int, float *);
+// S[i * ld + j] = <A_i, B_j> for fp32 rows of length d, A row-major [nA][d], B given transposed
+// (Bt[k * ld + j] = B_j[k], columns nB .. ld - 1 zero; ld a multiple of 32).  Every product is
+// summed over k in ascending order with one fused multiply-add per step, so all three forms give
+// the same bits.
+using DotsFn = void (*)(const float *, const float *, int, int, int, int, float *);
 
-void dots_scalar(const float *A, const float *B, int nA, int nB, int d, float *S) {
+void dots_scalar(const float *A, const float *Bt, int nA, int nB, int ld, int d, float *S) {
   for (int i = 0; i < nA; ++i)
     for (int j = 0; j < nB; ++j) {
       float acc = 0.f;
-      for (int k = 0; k < d; ++k) acc = std::fma(A[size_t(i) * d + k], B[size_t(j) * d + k], acc);
-      S[size_t(i) * nB + j] = acc;
+      for (int k = 0; k < d; ++k) acc = std::fma(A[size_t(i) * d + k], Bt[size_t(k) * ld + j], acc);
+      S[size_t(i) * ld + j] = acc;
     }
 }
 
@@ -125,76 +128,218 @@ __attribute__((target("avx2,fma"))) inline float hsum256(__m256 v) {
   return _mm_cvtss_f32(s);
 }
 
-__attribute__((target("avx2,fma"))) void dots_avx2(const float *A, const float *B, int nA, int nB,
-                                                   int d, float *S) {
-  for (int i = 0; i < nA; ++i) {
-    const float *a = A + size_t(i) * d;
-    int j = 0;
-    for (; j + 4 <= nB; j += 4) {  // four B rows share each A load
-      const float *b0 = B + size_t(j) * d, *b1 = b0 + d, *b2 = b1 + d, *b3 = b2 + d;
-      __m256 c0 = _mm256_setzero_ps(), c1 = c0, c2 = c0, c3 = c0;
-      for (int k = 0; k < d; k += 8) {
-        const __m256 av = _mm256_loadu_ps(a + k);
-        c0 = _mm256_fmadd_ps(av, _mm256_loadu_ps(b0 + k), c0);
-        c1 = _mm256_fmadd_ps(av, _mm256_loadu_ps(b1 + k), c1);
-        c2 = _mm256_fmadd_ps(av, _mm256_loadu_ps(b2 + k), c2);
-        c3 = _mm256_fmadd_ps(av, _mm256_loadu_ps(b3 + k), c3);
-      }
-      float *s = S + size_t(i) * nB + j;
-      s[0] = hsum256(c0);
-      s[1] = hsum256(c1);
-      s[2] = hsum256(c2);
-      s[3] = hsum256(c3);
+// Register tiles of R A rows x 16 B columns (AVX2: two 8-wide vectors per column block; AVX-512:
+// one 16-wide): each step over k broadcasts R A elements and loads one row of Bt.
+template <int R>
+__attribute__((target("avx2,fma"))) inline void tile_avx2(const float *A, const float *Bt, int ld,
+                                                          int d, int j, float *S) {
+  __m256 c[R][2];
+  for (int r = 0; r < R; ++r) c[r][0] = c[r][1] = _mm256_setzero_ps();
+  for (int k = 0; k < d; ++k) {
+    const __m256 b0 = _mm256_loadu_ps(Bt + size_t(k) * ld + j);
+    const __m256 b1 = _mm256_loadu_ps(Bt + size_t(k) * ld + j + 8);
+    for (int r = 0; r < R; ++r) {
+      const __m256 a = _mm256_broadcast_ss(A + size_t(r) * d + k);
+      c[r][0] = _mm256_fmadd_ps(a, b0, c[r][0]);
+      c[r][1] = _mm256_fmadd_ps(a, b1, c[r][1]);
     }
-    for (; j < nB; ++j) {
-      const float *b = B + size_t(j) * d;
-      __m256 c = _mm256_setzero_ps();
-      for (int k = 0; k < d; k += 8) c = _mm256_fmadd_ps(_mm256_loadu_ps(a + k), _mm256_loadu_ps(b + k), c);
-      S[size_t(i) * nB + j] = hsum256(c);
-    }
+  }
+  for (int r = 0; r < R; ++r) {
+    _mm256_storeu_ps(S + size_t(r) * ld + j, c[r][0]);
+    _mm256_storeu_ps(S + size_t(r) * ld + j + 8, c[r][1]);
   }
 }
 
-__attribute__((target("avx512f"))) void dots_avx512(const float *A, const float *B, int nA, int nB,
-                                                    int d, float *S) {
-  for (int i = 0; i < nA; ++i) {
-    const float *a = A + size_t(i) * d;
-    int j = 0;
-    for (; j + 4 <= nB; j += 4) {
-      const float *b0 = B + size_t(j) * d, *b1 = b0 + d, *b2 = b1 + d, *b3 = b2 + d;
-      __m512 c0 = _mm512_setzero_ps(), c1 = c0, c2 = c0, c3 = c0;
-      for (int k = 0; k < d; k += 16) {
-        const __m512 av = _mm512_loadu_ps(a + k);
-        c0 = _mm512_fmadd_ps(av, _mm512_loadu_ps(b0 + k), c0);
-        c1 = _mm512_fmadd_ps(av, _mm512_loadu_ps(b1 + k), c1);
-        c2 = _mm512_fmadd_ps(av, _mm512_loadu_ps(b2 + k), c2);
-        c3 = _mm512_fmadd_ps(av, _mm512_loadu_ps(b3 + k), c3);
-      }
-      float *s = S + size_t(i) * nB + j;
-      s[0] = _mm512_reduce_add_ps(c0);
-      s[1] = _mm512_reduce_add_ps(c1);
-      s[2] = _mm512_reduce_add_ps(c2);
-      s[3] = _mm512_reduce_add_ps(c3);
-    }
-    for (; j < nB; ++j) {
-      const float *b = B + size_t(j) * d;
-      __m512 c = _mm512_setzero_ps();
-      for (int k = 0; k < d; k += 16) c = _mm512_fmadd_ps(_mm512_loadu_ps(a + k), _mm512_loadu_ps(b + k), c);
-      S[size_t(i) * nB + j] = _mm512_reduce_add_ps(c);
+__attribute__((target("avx2,fma"))) void dots_avx2(const float *A, const float *Bt, int nA, int nB,
+                                                   int ld, int d, float *S) {
+  for (int j = 0; j < nB; j += 16) {
+    int i = 0;
+    for (; i + 6 <= nA; i += 6) tile_avx2<6>(A + size_t(i) * d, Bt, ld, d, j, S + size_t(i) * ld);
+    for (; i < nA; ++i) tile_avx2<1>(A + size_t(i) * d, Bt, ld, d, j, S + size_t(i) * ld);
+  }
+}
+
+template <int R>
+__attribute__((target("avx512f"))) inline void tile_avx512(const float *A, const float *Bt, int ld,
+                                                           int d, int j, float *S) {
+  __m512 c[R][2];
+  for (int r = 0; r < R; ++r) c[r][0] = c[r][1] = _mm512_setzero_ps();
+  for (int k = 0; k < d; ++k) {
+    const __m512 b0 = _mm512_loadu_ps(Bt + size_t(k) * ld + j);
+    const __m512 b1 = _mm512_loadu_ps(Bt + size_t(k) * ld + j + 16);
+    for (int r = 0; r < R; ++r) {
+      const __m512 a = _mm512_set1_ps(A[size_t(r) * d + k]);
+      c[r][0] = _mm512_fmadd_ps(a, b0, c[r][0]);
+      c[r][1] = _mm512_fmadd_ps(a, b1, c[r][1]);
     }
   }
+  for (int r = 0; r < R; ++r) {
+    _mm512_storeu_ps(S + size_t(r) * ld + j, c[r][0]);
+    _mm512_storeu_ps(S + size_t(r) * ld + j + 16, c[r][1]);
+  }
+}
+
+__attribute__((target("avx512f"))) void dots_avx512(const float *A, const float *Bt, int nA, int nB,
+                                                    int ld, int d, float *S) {
+  for (int j = 0; j < nB; j += 32) {  // 32 B columns per tile (ld covers the padding)
+    int i = 0;
+    for (; i + 12 <= nA; i += 12) tile_avx512<12>(A + size_t(i) * d, Bt, ld, d, j, S + size_t(i) * ld);
+    for (; i + 4 <= nA; i += 4) tile_avx512<4>(A + size_t(i) * d, Bt, ld, d, j, S + size_t(i) * ld);
+    for (; i < nA; ++i) tile_avx512<1>(A + size_t(i) * d, Bt, ld, d, j, S + size_t(i) * ld);
+  }
+}
+
+// Reciprocal norms 1 / max(|x|, 1e-12) of n rows (sum of squares in fp32).
+using NormsFn = void (*)(const float *, int, int, float *);
+// First b in [0, nB) with the largest (dots[b] * rb[b]) * ra (strict >, so the lowest b on
+// ties); returns b and the score.
+using BestFn = int (*)(const float *, const float *, float, int, float *);
+// a[e] = fma(w, x[e], a[e]) for e < d.
+using AxpyFn = void (*)(float, const float *, float *, int);
+
+void norms_scalar(const float *rows, int n, int d, float *inv) {
+  for (int i = 0; i < n; ++i) {
+    float ss = 0.f;
+    for (int k = 0; k < d; ++k) ss = std::fma(rows[size_t(i) * d + k], rows[size_t(i) * d + k], ss);
+    inv[i] = 1.0f / std::max(std::sqrt(ss), 1e-12f);
+  }
+}
+int best_scalar(const float *dots, const float *rb, float ra, int nB, float *score) {
+  float bs = -INFINITY;
+  int bi = 0;
+  for (int b = 0; b < nB; ++b) {
+    const float scv = (dots[b] * rb[b]) * ra;
+    if (scv > bs) {
+      bs = scv;
+      bi = b;
+    }
+  }
+  *score = bs;
+  return bi;
+}
+void axpy_scalar(float w, const float *x, float *a, int d) {
+  for (int e = 0; e < d; ++e) a[e] = std::fma(w, x[e], a[e]);
+}
+
+__attribute__((target("avx2,fma"))) void norms_avx2(const float *rows, int n, int d, float *inv) {
+  for (int i = 0; i < n; ++i) {
+    const float *x = rows + size_t(i) * d;
+    __m256 c0 = _mm256_setzero_ps(), c1 = c0;
+    for (int k = 0; k < d; k += 16) {
+      const __m256 a = _mm256_loadu_ps(x + k), b = _mm256_loadu_ps(x + k + 8);
+      c0 = _mm256_fmadd_ps(a, a, c0);
+      c1 = _mm256_fmadd_ps(b, b, c1);
+    }
+    inv[i] = 1.0f / std::max(std::sqrt(hsum256(_mm256_add_ps(c0, c1))), 1e-12f);
+  }
+}
+__attribute__((target("avx2,fma"))) int best_avx2(const float *dots, const float *rb, float ra,
+                                                  int nB, float *score) {
+  const __m256 vra = _mm256_set1_ps(ra), step = _mm256_set1_ps(8.f);
+  __m256 vbest = _mm256_set1_ps(-INFINITY), vidx = _mm256_setzero_ps();
+  __m256 lane = _mm256_setr_ps(0.f, 1.f, 2.f, 3.f, 4.f, 5.f, 6.f, 7.f);
+  int b = 0;
+  for (; b + 8 <= nB; b += 8) {  // per lane: the first index of its largest score
+    const __m256 sc = _mm256_mul_ps(_mm256_mul_ps(_mm256_loadu_ps(dots + b), _mm256_loadu_ps(rb + b)), vra);
+    const __m256 gt = _mm256_cmp_ps(sc, vbest, _CMP_GT_OQ);
+    vbest = _mm256_blendv_ps(vbest, sc, gt);
+    vidx = _mm256_blendv_ps(vidx, lane, gt);
+    lane = _mm256_add_ps(lane, step);
+  }
+  alignas(32) float bv[8], bi[8];
+  _mm256_store_ps(bv, vbest);
+  _mm256_store_ps(bi, vidx);
+  float bs = -INFINITY;
+  int best = 0;
+  for (int q = 0; q < 8; ++q)  // across lanes: the largest score, the lowest index on ties
+    if (bv[q] > bs || (bv[q] == bs && bv[q] != -INFINITY && int(bi[q]) < best)) {
+      bs = bv[q];
+      best = int(bi[q]);
+    }
+  for (; b < nB; ++b) {  // the tail, in order after every earlier index
+    const float scv = (dots[b] * rb[b]) * ra;
+    if (scv > bs) {
+      bs = scv;
+      best = b;
+    }
+  }
+  *score = bs;
+  return best;
+}
+__attribute__((target("avx2,fma"))) void axpy_avx2(float w, const float *x, float *a, int d) {
+  const __m256 vw = _mm256_set1_ps(w);
+  for (int e = 0; e < d; e += 8)
+    _mm256_storeu_ps(a + e, _mm256_fmadd_ps(vw, _mm256_loadu_ps(x + e), _mm256_loadu_ps(a + e)));
+}
+
+__attribute__((target("avx512f"))) void norms_avx512(const float *rows, int n, int d, float *inv) {
+  for (int i = 0; i < n; ++i) {
+    const float *x = rows + size_t(i) * d;
+    __m512 c = _mm512_setzero_ps();
+    for (int k = 0; k < d; k += 16) {
+      const __m512 a = _mm512_loadu_ps(x + k);
+      c = _mm512_fmadd_ps(a, a, c);
+    }
+    inv[i] = 1.0f / std::max(std::sqrt(_mm512_reduce_add_ps(c)), 1e-12f);
+  }
+}
+__attribute__((target("avx512f"))) int best_avx512(const float *dots, const float *rb, float ra,
+                                                   int nB, float *score) {
+  const __m512 vra = _mm512_set1_ps(ra);
+  __m512 vbest = _mm512_set1_ps(-INFINITY);
+  __m512i vidx = _mm512_setzero_si512();
+  __m512i lane = _mm512_setr_epi32(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  const __m512i step = _mm512_set1_epi32(16);
+  int b = 0;
+  for (; b + 16 <= nB; b += 16) {  // per lane: the first index of its largest score
+    const __m512 sc = _mm512_mul_ps(_mm512_mul_ps(_mm512_loadu_ps(dots + b), _mm512_loadu_ps(rb + b)), vra);
+    const __mmask16 gt = _mm512_cmp_ps_mask(sc, vbest, _CMP_GT_OQ);
+    vbest = _mm512_mask_mov_ps(vbest, gt, sc);
+    vidx = _mm512_mask_mov_epi32(vidx, gt, lane);
+    lane = _mm512_add_epi32(lane, step);
+  }
+  alignas(64) float bv[16];
+  alignas(64) int32_t bi[16];
+  _mm512_store_ps(bv, vbest);
+  _mm512_store_si512(bi, vidx);
+  float bs = -INFINITY;
+  int best = 0;
+  for (int q = 0; q < 16; ++q)  // across lanes: the largest score, the lowest index on ties
+    if (bv[q] > bs || (bv[q] == bs && bv[q] != -INFINITY && bi[q] < best)) {
+      bs = bv[q];
+      best = bi[q];
+    }
+  for (; b < nB; ++b) {  // the tail, in order after every earlier index
+    const float scv = (dots[b] * rb[b]) * ra;
+    if (scv > bs) {
+      bs = scv;
+      best = b;
+    }
+  }
+  *score = bs;
+  return best;
+}
+__attribute__((target("avx512f"))) void axpy_avx512(float w, const float *x, float *a, int d) {
+  const __m512 vw = _mm512_set1_ps(w);
+  for (int e = 0; e < d; e += 16)
+    _mm512_storeu_ps(a + e, _mm512_fmadd_ps(vw, _mm512_loadu_ps(x + e), _mm512_loadu_ps(a + e)));
 }
 
 struct Isa {
   DotsFn dots;
+  NormsFn norms;
+  BestFn best;
+  AxpyFn axpy;
   int code;  // CSMKV_HOST_ISA_*
 };
 
 Isa pick_isa() {
   __builtin_cpu_init();
-  if (__builtin_cpu_supports("avx512f")) return {dots_avx512, CSMKV_HOST_ISA_AVX512};
-  if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) return {dots_avx2, CSMKV_HOST_ISA_AVX2};
-  return {dots_scalar, CSMKV_HOST_ISA_SCALAR};
+  if (__builtin_cpu_supports("avx512f"))
+    return {dots_avx512, norms_avx512, best_avx512, axpy_avx512, CSMKV_HOST_ISA_AVX512};
+  if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma"))
+    return {dots_avx2, norms_avx2, best_avx2, axpy_avx2, CSMKV_HOST_ISA_AVX2};
+  return {dots_scalar, norms_scalar, best_scalar, axpy_scalar, CSMKV_HOST_ISA_SCALAR};
 }
 
 // ------------------------------------------------------------------ one round
@@ -223,13 +368,16 @@ struct Params {
   uint8_t *tap_sel;
   int32_t *tap_src;
   int64_t units;
-  DotsFn dots;
+  Isa isa;
 };
+
+// Row stride of the transposed B rows and of the products: nB rounded up to 32 columns.
+inline int ld_of(int nB) { return (nB + 31) / 32 * 32; }
 
 struct Scratch {  // per worker thread
   std::vector<char> k, v;
   std::vector<int32_t> n;
-  std::vector<float> af, bf, ra, rb, dots, acc, tmp, sc;
+  std::vector<float> af, bf, bt, ra, rb, dots, acc, tmp, sc;
   std::vector<int> best, src_list, src_cnt, src_off, outrow;
   std::vector<uint64_t> keys;
   std::vector<uint8_t> sel;
@@ -240,9 +388,10 @@ struct Scratch {  // per worker thread
     n.resize(c);
     af.resize(na * d);
     bf.resize(na * d);
+    bt.resize(d * ld_of(na));
     ra.resize(na);
     rb.resize(na);
-    dots.resize(na * na);
+    dots.resize(na * ld_of(na));
     acc.resize(2 * d);
     tmp.resize(d);
     sc.resize(na);
@@ -255,14 +404,6 @@ struct Scratch {  // per worker thread
     sel.resize(na);
   }
 };
-
-void inv_norms(const float *rows, int n, int d, float *inv) {
-  for (int i = 0; i < n; ++i) {
-    float ss = 0.f;
-    for (int k = 0; k < d; ++k) ss = std::fma(rows[size_t(i) * d + k], rows[size_t(i) * d + k], ss);
-    inv[i] = 1.0f / std::max(std::sqrt(ss), 1e-12f);
-  }
-}
 
 void round_slice(const Params &p, int64_t z, Scratch &w) {
   const int s = p.lens[z];
@@ -292,20 +433,18 @@ void round_slice(const Params &p, int64_t z, Scratch &w) {
     if (nB > 0) {
       for (int i = 0; i < nA; ++i) row_to_f32(w.k.data() + size_t(2 * i) * rowb, p.dtype, d, &w.af[size_t(i) * d]);
       for (int i = 0; i < nB; ++i) row_to_f32(w.k.data() + size_t(2 * i + 1) * rowb, p.dtype, d, &w.bf[size_t(i) * d]);
-      inv_norms(w.af.data(), nA, d, w.ra.data());
-      inv_norms(w.bf.data(), nB, d, w.rb.data());
-      p.dots(w.af.data(), w.bf.data(), nA, nB, d, w.dots.data());
+      p.isa.norms(w.af.data(), nA, d, w.ra.data());
+      p.isa.norms(w.bf.data(), nB, d, w.rb.data());
+      const int ld = ld_of(nB);
+      for (int k = 0; k < d; ++k) {  // B transposed, padding columns zero
+        float *col = &w.bt[size_t(k) * ld];
+        for (int b = 0; b < nB; ++b) col[b] = w.bf[size_t(b) * d + k];
+        for (int b = nB; b < ld; ++b) col[b] = 0.f;
+      }
+      p.isa.dots(w.af.data(), w.bt.data(), nA, nB, ld, d, w.dots.data());
       for (int i = 0; i < nA; ++i) {  // best B: ascending, strict >, so the lowest wins a tie
-        const float *row = &w.dots[size_t(i) * nB];
-        float bs = -INFINITY;
-        int bi = 0;
-        for (int b = 0; b < nB; ++b) {
-          const float scv = (row[b] * w.rb[b]) * w.ra[i];
-          if (scv > bs) {
-            bs = scv;
-            bi = b;
-          }
-        }
+        float bs;
+        const int bi = p.isa.best(&w.dots[size_t(i) * ld], w.rb.data(), w.ra[i], nB, &bs);
         w.best[i] = bi;
         w.sc[i] = bs;
         w.keys[i] = edge_key(bs, i);
@@ -346,7 +485,7 @@ void round_slice(const Params &p, int64_t z, Scratch &w) {
             const int ar = 2 * w.src_list[q];
             row_to_f32(rows + size_t(ar) * rowb, p.dtype, d, w.tmp.data());
             const float na = float(w.n[ar]);
-            for (int e = 0; e < d; ++e) a[e] = std::fma(na, w.tmp[e], a[e]);
+            p.isa.axpy(na, w.tmp.data(), a, d);
           }
           const float Wf = float(W);
           for (int e = 0; e < d; ++e) a[e] = a[e] / Wf;
@@ -424,7 +563,7 @@ int csm_compress_host(void *K, void *V, int32_t *N, int32_t *lens, const csmkv_c
   p.tap_src = src_pos;
   const int64_t Mmax = int64_t(cache->max_len) - n1 - n2;
   p.units = (Mmax >= 2 ? (Mmax + c - 1) / c : 0) + 1;  // the device round's tap layout
-  p.dots = pick_isa().dots;
+  p.isa = pick_isa();
   if (best_b) {
     int64_t need = 0;  // every slice's chunks must fit the tap layout of max_len
     for (int64_t z = 0; z < p.S; ++z)

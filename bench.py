@@ -691,9 +691,31 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
         sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps, g=w.g, n1=w.n1, n2=w.n2, c=w.c)
         rs = sched.prefill_rounds()
     stream = torch.cuda.current_stream(dev)
+    n_comp = int((maskh == 0).sum())
+    # round 0 by itself, as the headline round is timed: in place on a copy restored before every
+    # rep, the last-level cache flushed, the first rep not counted (when two copies fit in HBM)
+    round0_reps = None
+    cache_bytes = sum(t.numel() * t.element_size() for t in (K, V, N, L))
+    if 2 * cache_bytes < 160 * 2 ** 30:
+        Kc, Vc, Nc, Lc = (t.clone() for t in (K, V, N, L))
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        reps = []
+        for rep in range(4):
+            for dst, src in ((Kc, K), (Vc, V), (Nc, N), (Lc, L)):
+                dst.copy_(src)
+            flush.fill_(rep)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lib.csm_compress(Kc, Vc, Nc, Lc, w.n1, w.n2, w.c, rs[0], mask if maskh.any() else None,
+                             max_len=w.ctx, workspace=ws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1))
+        round0_reps = reps[1:]
+        del Kc, Vc, Nc, Lc, flush
+        torch.cuda.empty_cache()
     rounds = []
     s = w.ctx
-    n_comp = int((maskh == 0).sum())
     for r in rs:
         s2 = round_output_length(s, w.n1, w.n2, w.c, r)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -709,9 +731,19 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
         s = s2
     assert lib.read_error(ws) == lib.OK
     assert int(L[int(np.argmin(maskh))]) == s
+    r0 = dict(rounds[0])
+    if round0_reps:
+        r0["first_call_ms"] = r0["ms"]  # the prefill sequence's own first round (cold)
+        alg0 = n_comp * ((w.ctx - w.n1) + (r0["s_out"] - w.n1)) * row
+        r0["ms"] = sum(round0_reps) / len(round0_reps)
+        r0["min_ms"] = min(round0_reps)
+        r0["GBps"] = alg0 / r0["ms"] / 1e6
+        r0["slice_tokens_per_s"] = n_comp * w.ctx / (r0["ms"] * 1e-3)
+        r0["timing"] = (f"mean of {len(round0_reps)} reps in place on a restored copy, last-level "
+                        "cache flushed before each, after one untimed rep")
     out = {"workload": w.name, "slices": S, "dtype": w.dtype, "d": w.d, "c": w.c, "G": w.G,
            "ctx": w.ctx,
-           "round0": rounds[0],
+           "round0": r0,
            "prefill": {"rounds": len(rounds), "len": s, "ms": sum(x["ms"] for x in rounds),
                        "GBps": sum(n_comp * ((x["s_in"] - w.n1) + (x["s_out"] - w.n1)) * row
                                    for x in rounds) / sum(x["ms"] for x in rounds) / 1e6}}

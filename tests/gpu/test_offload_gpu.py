@@ -5,9 +5,9 @@ the device over the result.
 CentroidKV page, 它做不到的事（局限性） → 仍留在 GPU 上: grouping on the CPU, only the result sent to
 the GPU.  Checked: the device cache after the upload equals the host result bit for bit (rows
 [0, lens), lengths; outlier slices and rows before row_begin untouched); the host round and the
-device round (csm_compress_debug on a copy) both pass the oracle protocol and agree everywhere
-except in chunks where one of them took a near-tie the other did not; decode attention over the
-uploaded cache matches the oracle.
+device round (csm_compress_debug on a copy) both pass the oracle protocol, and their decisions
+are identical in every slice where neither met a near-tie; decode attention over the uploaded
+cache matches the oracle.
 """
 import numpy as np
 import pytest
@@ -55,21 +55,30 @@ def test_offload_round_trip_64k_slices(lib, dev):
                                                       mask.to(dev), max_len=w.ctx)
     assert lib.read_error(ws) == lib.OK
     rep_h, rep_g = parity.Report(), parity.Report()
-    same_slices = 0
+    same_slices = tie_slices = 0
     for z in range(S):
         if mask[z]:
             continue
         args = (parity.to_f64(Kin[z]), parity.to_f64(Vin[z]), Nin[z].numpy().astype(np.int64),
                 int(lin[z]), w.n1, w.n2, w.c, w.r_init, "bf16")
-        parity.compare_slice(rep_h, *args, best_h[z].numpy(), sel_h[z].numpy(), src_h[z].numpy(),
+        zh, zg = parity.Report(), parity.Report()
+        parity.compare_slice(zh, *args, best_h[z].numpy(), sel_h[z].numpy(), src_h[z].numpy(),
                              parity.to_f64(Kh[z]), parity.to_f64(Vh[z]),
                              Nh[z].numpy().astype(np.int64), int(Lh[z]))
-        parity.compare_slice(rep_g, *args, best_g[z].cpu().numpy(), sel_g[z].cpu().numpy(),
+        parity.compare_slice(zg, *args, best_g[z].cpu().numpy(), sel_g[z].cpu().numpy(),
                              src_g[z].cpu().numpy(), parity.to_f64(Kg[z].cpu()),
                              parity.to_f64(Vg[z].cpu()), Ng[z].cpu().numpy().astype(np.int64),
                              int(Lg[z]))
+        rep_h.add(zh)
+        rep_g.add(zg)
         s = int(Lh[z])
-        if (torch.equal(best_h[z], best_g[z].cpu()) and torch.equal(sel_h[z], sel_g[z].cpu())):
+        same = torch.equal(best_h[z], best_g[z].cpu()) and torch.equal(sel_h[z], sel_g[z].cpu())
+        if zh.match_near + zh.sel_near + zg.match_near + zg.sel_near == 0:
+            # neither round met a near-tie in this slice: both took the definition's decisions
+            assert same, z
+        else:
+            tie_slices += 1
+        if same:
             same_slices += 1
             assert torch.equal(Nh[z, :s], Ng[z, :s].cpu())
             # merged values: host divides, the device multiplies by a reciprocal; both within
@@ -78,10 +87,9 @@ def test_offload_round_trip_64k_slices(lib, dev):
             gk = parity.to_f64(Kg[z, :s].cpu()).ravel()
             assert parity.max_ulp_bf16(hk, gk) <= 2
     print("host round:", rep_h, "\ndevice round:", rep_g, "\nslices with identical decisions:",
-          same_slices)
+          same_slices, "slices with a near-tie on either side:", tie_slices)
     parity.check_report(rep_h)
     parity.check_report(rep_g)
-    assert same_slices >= int((mask == 0).sum()) - 3
     # decode attention on the device over the uploaded cache
     H_kv, G = 1, 4
     q = torch.randn((S, G, 128), generator=torch.Generator(device=dev).manual_seed(5),

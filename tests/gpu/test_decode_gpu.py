@@ -507,3 +507,30 @@ def test_rows_of_degree_zero_weigh_nothing(lib, dev, dtype):
     err = float(np.abs(O - ref).max())
     print(dtype, "max abs", err)
     assert err < (2e-5 if dtype == torch.float32 else 2e-4)
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 130])
+def test_slice_counts_around_the_wave_plan_limit(lib, dev, S):
+    """Calls over at most 64 slices plan inside each wave (lane z holds slice z), larger ones
+    through LDS: ragged lengths with empty slices on both sides of the limit, every slice against
+    the oracle, and a bad length in the last slice (lane 63 at S = 64) reported and zeroed."""
+    rng = np.random.default_rng(S)
+    cap = 900
+    lens = [int(x) for x in rng.choice([0, 1, 17, 256, 257, 511, 900], size=S)]
+    K, V, N, L = host_cache(S, cap, lens, seed=S, degrees=True)
+    q = torch.randn((S, 4, 128), generator=torch.Generator().manual_seed(S)).to(torch.bfloat16)
+    Kd, Vd, Nd, Ld, qd = K.to(dev), V.to(dev), N.to(dev), L.to(dev), q.to(dev)
+    O = lib.decode_attn_logn(qd, Kd, Vd, Nd, Ld, 4, 1)
+    ref = _oracle_all(q, K, V, N, L, 4, 1)
+    err = np.abs(O.cpu().double().numpy() - ref).max()
+    print(S, "max abs", err)
+    assert err < 2e-4
+    bad = Ld.clone()
+    bad[S - 1] = cap + 1
+    ws = lib.new_workspace(lib.decode_workspace_bytes(Kd, 4, 1), dev)
+    O2 = lib.decode_attn_logn(qd, Kd, Vd, Nd, bad, 4, 1, workspace=ws)
+    assert lib.read_error(ws) == lib.EDEVICE
+    assert torch.all(O2[S - 1] == 0)
+    if S > 1:
+        assert torch.equal(O2[:S - 1], O[:S - 1]) or np.abs(
+            O2[:S - 1].cpu().double().numpy() - ref[:S - 1]).max() < 2e-4

@@ -23,7 +23,10 @@
  *     K and V must be 16-byte aligned.  Rows at or beyond lens[] are ignored.
  *   - Device-side errors (a lens[] entry above max_len or cap) are reported through an
  *     int32 error word in device memory, read with csmkv_read_error().  The affected
- *     slice is left unchanged (compress, append) or produces zeros (attention).  The word
+ *     slice is left unchanged (compress, append) or produces zeros (attention).  An in-place
+ *     round also sets it if a workgroup's wait for another chunk of its slice does not end
+ *     within about a second (the output of that slice is then incomplete); the waits end by
+ *     construction, so this only turns a fault that would hang the launch into an error.  The word
  *     is sticky: kernels only ever set it (to CSMKV_EDEVICE), never clear it, so a loop or a
  *     graph replay of many calls reports an error from any of them.  It must hold 0 before
  *     the first call (allocate the workspace zeroed, or call csmkv_clear_error) and is
@@ -54,7 +57,8 @@ typedef enum {
   CSMKV_EUNSUPPORTED = -3,  /* shape outside what the kernels are built for */
   CSMKV_EWORKSPACE = -4,    /* workspace NULL, misaligned or smaller than required */
   CSMKV_EHIP = -5,          /* a HIP runtime call or kernel launch failed */
-  CSMKV_EDEVICE = -6        /* csmkv_read_error: a kernel flagged a bad lens[] entry */
+  CSMKV_EDEVICE = -6        /* csmkv_read_error: a kernel flagged a bad lens[] entry (or a
+                               round's in-place wait that did not end) */
 } csmkv_status;
 
 /* Storage formats of K, V (and q).  bf16 is the format the pages use; fp16 (IEEE binary16)

@@ -188,9 +188,16 @@ __device__ void copy_rows(const char *Ks, const char *Vs, const int32_t *Ns, cha
   }
 }
 
-__device__ __forceinline__ void wait_flag(const int32_t *f) {
-  while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+// Waits until *f is set by another workgroup; false if it is not set within kFlagPolls polls
+// (about a second, against the microseconds a wait takes), so that a wait that cannot end turns
+// into a reported error instead of a hung launch.
+constexpr uint32_t kFlagPolls = 1u << 24;
+__device__ __forceinline__ bool wait_flag(const int32_t *f) {
+  for (uint32_t i = 0; i < kFlagPolls; ++i) {
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
     __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
 }
 
 }  // namespace csmkv

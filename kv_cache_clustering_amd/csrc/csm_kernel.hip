@@ -108,16 +108,24 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
     return;
   }
   const int n1 = a.n1, n2 = a.n2, c = a.c;
+  __shared__ int s_stuck;
   if (!a.in_place) copy_rows<T, NT, D>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
+  if (t == 0) s_stuck = 0;
   if (a.in_place && !outl && t == 0) {
     // the recent rows land in [s_new - n2, s_new): wait for chunks whose sources overlap it
     const int d0 = s_new - n2, d1 = s_new;
     if (d1 > d0) {
       const int lo = (d0 - n1) / c, hi = min(nch - 1, (d1 - 1 - n1) / c);
-      for (int i = lo; i <= hi; ++i) wait_flag(a.flags + z * a.units + i);
+      bool ok = true;
+      for (int i = lo; i <= hi && ok; ++i) ok = wait_flag(a.flags + z * a.units + i);
+      if (!ok) {  // a wait that did not end: report it and leave the rows unwritten
+        atomicExch(a.err, kDeviceError);
+        s_stuck = 1;
+      }
     }
   }
   __syncthreads();
+  if (s_stuck) return;
   const int64_t so = (int64_t)(s - n2), dof = (int64_t)(s_new - n2);
   copy_rows<T, NT, D>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
                Vd + dof * TL::ROWB, Nd + dof, n2);
@@ -423,9 +431,15 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   if (a.in_place && t == 0) {
     // destination rows [base, base + nout) overlap the sources of chunks lo..j
     const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
-    for (int i = lo; i <= hi; ++i) wait_flag(a.flags + z * a.units + i);
+    bool ok = true;
+    for (int i = lo; i <= hi && ok; ++i) ok = wait_flag(a.flags + z * a.units + i);
+    if (!ok) {  // a wait that did not end: report it and leave the chunk's rows unwritten
+      atomicExch(a.err, kDeviceError);
+      s_misc[0] = -1;
+    }
   }
   __syncthreads();
+  if (s_misc[0] == -1) return;
 
   if (a.tap_best != nullptr && t < NA) {
     const int64_t o = (z * a.units + j) * NA + t;

@@ -368,13 +368,19 @@ __device__ __forceinline__ void dot_row(const char *row, const float (*s_q)[D], 
 }
 
 // One workgroup per slice: thresholds from the reference rows, the walk, the runs of kept blocks.
+// Trees of at most kEagerNodes nodes have every node's test evaluated in one parallel pass and
+// are then walked over the resulting bits (a leaf is kept when it and every ancestor passed: the
+// same set as the level-by-level walk, whose dependent loads per level it avoids); larger trees
+// are walked level by level, evaluating only the nodes whose parent passed.
 constexpr int kSelThreads = 512;
+constexpr int kEagerNodes = 4096;
 template <typename T, int G, int D>
 __global__ void __launch_bounds__(kSelThreads) prune_select(IdxArgs a) {
   constexpr int RB = D * (int)sizeof(T);
   constexpr int NW = kSelThreads / 64;
   __shared__ float s_q[G][D], s_qn[G], s_th[NW][G];
   __shared__ uint32_t s_vis[2][kPruneMaxLeaves / 32];
+  __shared__ uint32_t s_pass[kEagerNodes / 32];
   __shared__ int32_t s_cnt[NW], s_cnt2[NW];
   const int64_t z = blockIdx.x;
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
@@ -428,7 +434,10 @@ __global__ void __launch_bounds__(kSelThreads) prune_select(IdxArgs a) {
     if (l == 0) s_th[w][h] = m;
   }
   const int pw = (a.P + 31) / 32;  // words of a level's bits
+  const bool eager = 2 * a.P <= kEagerNodes;
   for (int i = t; i < pw; i += kSelThreads) s_vis[0][i] = s_vis[1][i] = 0u;
+  if (eager)
+    for (int i = t; i < (2 * a.P + 31) / 32; i += kSelThreads) s_pass[i] = 0u;
   __syncthreads();
   float th[G];
 #pragma unroll
@@ -438,38 +447,56 @@ __global__ void __launch_bounds__(kSelThreads) prune_select(IdxArgs a) {
     for (int ww = 1; ww < NW; ++ww) m = fmaxf(m, s_th[ww][h]);
     th[h] = m - a.tau_log2;
   }
-  // the walk: level `span` holds nodes [span, 2 span); a visited node that passes marks its
-  // children (next level) visited, or, at the leaves, keeps its block
-  if (t == 0 && v.wt[1] > 0) s_vis[0][0] = 1u;  // the root, bit 0 of level 1
-  __syncthreads();
+  // a node's test: its bound reaches the threshold for one of the heads (empty nodes never pass)
+  auto passes = [&](int u) {
+    const float rr = v.rho[u], lm = v.lmax[u];
+    float dq[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) dq[h] = 0.f;
+    dot_row<float, G, D>(reinterpret_cast<const char *>(v.mu + (int64_t)u * D), s_q, dq);
+    bool pass = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) pass |= fmaf(fmaf(s_qn[h], rr, dq[h]), a.scale_log2, lm) >= th[h];
+    return pass;
+  };
   int cur = 0;
-  for (int span = 1; span <= a.P; span *= 2) {
-    const bool leaves = span == a.P;
+  if (eager) {
 #pragma unroll 1
-    for (int i = t; i < span; i += kSelThreads) {
-      if (!((s_vis[cur][i >> 5] >> (i & 31)) & 1u)) continue;
-      const int u = span + i;
-      const float rr = v.rho[u], lm = v.lmax[u];
-      bool pass = false;
-      float dq[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) dq[h] = 0.f;
-      dot_row<float, G, D>(reinterpret_cast<const char *>(v.mu + (int64_t)u * D), s_q, dq);
-#pragma unroll
-      for (int h = 0; h < G; ++h) pass |= fmaf(fmaf(s_qn[h], rr, dq[h]), a.scale_log2, lm) >= th[h];
-      if (!pass) continue;
-      if (leaves) {
-        atomicOr(&s_vis[cur ^ 1][i >> 5], 1u << (i & 31));  // reused below as the kept set
-      } else {
-        for (int c = 0; c < 2; ++c)
-          if (v.wt[2 * u + c] > 0) atomicOr(&s_vis[cur ^ 1][(2 * i + c) >> 5], 1u << ((2 * i + c) & 31));
-      }
+    for (int u = 1 + t; u < 2 * a.P; u += kSelThreads)
+      if (v.wt[u] > 0 && passes(u)) atomicOr(&s_pass[u >> 5], 1u << (u & 31));
+    __syncthreads();
+    for (int b = t; b < a.P; b += kSelThreads) {  // the walk over the bits, from the leaf up
+      bool k = true;
+      for (int u = a.P + b; u >= 1 && k; u >>= 1) k = (s_pass[u >> 5] >> (u & 31)) & 1u;
+      if (k) atomicOr(&s_vis[1][b >> 5], 1u << (b & 31));
     }
     __syncthreads();
-    if (!leaves) {
-      for (int i = t; i < pw; i += kSelThreads) s_vis[cur][i] = 0u;
-      cur ^= 1;
+  } else {
+    // the walk: level `span` holds nodes [span, 2 span); a visited node that passes marks its
+    // children (next level) visited, or, at the leaves, keeps its block
+    if (t == 0 && v.wt[1] > 0) s_vis[0][0] = 1u;  // the root, bit 0 of level 1
+    __syncthreads();
+    for (int span = 1; span <= a.P; span *= 2) {
+      const bool leaves = span == a.P;
+#pragma unroll 1
+      for (int i = t; i < span; i += kSelThreads) {
+        if (!((s_vis[cur][i >> 5] >> (i & 31)) & 1u)) continue;
+        const int u = span + i;
+        if (!passes(u)) continue;
+        if (leaves) {
+          atomicOr(&s_vis[cur ^ 1][i >> 5], 1u << (i & 31));  // reused below as the kept set
+        } else {
+          for (int c = 0; c < 2; ++c)
+            if (v.wt[2 * u + c] > 0)
+              atomicOr(&s_vis[cur ^ 1][(2 * i + c) >> 5], 1u << ((2 * i + c) & 31));
+        }
+      }
       __syncthreads();
+      if (!leaves) {
+        for (int i = t; i < pw; i += kSelThreads) s_vis[cur][i] = 0u;
+        cur ^= 1;
+        __syncthreads();
+      }
     }
   }
   uint32_t *kept = s_vis[cur ^ 1];

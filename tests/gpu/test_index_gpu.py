@@ -279,3 +279,29 @@ def test_pruned_decode_bad_length_and_ar1_keys(lib, dev):
     O2, _, ws2 = lib.decode_attn_logn_pruned(q, K, V, N, L2, H_q, H_kv, index, 8.0, max_len=3000)
     assert lib.read_error(ws2) == lib.EDEVICE
     assert torch.all(O2[0, 4:] == 0)
+
+
+def test_pruned_decode_deep_trees_walk_level_by_level(lib, dev):
+    """Trees of more than 4096 nodes are walked level by level, evaluating only the nodes whose
+    parent passed (smaller ones evaluate every node at once and walk the bits): 16-row blocks
+    over 40000-row slices (4096 leaf slots), kept blocks and outputs against the oracle."""
+    B, H_kv, G = 16, 2, 4
+    lens = [40000, 2500, 0, 33333]
+    K, V, N, L, q = _setup(dev, "bf16", 128, B, 0.05, seed=77, lens=lens, cap=40000,
+                           H_q=G * H_kv, H_kv=H_kv)
+    index = lib.new_index(K, B)
+    assert lib.index_leaf_slots(40000, B) == 4096
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib.index_build(K, N, L, index, err, B)
+    assert lib.read_error(err) == lib.OK
+    total_dropped = 0
+    for tau in (2.0, float("inf")):
+        dropped, near, differ, wf, wfull, ok = _compare_pruned(lib, K, V, N, L, q, index, tau, B,
+                                                               16, 64, G * H_kv, H_kv)
+        print("deep tree, tau", tau, "dropped rows", dropped, "near-threshold differences", near,
+              "vs oracle (device's rows)", wf, "vs full", wfull)
+        assert wf < 2e-4 and ok
+        if tau == float("inf"):
+            assert dropped == 0 and wfull < 2e-4
+        total_dropped += dropped
+    assert total_dropped > 0

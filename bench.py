@@ -81,13 +81,10 @@ def csm_bytes(lens_in, lens_out, mask, n1):
                for s, s2, m in zip(lens_in, lens_out, mask) if not m)
 
 
-def csm_copy_bytes(lens_in, lens_out, mask):
-    """Bytes the out-of-place round moves besides the algorithmic ones: the sink rows of every
-    compressed slice (read and written) and whole outlier slices (read and written)."""
-    total = 0
-    for s, s2, m in zip(lens_in, lens_out, mask):
-        total += 2 * s * ROW_BYTES if m else 0
-    return total
+def csm_copy_bytes(lens_in, mask, n1):
+    """Bytes the out-of-place round moves besides the algorithmic ones: the n1 sink rows of every
+    compressed slice and every row of the outlier slices, each read once and written once."""
+    return sum(2 * (s if m else n1) * ROW_BYTES for s, m in zip(lens_in, mask))
 
 
 def main():
@@ -287,7 +284,7 @@ def main():
     assert lib.read_error(ws_c) == lib.OK
     assert torch.equal(Lw, Li)
     oop_avg = sum(oop_ms) / len(oop_ms)
-    oop_copy = csm_copy_bytes(lens_in, lens_out, maskh) + 2 * w.n1 * ROW_BYTES * int((maskh == 0).sum())
+    oop_copy = csm_copy_bytes(lens_in, maskh, w.n1)
     del Kw, Vw, Nw, Lw
 
     # decode as the serving loop runs it (append + attention, step after step): wall time per

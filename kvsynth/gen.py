@@ -5,7 +5,7 @@ so any subset of slices can be regenerated on its own.  Large caches are generat
 with torch on the target device (fp32, then rounded to the storage type); tiny ones
 for CPU tests with numpy.
 
-Data recipe (stated once more in the design doc):
+Data recipe:
   keys   k_0 ~ N(0, I); k_t = rho * k_{t-1} + sigma * eps_t, eps_t ~ N(0, I); sigma
          defaults to sqrt(1 - rho^2) (unit stationary variance); rho is fixed or drawn
          uniformly per (layer, kv head); an optional per-(layer, kv head) mean vector

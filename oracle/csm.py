@@ -12,7 +12,7 @@ TEST INFRASTRUCTURE ONLY (see the package header).  Written from:
     聚合: degree-weighted averaging of keys and values into one centroid, the degree
     accumulating over rounds.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * A = chunk offsets 0, 2, 4, ... (the theorem's 1-indexed odd positions), B = offsets
     1, 3, 5, ...; A tokens are the sources that disappear, B tokens the targets that stay.
   * Chunks tile the middle [n1, s - n2) from n1; the last chunk may be shorter (length

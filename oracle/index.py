@@ -9,7 +9,7 @@ recent block; the upper centroids are recomputed lazily), applied to the cache t
 Matching leaves (rows k, v with degrees N; Chelsea review, section 三, 核心公式 for log-N
 attention).
 
-Readings (each also listed in the design doc; the page gives only this outline):
+Readings (the page gives only this outline):
   * Blocks are fixed runs of B consecutive rows of a slice (the page's boundary detector needs
     a model and is not built).  Block b holds rows [bB, min((b+1)B, s)).
   * A node is a ball: centre mu = degree-weighted mean of its keys (a leaf) or of its children's

@@ -26,3 +26,22 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU only" in p.stderr
+
+
+def test_round_byte_counts():
+    """The roofline's algorithmic bytes: a compressed slice reads its rows after the sinks once
+    and writes its kept rows once, an outlier slice counts nothing; the out-of-place extras are
+    the sinks of compressed slices and every row of outlier slices, read and written."""
+    import bench
+    from oracle import schedule as osched
+    row = 2 * 128 * 2 + 4
+    assert bench.ROW_BYTES == row
+    lens_in = [65536, 65536, 1000]
+    s_out = osched.round_length(65536, 16, 64, 256, 0.5)
+    lens_out = [s_out, 65536, osched.round_length(1000, 16, 64, 256, 0.5)]
+    mask = [0, 1, 0]
+    want = ((65536 - 16) + (s_out - 16)) * row + ((1000 - 16) + (lens_out[2] - 16)) * row
+    assert bench.csm_bytes(lens_in, lens_out, mask, 16) == want
+    assert bench.csm_copy_bytes(lens_in, mask, 16) == 2 * (16 + 65536 + 16) * row
+    # the 64K workload's round: 246 compressed slices, 14.5565 GB
+    assert bench.csm_bytes([65536] * 256, [s_out] * 256, [0] * 246 + [1] * 10, 16) == 14556512736

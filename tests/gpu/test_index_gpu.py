@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import kvsynth
 from oracle import attention as oatt
 from oracle import index as oix
 from tests import parity
@@ -305,3 +306,70 @@ def test_pruned_decode_deep_trees_walk_level_by_level(lib, dev):
             assert dropped == 0 and wfull < 2e-4
         total_dropped += dropped
     assert total_dropped > 0
+
+
+def test_index_and_pruned_decode_full_size_sampled(lib, dev):
+    """The launch configuration the benchmark times: the 64K workload's serving geometry (246
+    slices of 13,081 rows and 10 outlier slices of 65,536, capacity for the decode appends,
+    64-row blocks, 2048 leaf slots), its queries, tau = 8.  Sampled slices (two compressed, one
+    outlier): the built tree node by node against the oracle's build, the kept blocks against
+    the oracle's walk over the same bounds, and the output against the oracle's attention over
+    the kept rows; every slice's output against the plain call."""
+    w = kvsynth.workload(4)
+    c = kvsynth.make_cache(w, dev, with_appends=False)
+    K, V, N, mask = c["K"], c["V"], c["N"], c["mask"]
+    maskh = mask.cpu().numpy()
+    L = torch.tensor(np.where(maskh != 0, w.ctx, 13081).astype(np.int32), device=dev)
+    q = kvsynth.make_queries(w, dev, steps=1)[0]
+    B, tau = 64, 8.0
+    S, cap, d = K.shape
+    P = lib.index_leaf_slots(cap, B)
+    index = lib.new_index(K, B)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib.index_build(K, N, L, index, err, B)
+    assert lib.read_error(err) == lib.OK
+    O, kept, ws = lib.decode_attn_logn_pruned(q, K, V, N, L, w.H_q, w.H_kv, index, tau, w.n1, w.n2,
+                                              B, kept=True)
+    assert lib.read_error(ws) == lib.OK
+    plain = lib.decode_attn_logn(q, K, V, N, L, w.H_q, w.H_kv)
+    print("full size: max |pruned - plain|", float((O - plain).abs().max()))
+    assert float((O - plain).abs().max()) < 1e-5
+    G = w.H_q // w.H_kv
+    nodes = 2 * P
+    out = [int(np.argmin(maskh)), 137, int(np.argmax(maskh))]
+    ib = index.view(torch.uint8)
+    al = lambda x: (x + 255) // 256 * 256
+    o_rho = al(S * nodes * d * 4)
+    o_lmax = o_rho + al(S * nodes * 4)
+    o_wt = o_lmax + al(S * nodes * 4)
+    for z in out:
+        s = int(L[z])
+        mu = ib[z * nodes * d * 4:(z + 1) * nodes * d * 4].cpu().numpy().view(np.float32).reshape(nodes, d)
+        rho = ib[o_rho + z * nodes * 4:o_rho + (z + 1) * nodes * 4].cpu().numpy().view(np.float32)
+        lmax = ib[o_lmax + z * nodes * 4:o_lmax + (z + 1) * nodes * 4].cpu().numpy().view(np.float32)
+        wt = ib[o_wt + z * nodes * 4:o_wt + (z + 1) * nodes * 4].cpu().numpy().view(np.int32)
+        K64 = parity.to_f64(K[z, :s].cpu())
+        V64 = parity.to_f64(V[z, :s].cpu())
+        N64 = N[z, :s].cpu().numpy().astype(np.int64)
+        ref = oix.build(K64, N64, s, B, cap=cap)
+        assert ref["P"] == P
+        used = ref["wt"] > 0
+        assert np.array_equal(wt[1:], ref["wt"][1:].astype(np.int32)), z
+        np.testing.assert_allclose(mu[1:][used[1:]], ref["mu"][1:][used[1:]], rtol=1e-5, atol=1e-5)
+        r_dev, r_ref = rho[1:][used[1:]], ref["rho"][1:][used[1:]]
+        assert np.all(r_dev >= r_ref * (1 - 1e-6) - 1e-6) and np.all(r_dev <= r_ref * (1 + 1e-4) + 1e-5)
+        np.testing.assert_allclose(lmax[1:][used[1:]], ref["lmax"][1:][used[1:]], atol=1e-5)
+        g, kvh = divmod(z, w.H_kv)
+        qs = parity.to_f64(q[g, kvh * G:(kvh + 1) * G].cpu())
+        T = oix.thresholds(qs, K64, N64, s, w.n1, w.n2, tau, B)
+        ref_keep = oix.kept_tree(ref, qs, T, oix.protected_blocks(s, w.n1, w.n2, B))
+        dev_keep = kept[z, :ref["nleaf"]].cpu().numpy().astype(bool)
+        assert not kept[z, ref["nleaf"]:].cpu().numpy().any()
+        for b in np.nonzero(dev_keep != ref_keep)[0]:
+            margin = max(oix.bound(ref, P + b, qq) - t for qq, t in zip(qs, T))
+            assert abs(margin) < NEAR, ("kept block differs", z, b, margin)
+        rows = oix.kept_rows(dev_keep, s, B)
+        for h in range(G):
+            want = oatt.logn_attention_one(qs[h], K64[rows], V64[rows], N64[rows])
+            assert float(np.abs(O[g, kvh * G + h].cpu().double().numpy() - want).max()) < 2e-4
+        print("slice", z, "rows", s, "kept blocks", int(dev_keep.sum()), "of", ref["nleaf"])

@@ -145,3 +145,41 @@ def test_lazy_appends_keep_bounds_valid_and_contain_a_rebuild():
             lazy = oix.kept_tree(idx, qs, T, forced)
             reb = oix.kept_tree(fresh, qs, T, forced)
             assert np.all(lazy[reb]), "lazy bounds dropped a block a rebuild keeps"
+
+
+def test_hand_worked_tree_and_lazy_appends(golden_dir):
+    """A four-row tree with unequal degrees (degree-weighted centres), its bounds for one query,
+    and two lazy appends (a new leaf, then a widened one), against values worked out by hand."""
+    import json
+    import os
+    with open(os.path.join(golden_dir, "index_tiny_case.json")) as f:
+        case = json.load(f)
+    K = np.array(case["K"], np.float64)
+    N = np.array(case["N"], np.int64)
+    B, cap = case["B"], case["cap"]
+    rows = np.zeros((cap, case["d"]))
+    rows[:len(K)] = K
+    degs = np.zeros(cap, np.int64)
+    degs[:len(N)] = N
+    idx = oix.build(rows, degs, case["s"], B, cap=cap)
+    exp = case["build"]
+    assert idx["P"] == exp["P"]
+
+    def check(e):
+        for u, v in e.get("wt", {}).items():
+            assert idx["wt"][int(u)] == v, ("wt", u)
+        for u, v in e.get("mu", {}).items():
+            assert np.allclose(idx["mu"][int(u)], v, atol=1e-12), ("mu", u)
+        for u, v in e.get("rho", {}).items():
+            assert idx["rho"][int(u)] == pytest.approx(v, abs=1e-12), ("rho", u)
+        for u, v in e.get("lmax", {}).items():
+            assert idx["lmax"][int(u)] == pytest.approx(v, abs=1e-12), ("lmax", u)
+    check(exp)
+    q = np.array(exp["bound_q"], np.float64)
+    for u, v in exp["bound"].items():
+        assert oix.bound(idx, int(u), q) == pytest.approx(v, abs=1e-12)
+    for ap in case["appends"]:
+        rows[ap["s"] - 1] = ap["row"]
+        degs[ap["s"] - 1] = ap["n"]
+        oix.append_lazy(idx, np.array(ap["row"], np.float64), ap["n"], ap["s"])
+        check(ap["expect"])

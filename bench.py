@@ -91,7 +91,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path "
-              "shards by slice with no exchange, and no multi-GPU run is part of this build.",
+              "shards by slice with no exchange, and this benchmark measures one GPU's share.",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

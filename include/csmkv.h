@@ -99,7 +99,8 @@ CSMKV_API size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t 
  *   rows from n1 (the last may be shorter, length L); in each chunk A = even offsets,
  *   B = odd offsets; every A row takes the B row of highest key cosine similarity (lowest
  *   B index on ties); the A rows are ranked by that similarity (descending, lower A index
- *   first on ties) and the first m = floor(r*L/2) merge into their targets:
+ *   first on ties) and the first m = floor(r*L/2 + 1e-9) merge into their targets (fp64;
+ *   the guard keeps an r*L/2 meant to be whole from rounding below it; m = 0 when L < 2):
  *   k_b <- (N_b k_b + sum N_a k_a) / (N_b + sum N_a), same for v, N_b <- N_b + sum N_a,
  *   accumulated in fp32 in ascending A order and stored with round-to-nearest-even;
  *   merged A rows are removed and the slice is compacted in its original order;

@@ -43,8 +43,10 @@ Readings (the page gives only this outline):
 Pins (tests/oracle/test_index.py): every row's logit is below its leaf's and every ancestor's
 bound (brute force); the tree walk keeps exactly the leaves the direct test keeps; tau = inf
 gives full log-N attention; the dropped-mass error bound holds; after lazy appends the bounds
-stay valid and the kept set contains a fresh rebuild's.  Values of the index at specific inputs:
-parity unpinned (the page prints none).
+stay valid and the kept set contains a fresh rebuild's; a four-row tree with unequal degrees,
+worked by hand from the definitions above (tests/golden/index_tiny_case.json), fixes its centres,
+radii, largest log-degrees, two bounds and two lazy appends.  Values at generic inputs beyond
+these pins: parity unpinned (the page prints no worked example).
 """
 
 import numpy as np

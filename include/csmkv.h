@@ -291,7 +291,8 @@ CSMKV_API int csm_upload_rows(const void *K_host, const void *V_host, const int3
  * radius covering both child balls), in heap order over P leaf slots, P = the power of two that
  * holds cap / block_rows blocks (at most 65536).  block_rows: 16, 32, 64, 128 or 256.
  * Index memory (device, caller-owned, 256-byte aligned): csm_index_bytes() bytes, laid out as
- * centres [num_slices][2P][d] fp32, radii, largest log2 degree and degree totals [num_slices][2P].
+ * centres [num_slices][2P][d] fp32, radii, largest log2 degree and degree totals [num_slices][2P],
+ * then a work table the build fills and reads (one 16-byte entry per group of eight leaf slots).
  */
 CSMKV_API size_t csm_index_bytes(const csmkv_cache *cache, int32_t block_rows);
 

@@ -385,16 +385,20 @@ int64_t index_leaf_slots(const csmkv_cache *c, int32_t B) {
 }
 
 struct IdxLayout {
-  size_t mu, rho, lmax, wt, total;
+  size_t mu, rho, lmax, wt, items, nitems, total;
 };
 IdxLayout idx_layout(const csmkv_cache *c, int64_t P) {
   IdxLayout L;
   const size_t nodes = (size_t)c->num_slices * 2 * (size_t)P;
+  // the build's work table: one 16-byte entry per leaf group of every slice
+  const size_t groups = (size_t)c->num_slices * (size_t)(P / csmkv::index_leaf_group((int32_t)P));
   L.mu = 0;
   L.rho = align_up(nodes * (size_t)c->d * 4);
   L.lmax = L.rho + align_up(nodes * 4);
   L.wt = L.lmax + align_up(nodes * 4);
-  L.total = L.wt + align_up(nodes * 4);
+  L.items = L.wt + align_up(nodes * 4);
+  L.nitems = L.items + align_up(groups * 16);
+  L.total = L.nitems + kAlign;
   return L;
 }
 
@@ -407,6 +411,9 @@ int index_common(const void *K, const int32_t *N, const int32_t *lens, const csm
   if (P == 0) return CSMKV_EUNSUPPORTED;
   if (!K || !N || !lens || !index || !error_word) return CSMKV_EINVAL;
   if (!aligned(K, 16) || !aligned(index, kAlign) || !aligned(error_word, 4)) return CSMKV_EINVAL;
+  // work-table entries are counted in int32
+  if (cache->num_slices * (P / csmkv::index_leaf_group((int32_t)P)) > (int64_t)INT32_MAX / 4)
+    return CSMKV_EUNSUPPORTED;
   const IdxLayout lay = idx_layout(cache, P);
   if (index_bytes < lay.total) return CSMKV_EWORKSPACE;
   char *x = static_cast<char *>(index);
@@ -419,6 +426,8 @@ int index_common(const void *K, const int32_t *N, const int32_t *lens, const csm
   a.rho = reinterpret_cast<float *>(x + lay.rho);
   a.lmax = reinterpret_cast<float *>(x + lay.lmax);
   a.wt = reinterpret_cast<int32_t *>(x + lay.wt);
+  a.items = reinterpret_cast<int32_t *>(x + lay.items);
+  a.nitems = reinterpret_cast<int32_t *>(x + lay.nitems);
   a.num_slices = cache->num_slices;
   a.cap = cache->cap;
   a.max_len = cache->max_len;

@@ -86,30 +86,6 @@ __device__ __forceinline__ bool len_ok(const DecArgs &a, int s) {
   return s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
 }
 
-// Exclusive prefix sum of one value per thread over a block of NT threads; *total gets the
-// block's sum.  wsum: NT / 64 ints of LDS.  Ends with a barrier.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    before += i < w ? wsum[i] : 0;
-    all += wsum[i];
-  }
-  *total = all;
-  return before + incl - v;
-}
-
-
 __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
   __shared__ int32_t wsum[16];
   const int t = threadIdx.x;
@@ -214,15 +190,6 @@ struct DecStage {
 struct DecRows {
   __amdgpu_buffer_rsrc_t k, v, n;
 };
-constexpr int kBufWord3 = 0x00020000;  // raw (unformatted) buffer, 32-bit data format
-// A pointer that holds the same value in every lane, moved to scalar registers (the compiler
-// cannot always prove that a slice index found at run time is wave-uniform).
-__device__ __forceinline__ void *wave_uniform(const void *p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-  return reinterpret_cast<void *>(lo | (hi << 32));
-}
 __device__ __forceinline__ DecRows dec_rows(const char *Kz, const char *Vz, const int32_t *Nz,
                                             int rowb, int wb, int we) {
   const int rows = __builtin_amdgcn_readfirstlane(max(we - wb, 0));

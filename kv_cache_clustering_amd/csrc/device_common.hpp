@@ -94,6 +94,39 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
+constexpr int kBufWord3 = 0x00020000;  // raw (unformatted) buffer, 32-bit data format
+// A pointer that holds the same value in every lane, moved to scalar registers (the compiler
+// cannot always prove that a slice index found at run time is wave-uniform).
+__device__ __forceinline__ void *wave_uniform(const void *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<void *>(lo | (hi << 32));
+}
+
+// Exclusive prefix sum of one value per thread over a block of NT threads; *total gets the
+// block's sum.  wsum: NT / 64 ints of LDS.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    before += i < w ? wsum[i] : 0;
+    all += wsum[i];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
 // Merge count of a chunk of length L: floor(r * L / 2 + 1e-9) in fp64 (no contraction),
 // clamped to [0, ceil(L/2)]; 0 for L < 2.
 __device__ __forceinline__ int merge_count_dev(double r, int L) {

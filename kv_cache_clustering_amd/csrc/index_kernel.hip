@@ -79,12 +79,45 @@ __device__ __forceinline__ IdxView idx_view(const IdxArgs &a, int64_t z) {
   return {a.mu + z * nodes * a.d, a.rho + z * nodes, a.lmax + z * nodes, a.wt + z * nodes};
 }
 
-// Inner node u from its children (one wave; lanes over the D / 64 elements each).
+// Centre, radius and largest log-degree of an inner node from its two children (one wave; lane l
+// holds elements l + 64 e).  The caller has handled two empty children; an empty child's centre
+// enters neither the centre nor the radius.
+template <int EL>
+__device__ __forceinline__ void combine_children(const float (&a0)[EL], const float (&a1)[EL],
+                                                 int32_t w0, int32_t w1, float r0, float r1,
+                                                 float l0, float l1, float (&m)[EL], float &rho,
+                                                 float &lmax) {
+  const float f0 = (float)w0, f1 = (float)w1, inv = 1.0f / (f0 + f1);
+  float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    m[e] = (w0 == 0) ? a1[e] : (w1 == 0) ? a0[e] : fmaf(f0, a0[e], f1 * a1[e]) * inv;
+    d0 = fmaf(a0[e] - m[e], a0[e] - m[e], d0);
+    d1 = fmaf(a1[e] - m[e], a1[e] - m[e], d1);
+  }
+  d0 = wave_sum(d0);
+  d1 = wave_sum(d1);
+  float r = 0.f;
+  if (w0) r = fmaxf(r, sqrtf(d0) + r0);
+  if (w1) r = fmaxf(r, sqrtf(d1) + r1);
+  rho = r * kRadiusUp;
+  lmax = fmaxf(w0 ? l0 : -__builtin_inff(), w1 ? l1 : -__builtin_inff());
+}
+
+// Inner node u from its children in the index (one wave).  Every load of the children is issued
+// before any is used, so a node costs one round trip to memory.
 template <int D>
 __device__ __forceinline__ void inner_node(const IdxView &v, int u, int l) {
   constexpr int EL = D / 64;
   const int c0 = 2 * u, c1 = 2 * u + 1;
   const int32_t w0 = v.wt[c0], w1 = v.wt[c1];
+  const float r0 = v.rho[c0], r1 = v.rho[c1], l0 = v.lmax[c0], l1 = v.lmax[c1];
+  float a0[EL], a1[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    a0[e] = v.mu[(int64_t)c0 * D + l + 64 * e];
+    a1[e] = v.mu[(int64_t)c1 * D + l + 64 * e];
+  }
   if (w0 + w1 == 0) {
     if (l == 0) {
       v.wt[u] = 0;
@@ -93,35 +126,66 @@ __device__ __forceinline__ void inner_node(const IdxView &v, int u, int l) {
     }
     return;
   }
-  const float f0 = (float)w0, f1 = (float)w1, inv = 1.0f / (f0 + f1);
-  float m[EL], d0 = 0.f, d1 = 0.f;
+  float m[EL], rho, lmax;
+  combine_children<EL>(a0, a1, w0, w1, r0, r1, l0, l1, m, rho, lmax);
 #pragma unroll
-  for (int e = 0; e < EL; ++e) {
-    const int k = l + 64 * e;
-    const float a0 = v.mu[(int64_t)c0 * D + k], a1 = v.mu[(int64_t)c1 * D + k];
-    m[e] = (w0 == 0) ? a1 : (w1 == 0) ? a0 : (f0 * a0 + f1 * a1) * inv;
-    v.mu[(int64_t)u * D + k] = m[e];
-    d0 = fmaf(a0 - m[e], a0 - m[e], d0);
-    d1 = fmaf(a1 - m[e], a1 - m[e], d1);
-  }
-  d0 = wave_sum(d0);
-  d1 = wave_sum(d1);
+  for (int e = 0; e < EL; ++e) v.mu[(int64_t)u * D + l + 64 * e] = m[e];
   if (l == 0) {
-    float r = 0.f;
-    if (w0) r = fmaxf(r, sqrtf(d0) + v.rho[c0]);
-    if (w1) r = fmaxf(r, sqrtf(d1) + v.rho[c1]);
-    v.rho[u] = r * kRadiusUp;
-    v.lmax[u] = fmaxf(w0 ? v.lmax[c0] : -__builtin_inff(), w1 ? v.lmax[c1] : -__builtin_inff());
+    v.rho[u] = rho;
+    v.lmax[u] = lmax;
     v.wt[u] = w0 + w1;
   }
 }
 
-// Leaves: one wave per leaf, kLeavesPerGroup leaves per workgroup, grid over (slice, leaf
-// group).  A wave reads its leaf's rows 16 bytes per lane (SEG lanes per row, 64 / SEG rows per
-// wave load, up to 64 rows a pass, every load of a pass issued before any is used), sums the
-// degree-weighted keys in fp32, reduces over the rows of the wave, and in a second pass over the
-// same rows (from cache) takes the largest distance to the centre.
-constexpr int kLeavesPerGroup = 16;
+// A build runs three launches.  index_plan (one workgroup) lists the non-empty leaf groups of every
+// slice: kLeafGroup consecutive leaf slots (fewer when P is smaller), the leaves of one subtree.
+// index_leaves (a fixed grid, two workgroups per CU, each taking groups from that list in turn):
+// one wave per leaf reads the leaf's rows 16 bytes per lane (SEG lanes per row, 64 / SEG rows
+// per wave load, up to 64 rows and 16 loads a pass, every load of a pass issued before any is
+// used), sums the degree-weighted keys in fp32, reduces over the rows of the wave, and in a second
+// pass over the same rows takes the largest distance to the centre.  A leaf that fits one pass
+// keeps its rows in registers for that (its loads are then non-temporal); a longer one reads them
+// again through the caches.  The workgroup then computes the inner nodes of its subtree from LDS.
+// index_inner (one workgroup per slice) empties the subtrees past the slice's rows and computes
+// the levels above the subtree roots.
+constexpr int kLeafGroup = 8;                  // leaves per group: a subtree of height 3
+constexpr int kLeafThreads = 64 * kLeafGroup;  // one wave per leaf
+constexpr int kLeafGrid = 256 * 2;             // two workgroups per CU
+
+__host__ __device__ inline int leaf_group_size(int P) { return P < kLeafGroup ? P : kLeafGroup; }
+
+int32_t index_leaf_group(int32_t P) { return leaf_group_size(P); }
+
+// Leaf groups of a slice of s rows (none if s is out of range: that slice's tree is empty).
+__device__ __forceinline__ int slice_groups(const IdxArgs &a, int s) {
+  const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
+  const int nleaf = ok ? (s + a.B - 1) / a.B : 0;
+  const int lpg = leaf_group_size(a.P);
+  return (nleaf + lpg - 1) / lpg;
+}
+
+__global__ void __launch_bounds__(1024) index_plan(IdxArgs a) {
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x;
+  const int64_t S = a.num_slices;
+  const int64_t per = (S + 1023) / 1024;
+  const int64_t z0 = t * per, z1 = min(S, z0 + per);
+  int local = 0;
+  for (int64_t z = z0; z < z1; ++z) {
+    const int s = a.lens[z];
+    if (!(s >= 0 && s <= a.max_len && (int64_t)s <= a.cap)) atomicExch(a.err, kDeviceError);
+    local += slice_groups(a, s);
+  }
+  int total;
+  int run = block_excl_scan<1024>(local, wsum, &total);
+  for (int64_t z = z0; z < z1; ++z) {
+    const int s = a.lens[z], g = slice_groups(a, s);
+    for (int gi = 0; gi < g; ++gi)
+      *reinterpret_cast<int4 *>(a.items + 4 * (int64_t)(run + gi)) = make_int4((int)z, gi, s, 0);
+    run += g;
+  }
+  if (t == 0) *a.nitems = total;
+}
 
 template <typename T, int D>
 __device__ __forceinline__ void seg_f32(u32x4 v, float *o) {
@@ -143,101 +207,179 @@ __device__ __forceinline__ void seg_f32(u32x4 v, float *o) {
   }
 }
 
+// NL wave loads of a leaf's rows, STEP bytes apart, from byte soff of the leaf (AUX: the
+// buffer load's cache policy bits).
+template <int NL, int STEP, int AUX>
+__device__ __forceinline__ void leaf_rows(u32x4 *kv, __amdgpu_buffer_rsrc_t rk, int lane_off,
+                                          int soff) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    kv[i] = __builtin_bit_cast(u32x4,
+                               __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + i * STEP, soff, AUX));
+}
+
 template <typename T, int D>
-__global__ void __launch_bounds__(kIdxThreads) index_leaves(IdxArgs a) {
+__global__ void __launch_bounds__(kLeafThreads) __attribute__((amdgpu_waves_per_eu(4)))
+index_leaves(IdxArgs a) {
   constexpr int RB = D * (int)sizeof(T), SEG = RB / 16, RPL = 64 / SEG;  // lanes per row, rows per load
   constexpr int EPS = 16 / (int)sizeof(T);                               // elements per lane
-  constexpr int NL = 64 / RPL;                                           // loads per 64-row pass
-  const int groups = (a.P + kLeavesPerGroup - 1) / kLeavesPerGroup;
-  const int64_t z = blockIdx.x / groups;
+  constexpr int NL = 64 / RPL < 16 ? 64 / RPL : 16;                     // loads per pass
+  constexpr int ROWS = NL * RPL;                                         // rows per pass (<= 64)
+  constexpr int EL = D / 64;
+  // the subtree in heap order: node 1 its root, nodes [lpg, 2 lpg) its leaves
+  __shared__ __attribute__((aligned(16))) float s_mu[2 * kLeafGroup][D];
+  __shared__ float s_rho[2 * kLeafGroup], s_lmax[2 * kLeafGroup];
+  __shared__ int32_t s_wt[2 * kLeafGroup];
+  const int lpg = leaf_group_size(a.P);
   const int t = threadIdx.x, w = t >> 6, l = t & 63, sg = l % SEG, rw = l / SEG;
-  const int s = a.lens[z];
-  const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
-  if (!ok && t == 0 && blockIdx.x % groups == 0) atomicExch(a.err, kDeviceError);
-  const int nleaf = ok ? (s + a.B - 1) / a.B : 0;
-  const IdxView v = idx_view(a, z);
-  const char *Kz = a.K + z * a.cap * RB;
-  const int32_t *Nz = a.N + z * a.cap;
-  const int b0 = (blockIdx.x % groups) * kLeavesPerGroup;
-  for (int b = b0 + w; b < min(b0 + kLeavesPerGroup, a.P); b += kIdxThreads / 64) {
-    const int u = a.P + b;
-    const int r0 = b * a.B, r1 = b < nleaf ? min(r0 + a.B, s) : r0;
-    float acc[EPS];
+  const int total = *a.nitems;
+  const int4 *items = reinterpret_cast<const int4 *>(a.items);
+  int4 next = (int)blockIdx.x < total ? items[blockIdx.x] : make_int4(0, 0, 0, 0);
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    const int4 cur = next;  // (slice, group, rows)
+    if (it + (int)gridDim.x < total) next = items[it + gridDim.x];
+    const int64_t z = cur.x;
+    const int gi = cur.y, s = cur.z;
+    const int nleaf = (s + a.B - 1) / a.B;
+    const IdxView v = idx_view(a, z);
+    const char *Kz = a.K + z * a.cap * RB;
+    const int32_t *Nz = a.N + z * a.cap;
+    if (w < lpg) {
+      const int b = gi * lpg + w, u = a.P + b, li = lpg + w;
+      const int r0 = b * a.B, r1 = b < nleaf ? min(r0 + a.B, s) : r0;
+      // the leaf's rows as range-checked buffers: rows at or past r1 read as zeros, so every
+      // load is issued unconditionally
+      const int nrows = __builtin_amdgcn_readfirstlane(r1 - r0);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          wave_uniform(Kz + (int64_t)r0 * RB), 0, nrows * RB, kBufWord3);
+      const __amdgpu_buffer_rsrc_t rn =
+          __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Nz + r0), 0, nrows * 4, kBufWord3);
+      const int lane_off = rw * RB + sg * 16;
+      float acc[EPS];
 #pragma unroll
-    for (int e = 0; e < EPS; ++e) acc[e] = 0.f;
-    int32_t W = 0, nmax = 0;
-    for (int rb = r0; rb < r1; rb += 64) {  // pass 1: degree-weighted sum
-      u32x4 kv[NL];
-      int32_t nv[NL];
+      for (int e = 0; e < EPS; ++e) acc[e] = 0.f;
+      int32_t W = 0, nmax = 0;
+      u32x4 kv[NL];  // a leaf of at most ROWS rows stays here for pass 2
+      for (int p = 0; p < nrows; p += ROWS) {  // pass 1: degree-weighted sum
+        // the pass's degrees, one row per lane, handed to the lanes of each row by a shuffle
+        const int32_t nrow = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rn, l < ROWS ? (p + l) * 4 : nrows * 4, 0, 0);
+        if (nrows <= ROWS)  // read once: non-temporal
+          leaf_rows<NL, RPL * RB, 2>(kv, rk, lane_off, p * RB);
+        else  // read again in pass 2: through the caches
+          leaf_rows<NL, RPL * RB, 0>(kv, rk, lane_off, p * RB);
+        W += nrow;
+        nmax = max(nmax, nrow);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int r = rb + RPL * i + rw;
-        kv[i] = r < r1 ? ld16(Kz + (int64_t)r * RB + sg * 16) : u32x4{0u, 0u, 0u, 0u};
-        nv[i] = r < r1 ? Nz[r] : 0;
+        for (int i = 0; i < NL; ++i) {
+          const float wi = (float)__shfl(nrow, RPL * i + rw);
+          float x[EPS];
+          seg_f32<T, D>(kv[i], x);
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) acc[e] = fmaf(wi, x[e], acc[e]);
+        }
       }
+      // sum over the rows of the wave: lanes with the same segment hold the same elements
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        float x[EPS];
-        seg_f32<T, D>(kv[i], x);
+      for (int o = SEG; o < 64; o <<= 1) {
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) acc[e] = fmaf((float)nv[i], x[e], acc[e]);
-        W += sg == 0 ? nv[i] : 0;
-        nmax = max(nmax, nv[i]);
+        for (int e = 0; e < EPS; ++e) acc[e] += __shfl_xor(acc[e], o);
+      }
+      W = wave_sum_i(W);
+      nmax = wave_max_i(nmax);
+      if (W == 0) {  // no rows, or rows of degree 0 only (they weigh nothing): an empty leaf
+        if (l == 0) {
+          v.wt[u] = 0;
+          v.rho[u] = 0.f;
+          v.lmax[u] = -__builtin_inff();
+          s_wt[li] = 0;
+        }
+      } else {
+        const float inv = 1.0f / (float)W;
+        float m[EPS];
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) m[e] = acc[e] * inv;
+        if (rw == 0) {
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            v.mu[(int64_t)u * D + sg * EPS + e] = m[e];
+            s_mu[li][sg * EPS + e] = m[e];
+          }
+        }
+        float rmax = 0.f;
+        const bool held = nrows <= ROWS;  // pass 1 left the leaf's rows in kv
+        for (int p = 0; p < nrows; p += ROWS) {  // pass 2: the farthest row
+          if (!held) leaf_rows<NL, RPL * RB, 0>(kv, rk, lane_off, p * RB);
+#pragma unroll
+          for (int i = 0; i < NL; ++i) {
+            float x[EPS], d2 = 0.f;
+            seg_f32<T, D>(kv[i], x);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) d2 = fmaf(x[e] - m[e], x[e] - m[e], d2);
+            d2 = lanes_sum<SEG>(d2);
+            if (p + RPL * i + rw < nrows) rmax = fmaxf(rmax, d2);
+          }
+        }
+        rmax = wave_max(rmax);
+        if (l == 0) {
+          const float rho = sqrtf(rmax) * kRadiusUp;
+          const float lm = __builtin_amdgcn_logf((float)nmax);  // log2
+          v.rho[u] = rho;
+          v.lmax[u] = lm;
+          v.wt[u] = W;
+          s_rho[li] = rho;
+          s_lmax[li] = lm;
+          s_wt[li] = W;
+        }
       }
     }
-    // sum over the rows of the wave: lanes with the same segment hold the same elements
+    __syncthreads();
+    // the subtree's inner nodes: node i of a level of n nodes is global node n (P / lpg + gi) + i - n
+    for (int n = lpg / 2; n >= 1; n /= 2) {
+      if (w < n) {
+        const int li = n + w, c0 = 2 * li, c1 = 2 * li + 1;
+        const int64_t u = (int64_t)n * (a.P / lpg + gi) + w;
+        const int32_t w0 = s_wt[c0], w1 = s_wt[c1];
+        if (w0 + w1 == 0) {
+          if (l == 0) {
+            v.wt[u] = 0;
+            v.rho[u] = 0.f;
+            v.lmax[u] = -__builtin_inff();
+            s_wt[li] = 0;
+          }
+        } else {
+          float a0[EL], a1[EL], m[EL], rho, lmax;
 #pragma unroll
-    for (int o = SEG; o < 64; o <<= 1) {
+          for (int e = 0; e < EL; ++e) {
+            a0[e] = s_mu[c0][l + 64 * e];
+            a1[e] = s_mu[c1][l + 64 * e];
+          }
+          combine_children<EL>(a0, a1, w0, w1, s_rho[c0], s_rho[c1], s_lmax[c0], s_lmax[c1], m,
+                               rho, lmax);
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) acc[e] += __shfl_xor(acc[e], o);
-    }
-    W = wave_sum_i(W);
-    nmax = wave_max_i(nmax);
-    if (W == 0) {  // no rows, or rows of degree 0 only (they weigh nothing): an empty leaf
-      if (l == 0) {
-        v.wt[u] = 0;
-        v.rho[u] = 0.f;
-        v.lmax[u] = -__builtin_inff();
+          for (int e = 0; e < EL; ++e) {
+            v.mu[u * D + l + 64 * e] = m[e];
+            s_mu[li][l + 64 * e] = m[e];
+          }
+          if (l == 0) {
+            v.rho[u] = rho;
+            v.lmax[u] = lmax;
+            v.wt[u] = w0 + w1;
+            s_rho[li] = rho;
+            s_lmax[li] = lmax;
+            s_wt[li] = w0 + w1;
+          }
+        }
       }
-      continue;
-    }
-    const float inv = 1.0f / (float)W;
-    float m[EPS];
-#pragma unroll
-    for (int e = 0; e < EPS; ++e) m[e] = acc[e] * inv;
-    if (rw == 0) {
-#pragma unroll
-      for (int e = 0; e < EPS; ++e) v.mu[(int64_t)u * D + sg * EPS + e] = m[e];
-    }
-    float rmax = 0.f;
-    for (int rb = r0; rb < r1; rb += 64) {  // pass 2: the farthest row
-      u32x4 kv[NL];
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int r = rb + RPL * i + rw;
-        kv[i] = r < r1 ? ld16(Kz + (int64_t)r * RB + sg * 16) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        float x[EPS], d2 = 0.f;
-        seg_f32<T, D>(kv[i], x);
-#pragma unroll
-        for (int e = 0; e < EPS; ++e) d2 = fmaf(x[e] - m[e], x[e] - m[e], d2);
-        d2 = lanes_sum<SEG>(d2);
-        if (rb + RPL * i + rw < r1) rmax = fmaxf(rmax, d2);
-      }
-    }
-    rmax = wave_max(rmax);
-    if (l == 0) {
-      v.rho[u] = sqrtf(rmax) * kRadiusUp;
-      v.lmax[u] = __builtin_amdgcn_logf((float)nmax);  // log2
-      v.wt[u] = W;
+      __syncthreads();
     }
   }
 }
 
-// Inner levels, bottom-up: one workgroup per slice, a wave per node.  A node whose leaves all lie
-// at or past the slice's last block is empty without looking at its children.
+// The rest of each slice's tree, bottom-up: one workgroup per slice, a wave per node.  First the
+// subtrees past the slice's last leaf group (no item of the build) are emptied; then the levels
+// above the subtree roots are computed, a node whose leaves all lie at or past the slice's last
+// block being empty without looking at its children.
 constexpr int kInnerThreads = 1024;
 template <int D>
 __global__ void __launch_bounds__(kInnerThreads) index_inner(IdxArgs a) {
@@ -247,7 +389,16 @@ __global__ void __launch_bounds__(kInnerThreads) index_inner(IdxArgs a) {
   const int s = a.lens[z];
   const bool ok = s >= 0 && s <= a.max_len && (int64_t)s <= a.cap;
   const int nleaf = ok ? (s + a.B - 1) / a.B : 0;
-  for (int lvl = a.P / 2; lvl >= 1; lvl /= 2) {
+  const int roots = a.P / leaf_group_size(a.P), groups = slice_groups(a, s);
+  for (int n = a.P; n >= roots; n /= 2) {
+    for (int u = n + groups * (n / roots) + t; u < 2 * n; u += kInnerThreads) {
+      v.wt[u] = 0;
+      v.rho[u] = 0.f;
+      v.lmax[u] = -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  for (int lvl = roots / 2; lvl >= 1; lvl /= 2) {
     const int span = a.P / lvl;  // leaves under a node of this level
     for (int u = lvl + w; u < 2 * lvl; u += kInnerThreads / 64) {
       if ((u - lvl) * span >= nleaf) {
@@ -596,10 +747,13 @@ __global__ void __launch_bounds__(1024) prune_plan(IdxArgs a) {
 template <typename T, int D>
 static int launch_idx_t(const IdxArgs &a, int op, hipStream_t st) {
   if (op == 0) {
-    const int64_t groups = (a.P + kLeavesPerGroup - 1) / kLeavesPerGroup;
-    hipLaunchKernelGGL((index_leaves<T, D>), dim3((uint32_t)(a.num_slices * groups)),
-                       dim3(kIdxThreads), 0, st, a);
-    const hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL(index_plan, dim3(1), dim3(1024), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const int64_t items = a.num_slices * (a.P / leaf_group_size(a.P));
+    const uint32_t grid = (uint32_t)std::min<int64_t>(items, kLeafGrid);
+    hipLaunchKernelGGL((index_leaves<T, D>), dim3(grid), dim3(kLeafThreads), 0, st, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL((index_inner<D>), dim3((uint32_t)a.num_slices), dim3(kInnerThreads), 0, st, a);
   } else

@@ -71,6 +71,8 @@ struct IdxArgs {
   int32_t *err;
   float *mu, *rho, *lmax;  // [num_slices][2P][d], [num_slices][2P] x 2
   int32_t *wt;             // [num_slices][2P] degree totals (0 = empty node)
+  int32_t *items;          // build: [num_slices * (P / leaf group)][4] (slice, group, length, 0)
+  int32_t *nitems;         // build: number of items
   int64_t num_slices, cap;
   int32_t max_len, d, P, B;
   // pruned decode
@@ -93,6 +95,9 @@ int launch_decode(const DecArgs &a, int dtype, int d, int G, int64_t max_items, 
 int launch_append(const AppArgs &a, hipStream_t st);
 // op 0: build the index over each slice's rows; op 1: take in the row just appended.
 int launch_index(const IdxArgs &a, int dtype, int d, int op, hipStream_t st);
+// Leaf slots a build workgroup takes for a tree of P leaf slots (the work table of a build holds
+// num_slices * P / this entries).
+int32_t index_leaf_group(int32_t P);
 // Thresholds, walk and runs per slice, then the item table (the decode split and combine kernels
 // follow with launch_decode_table).
 int launch_prune(const IdxArgs &a, int dtype, int d, int G, hipStream_t st);

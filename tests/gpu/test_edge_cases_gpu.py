@@ -100,7 +100,9 @@ def test_zero_and_tiny_norm_keys(lib, dev, dt, d, c):
     keys whose norm is below the 1e-12 floor score as if their norm were 1e-12; keys just above
     it score as plain cosines.  fp16 cannot hold a norm near the floor (nor the elements of such
     a key, which would be subnormal), so there zero keys and keys scaled by 2^-4 and 2^-2 are
-    planted."""
+    planted.  A merge of a zero or tiny key into a target can leave a mean far below the terms it
+    came from, where fp32 accumulation error exceeds one ulp of the result: the absolute floor of
+    the value check is allowed here (and counted in the report)."""
     lens = [2600, 2600]
     K, V, N, L = _np_cache(2, 2600, lens, d, seed=17 + d + c)
     rng = np.random.default_rng(23 + d)
@@ -118,7 +120,7 @@ def test_zero_and_tiny_norm_keys(lib, dev, dt, d, c):
     for r in (0.5, 1.0):
         rep = run_and_compare(lib, dev, *_to(dt, K, V, N, L), 16, 64, c, r)
         print(dt, d, c, r, rep)
-        parity.check_report(rep)
+        parity.check_report(rep, floor_allowed=True)
         total.add(rep)
     assert total.exact_match_ties > 0 and total.exact_cut_ties > 0
 

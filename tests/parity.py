@@ -184,6 +184,10 @@ def compare_slice(rep, Kin, Vin, Nin, s, n1, n2, c, r, storage, gpu_best, gpu_se
         check_values(rep, g, o, storage)
 
 
-def check_report(rep, near_bar=1e-3):
+def check_report(rep, near_bar=1e-3, floor_allowed=False):
+    """No hard mismatch, near-ties below near_bar of the A edges, and (unless the inputs are built
+    to make weighted means cancel) no merged value that needed the absolute floor."""
     assert rep.match_hard == 0 and rep.sel_hard == 0, rep
     assert rep.near_fraction() < near_bar, rep
+    if not floor_allowed:
+        assert rep.abs_floor_used == 0, rep

@@ -24,7 +24,8 @@
 // per visited node in LDS) evaluates a node only if its parent passed; since child balls lie in
 // their parents, this keeps exactly the blocks that pass their own test.
 //
-// Launches of decode_attn_logn_pruned: prune_select (one workgroup per slice: thresholds, walk,
+// Launches of csm_index_build: index_plan, index_leaves and index_inner (described with them);
+// csm_index_append: index_append.  Launches of decode_attn_logn_pruned: prune_select (one workgroup per slice: thresholds, walk,
 // runs of consecutive kept blocks), prune_plan (one workgroup: the runs cut into work items and
 // scanned into the item table), then the decode split and combine kernels over that table.
 #include <algorithm>

@@ -124,6 +124,38 @@ def test_index_build_matches_oracle_and_bounds_hold(lib, dev, dt, d, B):
     _check_index(K64, N64, lens, cap, B, mu, rho, lmax, wt, qs)
 
 
+@pytest.mark.parametrize("cap,B,lens,max_len", [
+    (16, 16, [16, 3, 0, 9], 16),          # one leaf slot: the leaf is the root
+    (32, 16, [32, 17, 1, 0], 32),         # two leaf slots
+    (100, 16, [100, 64, 33, 5], 100),     # eight leaf slots: one leaf group, its whole subtree
+    (300, 16, [300, 129, 200, 7], 200),   # 32 leaf slots, the length bound below the capacity
+])
+def test_index_build_small_trees_and_length_bound(lib, dev, cap, B, lens, max_len):
+    """Trees smaller than a leaf group, exactly one group, and several groups under a length bound
+    below the capacity (the build covers max_len rows; the slots past them are emptied), over an
+    index filled with arbitrary bytes first, so every node must be written.  A slice longer than
+    the bound sets the error word and gets an empty tree; the others match the oracle's node by
+    node."""
+    d = 128
+    K, V, N, L, q = _setup(dev, "bf16", d, B, 0.3, seed=cap + B, lens=lens, cap=cap)
+    index = lib.new_index(K, B)
+    index.fill_(0x5A)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    lib.index_build(K, N, L, index, err, B, max_len=max_len)
+    bad = [z for z, s in enumerate(lens) if s > max_len]
+    assert (lib.read_error(err) == lib.OK) == (not bad)
+    P = lib.index_leaf_slots(cap, B)
+    mu, rho, lmax, wt = _node_arrays(lib, index, len(lens), P, d)
+    for z in bad:
+        assert np.all(wt[z][1:] == 0), z
+    good = [z for z in range(len(lens)) if z not in bad]
+    K64, N64 = parity.to_f64(K.cpu()), N.cpu().numpy().astype(np.int64)
+    qh = parity.to_f64(q.cpu())
+    qs = [qh[z // 2, (z % 2) * 4:(z % 2) * 4 + 4] for z in range(len(lens))]
+    _check_index(K64[good], N64[good], [lens[z] for z in good], cap, B, mu[good], rho[good],
+                 lmax[good], wt[good], [qs[z] for z in good])
+
+
 def _compare_pruned(lib, K, V, N, L, q, index, tau, B, n1, n2, H_q, H_kv):
     """Pruned decode on the device against the oracle; returns (dropped rows, worst error vs the
     oracle over the device's kept rows, worst error vs full attention, bound)."""

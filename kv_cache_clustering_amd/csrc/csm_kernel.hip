@@ -12,37 +12,41 @@
 //                slices run (all, or those at their trigger threshold) and with which r,
 //                records each slice's input and output length, resets the per-slice
 //                ticket counters and clears the per-chunk "source consumed" flags.
-//   csm_round  : one 256-thread workgroup per unit; units are (slice, chunk) pairs plus
-//                one "tail" unit per slice that moves the recent rows and writes lens.
-//                A workgroup's slice comes from its block index (a slice that does not
-//                run exits at once, touching no counter); its unit within the slice is a
-//                ticket from that slice's atomic counter, so every lower-numbered unit of
-//                the slice has already started when a unit runs.
+//   csm_round  : one workgroup per unit (512 threads for chunks of up to 256 rows, 256 for
+//                fp32 storage at d = 128, 1024 for chunks of up to 512 rows); units are (slice,
+//                chunk) pairs plus one "tail" unit per slice that moves the recent rows and
+//                writes lens.  A workgroup's slice comes from its block index (a slice that does
+//                not run exits at once, touching no counter); its unit within the slice is a
+//                ticket from that slice's atomic counter, so every lower-numbered unit of the
+//                slice has already started when a unit runs.
 //
 // In-place compaction: chunk j of a slice writes rows [n1 + j*(c - m), ...), which may
 // overlap the source rows of chunks i <= j.  A chunk loads its whole source (K, V, N)
 // into LDS and registers, waits for its loads to land, and raises its flag; before
 // writing it waits for the flags of the lower chunks whose sources its destination
 // overlaps.  Those chunks hold lower tickets of the same slice, are already running and
-// raise their flag
-// without waiting on anything, so every wait ends.  Lower chunks never write into a
-// higher chunk's source.
+// raise their flag without waiting on anything, so every wait ends (a bounded poll turns a
+// wait that does not end into the sticky error word).  Lower chunks never write into a higher
+// chunk's source.
 //
-// Per chunk (c <= 256, head dim d = 64 or 128):
-//   keys -> LDS tile (swizzled rows), fp32 norms from the same registers;
-//   S^T = B_keys . A_keys^T on MFMA (bf16: v_mfma_f32_32x32x16_bf16, fp32:
-//   v_mfma_f32_32x32x2_f32), wave w owning A columns [32w, 32w+32) and all B rows;
-//   cosine = (dot * fl(1/max(|b|,1e-12))) * fl(1/max(|a|,1e-12)) in fp32 (reciprocal norms
-//   computed once per row at load time), branch-free arg-max per A column inside each
-//   lane then across the two half-waves (lowest B index on ties);
-//   rank of every A edge by (score desc, index asc) through a 128-way comparison count
-//   split over all four waves;
-//   per-target source lists in ascending A order: same-target lanes found with seven
-//   ballots over the target index bits, slots by mbcnt, counts scanned across targets;
+// Per chunk (A = even offsets, B = odd; up to 128 of each for c <= 256, 256 for c <= 512; head
+// dim d = 64 or 128):
+//   keys -> LDS tile (swizzled rows), reciprocal fp32 norms from the same registers; values
+//   stay in registers;
+//   S^T = B_keys . A_keys^T on MFMA (16-bit: v_mfma_f32_32x32x16_bf16 / _f16, fp32:
+//   v_mfma_f32_32x32x2_f32): the waves split the tile into 32-column A groups times B parts;
+//   cosine = (dot * fl(1/max(|b|,1e-12))) * fl(1/max(|a|,1e-12)) in fp32, branch-free arg-max
+//   per A column inside each lane, then across the two half-waves, then across the B parts
+//   through LDS (lowest B index on ties);
+//   rank of every A edge by (score desc, index asc) from unique 64-bit keys, a comparison count
+//   split over all threads;
+//   per-target source lists in ascending A order: same-target lanes found with ballots over the
+//   target index bits, slots by mbcnt, counts scanned across targets;
 //   keep-mask prefix sum (ballot + mbcnt) gives each kept row its output slot;
 //   rows that are not merge targets are copied in one pass; merge targets, compacted into
 //   a list, are computed as (N_b k_b + sum N_a k_a) * rcp(N_b + sum N_a) in fp32 and
-//   stored RNE (v_cvt_pk_bf16_f32); stores are non-temporal (the output is not re-read).
+//   stored rounded to nearest even; values pass through the same LDS tile after the keys;
+//   stores are non-temporal (the output is not re-read by the round).
 #include <algorithm>
 
 #include "csm_common.hpp"

@@ -7,8 +7,9 @@
 //                 every slice ceil(len / tsplit) work items and scans them into item offsets.
 //                 tsplit (512 to 2048 tokens) is chosen on the host from the slice count and
 //                 the length bound so that a call has about 2048 items.  Smaller calls plan
-//                 in the split kernel itself, from the total length: about one item per CU
-//                 for a layer's few slices, items of up to 2048 tokens for many slices.
+//                 in the split kernel itself, from the total length (a wave-level scan for up
+//                 to 64 slices, an LDS scan beyond): about one item per CU for a layer's few
+//                 slices, items of up to 2048 tokens for many slices.
 //   dec_split   : workgroups stride over the work items (at most 2048 workgroups).  A work
 //                 item is up to tsplit tokens of one slice, shared by the G query heads of
 //                 that KV head, so K, V and N are read from HBM once per step.  Each wave
@@ -17,8 +18,8 @@
 //                 computed; base-2 online softmax (log2 N added, log2 e folded into the
 //                 scale).  bf16 / fp16: q.k and P.V on MFMA tiles (described below); fp32:
 //                 FMAs with a DPP reduction over the lanes of a row, and at G = 8 two
-//                 workgroups of four heads each.  Waves merge in LDS; each item writes one (max, sum, 0, 0, o[d])
-//                 partial per head.
+//                 workgroups of four heads each.  Waves merge in LDS; each item writes one
+//                 (max, sum, 0, 0, o[d]) partial per head.
 //   dec_combine : one 1024-thread workgroup per slice merges the item partials by
 //                 log-sum-exp (a running maximum per thread over item groups in parallel,
 //                 then the groups merged against their common maximum).

@@ -108,15 +108,25 @@ def _stream(device):
 
 
 def _check_cache(K, V, N, lens):
-    if not (K.is_cuda and V.is_cuda and N.is_cuda and lens.is_cuda):
+    if not V.is_cuda:
         raise ValueError("cache tensors must be on the GPU")
     if K.shape != V.shape or K.dtype != V.dtype:
         raise ValueError("K and V must have the same shape and dtype")
+    if not V.is_contiguous():
+        raise ValueError("cache tensors must be contiguous")
+    _check_keys(K, N, lens)
+
+
+def _check_keys(K, N, lens):
+    if not (K.is_cuda and N.is_cuda and lens.is_cuda):
+        raise ValueError("cache tensors must be on the GPU")
+    if K.dim() != 3:
+        raise ValueError("K must be [num_slices, cap, d]")
     if N.shape != K.shape[:2] or N.dtype != torch.int32:
         raise ValueError("N must be int32 [num_slices, cap]")
     if lens.shape != K.shape[:1] or lens.dtype != torch.int32:
         raise ValueError("lens must be int32 [num_slices]")
-    for t in (K, V, N, lens):
+    for t in (K, N, lens):
         if not t.is_contiguous():
             raise ValueError("cache tensors must be contiguous")
 
@@ -136,9 +146,16 @@ def new_workspace(nbytes, device):
 def _workspace(nbytes, device, ws):
     if ws is None:
         return new_workspace(nbytes, device)
-    if ws.dtype != torch.uint8 or not ws.is_cuda or ws.numel() < nbytes:
-        raise ValueError(f"workspace must be a uint8 GPU tensor of at least {nbytes} bytes")
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous() or ws.numel() < nbytes:
+        raise ValueError(f"workspace must be a contiguous uint8 GPU tensor of at least {nbytes} bytes")
     return ws
+
+
+def _check_word(error_word, allow_none=False):
+    if error_word is None and allow_none:
+        return
+    if error_word is None or error_word.dtype != torch.int32 or not error_word.is_cuda:
+        raise ValueError("error_word must be an int32 GPU tensor")
 
 
 def _raise(rc, what):
@@ -243,8 +260,9 @@ def decode_attn_logn(q, K, V, N, lens, H_q, H_kv, out=None, max_len=None, worksp
         raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
     if out is None:
         out = torch.empty((groups, H_q, d), dtype=torch.float32, device=K.device)
-    elif out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be contiguous fp32 [groups, H_q, d]")
+    elif (out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous()
+          or not out.is_cuda):
+        raise ValueError("out must be a contiguous fp32 GPU tensor [groups, H_q, d]")
     desc = cache_desc(K, max_len)
     ws = _workspace(_lib.decode_attn_logn_workspace_bytes(ctypes.byref(desc), H_q, H_kv),
                     K.device, workspace)
@@ -266,10 +284,10 @@ def decode_attn_logn_noalloc(q, K, V, N, lens, H_q, H_kv, out, error_word, max_l
     groups = S // H_kv if H_kv > 0 else 0
     if q.shape != (groups, H_q, d) or q.dtype != K.dtype or not q.is_contiguous() or not q.is_cuda:
         raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
-    if out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be contiguous fp32 [groups, H_q, d]")
-    if error_word.dtype != torch.int32 or not error_word.is_cuda:
-        raise ValueError("error_word must be an int32 GPU tensor")
+    if (out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous()
+            or not out.is_cuda):
+        raise ValueError("out must be a contiguous fp32 GPU tensor [groups, H_q, d]")
+    _check_word(error_word)
     desc = cache_desc(K, max_len)
     rc = _lib.decode_attn_logn_noalloc(_ptr(q), _ptr(K), _ptr(V), _ptr(N), _ptr(lens),
                                        ctypes.byref(desc), H_q, H_kv, _ptr(out), _ptr(error_word),
@@ -281,6 +299,7 @@ def decode_attn_logn_noalloc(q, K, V, N, lens, H_q, H_kv, out, error_word, max_l
 def kv_append(K, V, N, lens, k_new, v_new, error_word=None):
     """Append one token per slice: K[s]=k, V[s]=v, N[s]=1, s+=1."""
     _check_cache(K, V, N, lens)
+    _check_word(error_word, allow_none=True)
     S, _, d = K.shape
     for t in (k_new, v_new):
         if t.shape != (S, d) or t.dtype != K.dtype or not t.is_contiguous() or not t.is_cuda:
@@ -338,8 +357,16 @@ def csm_upload_rows(K_host, V_host, N_host, lens_host, K, V, N, lens, row_begin=
     """Enqueue the copy of the host cache's rows [row_begin, lens) (K, V, N) and lens into the
     device cache, for every slice not flagged in outlier_mask (a CPU uint8 tensor or None)."""
     _check_host(K_host, V_host, N_host, lens_host, outlier_mask)
+    S = K_host.shape[0] if K_host.dim() == 3 else -1
+    if (K_host.dim() != 3 or V_host.shape != K_host.shape or V_host.dtype != K_host.dtype
+            or N_host.shape != K_host.shape[:2] or N_host.dtype != torch.int32
+            or lens_host.shape != (S,) or lens_host.dtype != torch.int32):
+        raise ValueError("host cache: K, V [num_slices, cap, d] of one dtype, N int32 "
+                         "[num_slices, cap], lens int32 [num_slices]")
+    if outlier_mask is not None and (outlier_mask.dtype != torch.uint8 or outlier_mask.shape != (S,)):
+        raise ValueError("outlier_mask must be uint8 [num_slices]")
     _check_cache(K, V, N, lens)
-    if K_host.shape != K.shape or K_host.dtype != K.dtype or N_host.shape != N.shape:
+    if K_host.shape != K.shape or K_host.dtype != K.dtype:
         raise ValueError("host and device caches must share their geometry")
     desc = cache_desc(K)
     rc = _lib.csm_upload_rows(_ptr(K_host), _ptr(V_host), _ptr(N_host), _ptr(lens_host), _ptr(K),
@@ -365,9 +392,15 @@ def new_index(K, block_rows=64):
     return torch.zeros(n, dtype=torch.uint8, device=K.device)
 
 
+def _check_index_mem(index):
+    if index.dtype != torch.uint8 or not index.is_cuda or not index.is_contiguous():
+        raise ValueError("index must be a contiguous uint8 GPU tensor (see new_index)")
+
+
 def _index_call(fn, K, N, lens, index, block_rows, error_word, max_len):
-    if error_word is None or error_word.dtype != torch.int32 or not error_word.is_cuda:
-        raise ValueError("error_word must be an int32 GPU tensor")
+    _check_keys(K, N, lens)
+    _check_word(error_word)
+    _check_index_mem(index)
     desc = cache_desc(K, max_len)
     rc = fn(_ptr(K), _ptr(N), _ptr(lens), ctypes.byref(desc), int(block_rows), _ptr(index),
             index.numel(), _ptr(error_word), _stream(K.device))
@@ -395,6 +428,10 @@ def decode_attn_logn_pruned(q, K, V, N, lens, H_q, H_kv, index, tau, n1=16, n2=6
         raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
     if out is None:
         out = torch.empty((groups, H_q, d), dtype=torch.float32, device=K.device)
+    elif (out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous()
+          or not out.is_cuda):
+        raise ValueError("out must be a contiguous fp32 GPU tensor [groups, H_q, d]")
+    _check_index_mem(index)
     desc = cache_desc(K, max_len)
     ws = _workspace(_lib.decode_attn_logn_pruned_workspace_bytes(ctypes.byref(desc), H_q, H_kv,
                                                                  block_rows), K.device, workspace)

@@ -168,7 +168,7 @@ const char *csmkv_status_string(int status) {
   }
 }
 
-int csmkv_version(void) { return 104; }
+int csmkv_version(void) { return 105; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
   if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 512) return 0;

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.version() == 104
+    assert lib.version() == 105
     for code in range(-6, 1):
         assert lib.status_string(code).startswith("CSMKV_")
     assert "unknown" in lib.status_string(-99)
@@ -214,3 +214,20 @@ def test_decode_workspace_holds_every_item_plan(lib):
             for lens in mixes:
                 items = _items_for_lengths(S, max_len, [int(x) for x in lens])
                 assert items * part + (S + 1) * 4 <= ws, (S, max_len, d, G, items, ws)
+
+
+def test_binding_checks_the_host_cache_first(lib):
+    """csm_upload_rows' binding rejects a host cache whose V, N or lens do not match K (the
+    library would read past them) before it looks at the device tensors."""
+    import torch
+    K = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    V = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    N = torch.zeros((2, 8), dtype=torch.int32)
+    L = torch.zeros(2, dtype=torch.int32)
+    bad = [(K, torch.zeros((2, 4, 64), dtype=torch.bfloat16), N, L), (K, V, N.to(torch.int64), L), (K, V, N, L[:1]),
+           (K, V.to(torch.float16), N, L)]
+    for kh, vh, nh, lh in bad:
+        with pytest.raises(ValueError, match="host cache"):
+            lib.csm_upload_rows(kh, vh, nh, lh, K, V, N, L)
+    with pytest.raises(ValueError, match="outlier_mask"):
+        lib.csm_upload_rows(K, V, N, L, K, V, N, L, outlier_mask=torch.zeros(3, dtype=torch.uint8))

@@ -9,8 +9,9 @@ Every length is known on the host in closed form (schedule.Algorithm1), so drivi
 device needs no read-back: the whole loop is a sequence of asynchronous library calls on
 the current stream.  With the device-side trigger (csm_compress_triggered) the round of a
 step is decided on the device from each slice's length and round counter, so many steps can
-also be captured in one HIP graph (capture_loop / run_loop).  All sequences of a batch share one prefill length and therefore one
-schedule; slices flagged outlier are never clustered and keep growing.
+also be captured in one HIP graph (capture_loop / run_loop).  All sequences of a batch share one
+prefill length and therefore one schedule; slices flagged outlier are never clustered and keep
+growing.
 """
 
 import torch

@@ -230,7 +230,8 @@ def main():
             lib.decode_attn_logn(q_last[layer:layer + 1], Kl, Vl, Nl, Ll, w.H_q, w.H_kv, out=Ol,
                                  max_len=dec_bound, workspace=ws_l)
 
-    layer_calls()
+    for _ in range(3):
+        layer_calls()
     torch.cuda.synchronize()
     layer_ms = []
     for _ in range(10):
@@ -253,7 +254,8 @@ def main():
     layer_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(layer_graph):
         layer_calls()
-    layer_graph.replay()
+    for _ in range(3):
+        layer_graph.replay()
     torch.cuda.synchronize()
     assert torch.equal(O, O_eager)
     layer_graph_ms = []
@@ -654,6 +656,10 @@ def trigger_round(lib, w, sched, Kd, Vd, Nd, Ld, app_k, app_v, mask, maskh, flus
             "slice_tokens_per_s": comp * s_in / (avg * 1e-3)}
 
 
+ROUND0_WARMUP, ROUND0_REPS = 3, 10  # untimed and timed reps of a workload's round 0
+DEC_WARMUP, DEC_STEPS = 3, 10        # untimed and timed decode steps of a workload
+
+
 def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
     """One synthetic workload: every prefill round in place (HIP events per round), then
     decode steps (append + attention) over the compressed cache.  Figures are algorithmic
@@ -697,7 +703,7 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
         Kc, Vc, Nc, Lc = (t.clone() for t in (K, V, N, L))
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         reps = []
-        for rep in range(4):
+        for rep in range(ROUND0_WARMUP + ROUND0_REPS):
             for dst, src in ((Kc, K), (Vc, V), (Nc, N), (Lc, L)):
                 dst.copy_(src)
             flush.fill_(rep)
@@ -708,7 +714,7 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
             e1.record(stream)
             torch.cuda.synchronize()
             reps.append(e0.elapsed_time(e1))
-        round0_reps = reps[1:]
+        round0_reps = reps[ROUND0_WARMUP:]
         del Kc, Vc, Nc, Lc, flush
         torch.cuda.empty_cache()
     rounds = []
@@ -733,11 +739,12 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
         r0["first_call_ms"] = r0["ms"]  # the prefill sequence's own first round (cold)
         alg0 = n_comp * ((w.ctx - w.n1) + (r0["s_out"] - w.n1)) * row
         r0["ms"] = sum(round0_reps) / len(round0_reps)
+        r0["median_ms"] = median(round0_reps)
         r0["min_ms"] = min(round0_reps)
         r0["GBps"] = alg0 / r0["ms"] / 1e6
         r0["slice_tokens_per_s"] = n_comp * w.ctx / (r0["ms"] * 1e-3)
         r0["timing"] = (f"mean of {len(round0_reps)} reps in place on a restored copy, last-level "
-                        "cache flushed before each, after one untimed rep")
+                        f"cache flushed before each, after {ROUND0_WARMUP} untimed reps")
     out = {"workload": w.name, "slices": S, "dtype": w.dtype, "d": w.d, "c": w.c, "G": w.G,
            "ctx": w.ctx,
            "round0": r0,
@@ -745,7 +752,7 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
                        "GBps": sum(n_comp * ((x["s_in"] - w.n1) + (x["s_out"] - w.n1)) * row
                                    for x in rounds) / sum(x["ms"] for x in rounds) / 1e6}}
     ws_d = lib.new_workspace(lib.decode_workspace_bytes(K, w.H_q, w.H_kv), dev)
-    q = kvsynth.make_queries(w, dev, steps=min(w.steps, 8))
+    q = kvsynth.make_queries(w, dev, steps=min(w.steps, DEC_WARMUP + DEC_STEPS))
     O = torch.empty((w.groups, w.H_q, d), dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     nsteps = q.shape[0]
@@ -758,10 +765,12 @@ def measure_workload(cid, dtype=None, head_dim=None, chunk=None, group=None):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     assert lib.read_error(ws_d) == lib.OK and lib.read_error(err) == lib.OK
-    times = [a.elapsed_time(b) for a, b in evs[1:]] or [evs[0][0].elapsed_time(evs[0][1])]
+    warm = DEC_WARMUP if nsteps > DEC_WARMUP else 0
+    times = [a.elapsed_time(b) for a, b in evs[warm:]]
     us = sum(times) / len(times) * 1e3
     dec_alg = int(L.sum()) * row + w.groups * w.H_q * d * (K.element_size() + 4)
-    out["decode"] = {"us": us, "GBps": dec_alg / (us * 1e-6) / 1e9,
+    out["decode"] = {"us": us, "median_us": median(times) * 1e3, "min_us": min(times) * 1e3,
+                     "GBps": dec_alg / (us * 1e-6) / 1e9,
                      "frac": dec_alg / (us * 1e-6) / 1e9 / PEAK_GBPS, "steps_timed": len(times)}
     out["round0"]["frac"] = out["round0"]["GBps"] / PEAK_GBPS
     del c, K, V, N, L, q, ws, ws_d

@@ -106,8 +106,10 @@ def _check_index(K64, N64, lens, cap, B, mu, rho, lmax, wt, qs_by_slice):
                     u //= 2
 
 
+# leaves read in one pass of at most 64 rows (their rows kept in registers for the radius) and in
+# several (read again): fp32 at d = 128 takes 32 rows a pass, so its 64-row leaves need two
 @pytest.mark.parametrize("dt,d,B", [("bf16", 128, 64), ("f16", 64, 32), ("f32", 128, 16),
-                                    ("bf16", 64, 256)])
+                                    ("bf16", 64, 256), ("f32", 128, 64), ("f16", 128, 128)])
 def test_index_build_matches_oracle_and_bounds_hold(lib, dev, dt, d, B):
     lens = [3000, 1, 0, 777]
     cap = 3100

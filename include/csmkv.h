@@ -201,6 +201,28 @@ CSMKV_API int decode_attn_logn(const void *q, const void *K, const void *V, cons
                      const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
                      float *O, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kv_append_decode_attn_logn -- one decode step of Algorithm 1 in one call: every slice appends
+ * the token (k_new, v_new) with degree 1 (as kv_append) and then attends over its rows, the new
+ * one included (as decode_attn_logn).
+ *   Chelsea review, section 三, Algorithm 1 (K = [K, k], V = [V, v], N = [N, 1], s = s + 1, then
+ *   O = Softmax(q K^T / sqrt(d) + log N) V; 核心公式).
+ * The attention kernels read the rows that were there before the call; the token enters the
+ * last merge of the per-item partials as one more partial, and is then written into the cache
+ * (K[s], V[s], N[s] = 1, lens[z] = s + 1).  The output equals that of kv_append followed by
+ * decode_attn_logn up to the order of the fp32 sums.  A slice whose length is negative or equal
+ * to cap is not appended and sets the error word (its attention then covers its current rows);
+ * the length attended over (after the append) must lie within cache->max_len, else the error word
+ * is set and that slice's output is zeros (as the two separate calls would give).
+ * k_new, v_new : [num_slices][d] in the cache dtype, 16-byte aligned, not NULL.  Other arguments,
+ *   layout, workspace (decode_attn_logn_workspace_bytes) and status codes as decode_attn_logn.
+ */
+CSMKV_API int kv_append_decode_attn_logn(const void *q, void *K, void *V, int32_t *N,
+                                         int32_t *lens, const csmkv_cache *cache, int32_t H_q,
+                                         int32_t H_kv, const void *k_new, const void *v_new,
+                                         float *O, void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
 /* Size of the fixed device scratch array decode_attn_logn_noalloc works in (per GPU). */
 #define CSMKV_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 

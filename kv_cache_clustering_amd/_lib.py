@@ -51,6 +51,8 @@ _SIGS = {
     "decode_attn_logn_workspace_bytes": (_sz, [_desc, _i32, _i32]),
     "decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _sz, _p]),
     "decode_attn_logn_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p, _p]),
+    "kv_append_decode_attn_logn": (ctypes.c_int, [_p, _p, _p, _p, _p, _desc, _i32, _i32, _p, _p,
+                                                  _p, _p, _sz, _p]),
     "kv_append": (ctypes.c_int, [_p, _p, _p, _p, _desc, _p, _p, _p, _p]),
     "csm_host_isa": (ctypes.c_int, []),
     "csm_compress_host": (ctypes.c_int, [_p, _p, _p, _p, _desc, _i32, _i32, _i32, _d, _p, _i32, _p,
@@ -270,6 +272,33 @@ def decode_attn_logn(q, K, V, N, lens, H_q, H_kv, out=None, max_len=None, worksp
                                H_q, H_kv, _ptr(out), _ptr(ws), ws.numel(), _stream(K.device))
     _raise(rc, "decode_attn_logn")
     return out
+
+
+def kv_append_decode_attn_logn(q, K, V, N, lens, H_q, H_kv, k_new, v_new, out=None, max_len=None,
+                               workspace=None):
+    """One decode step in one call: every slice appends (k_new, v_new) with degree 1, then
+    attends; O is fp32 [groups, H_q, d].  max_len bounds the lengths after the append."""
+    _check_cache(K, V, N, lens)
+    S, cap, d = K.shape
+    groups = S // H_kv if H_kv > 0 else 0
+    if q.shape != (groups, H_q, d) or q.dtype != K.dtype or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError(f"q must be a contiguous {K.dtype} GPU tensor [{groups}, {H_q}, {d}]")
+    for t in (k_new, v_new):
+        if t.shape != (S, d) or t.dtype != K.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"k_new / v_new must be contiguous {K.dtype} GPU tensors [{S}, {d}]")
+    if out is None:
+        out = torch.empty((groups, H_q, d), dtype=torch.float32, device=K.device)
+    elif (out.shape != (groups, H_q, d) or out.dtype != torch.float32 or not out.is_contiguous()
+          or not out.is_cuda):
+        raise ValueError("out must be a contiguous fp32 GPU tensor [groups, H_q, d]")
+    desc = cache_desc(K, max_len)
+    ws = _workspace(_lib.decode_attn_logn_workspace_bytes(ctypes.byref(desc), H_q, H_kv),
+                    K.device, workspace)
+    rc = _lib.kv_append_decode_attn_logn(_ptr(q), _ptr(K), _ptr(V), _ptr(N), _ptr(lens),
+                                         ctypes.byref(desc), H_q, H_kv, _ptr(k_new), _ptr(v_new),
+                                         _ptr(out), _ptr(ws), ws.numel(), _stream(K.device))
+    _raise(rc, "kv_append_decode_attn_logn")
+    return out, ws
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

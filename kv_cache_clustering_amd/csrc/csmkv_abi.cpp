@@ -168,7 +168,7 @@ const char *csmkv_status_string(int status) {
   }
 }
 
-int csmkv_version(void) { return 105; }
+int csmkv_version(void) { return 106; }
 
 size_t csm_compress_workspace_bytes(const csmkv_cache *cache, int32_t n1, int32_t n2, int32_t c) {
   if (check_cache(cache) || n1 < 0 || n2 < 0 || c < 2 || c > 512) return 0;
@@ -225,15 +225,22 @@ size_t decode_attn_logn_workspace_bytes(const csmkv_cache *cache, int32_t H_q, i
   return dec_layout(cache, H_q / H_kv).total;
 }
 
-int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t *N,
-                     const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
-                     float *O, void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// decode_attn_logn, and with k_new / v_new the fused append of kv_append_decode_attn_logn.
+int decode_common(const void *q, const void *K, const void *V, const int32_t *N,
+                  const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                  float *O, void *workspace, size_t workspace_bytes, void *stream,
+                  const void *k_new, const void *v_new) {
   int rc = check_cache(cache);
   if (rc) return rc;
   rc = check_heads(cache, H_q, H_kv);
   if (rc) return rc;
   if (!q || !K || !V || !N || !lens || !O) return CSMKV_EINVAL;
   if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16)) return CSMKV_EINVAL;
+  const bool fuse = k_new != nullptr || v_new != nullptr;
+  if (fuse && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
+    return CSMKV_EINVAL;
   const int G = H_q / H_kv;
   const DecLayout lay = dec_layout(cache, G);
   if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < lay.total)
@@ -242,7 +249,7 @@ int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t 
   if (items > (int64_t)INT32_MAX / 2) return CSMKV_EUNSUPPORTED;
   if (cache->num_slices == 0) return CSMKV_OK;
   char *w = static_cast<char *>(workspace);
-  csmkv::DecArgs a;
+  csmkv::DecArgs a = {};
   a.q = static_cast<const char *>(q);
   a.K = static_cast<const char *>(K);
   a.V = static_cast<const char *>(V);
@@ -260,9 +267,35 @@ int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t 
   a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
   a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
   a.part = reinterpret_cast<float *>(w + lay.part);
+  if (fuse) {  // the caller passed writable cache buffers (kv_append_decode_attn_logn)
+    a.k_new = static_cast<const char *>(k_new);
+    a.v_new = static_cast<const char *>(v_new);
+    a.K_app = const_cast<char *>(a.K);
+    a.V_app = const_cast<char *>(a.V);
+    a.N_app = const_cast<int32_t *>(N);
+    a.lens_app = const_cast<int32_t *>(lens);
+  }
   const int e = csmkv::launch_decode(a, cache->dtype, cache->d, G, items,
                                      static_cast<hipStream_t>(stream));
   return e ? CSMKV_EHIP : CSMKV_OK;
+}
+
+}  // namespace
+
+int decode_attn_logn(const void *q, const void *K, const void *V, const int32_t *N,
+                     const int32_t *lens, const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                     float *O, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_common(q, K, V, N, lens, cache, H_q, H_kv, O, workspace, workspace_bytes, stream,
+                       nullptr, nullptr);
+}
+
+int kv_append_decode_attn_logn(const void *q, void *K, void *V, int32_t *N, int32_t *lens,
+                               const csmkv_cache *cache, int32_t H_q, int32_t H_kv,
+                               const void *k_new, const void *v_new, float *O, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  if (!k_new || !v_new) return CSMKV_EINVAL;
+  return decode_common(q, K, V, N, lens, cache, H_q, H_kv, O, workspace, workspace_bytes, stream,
+                       k_new, v_new);
 }
 
 int decode_attn_logn_noalloc(const void *q, const void *K, const void *V, const int32_t *N,
@@ -286,7 +319,7 @@ int decode_attn_logn_noalloc(const void *q, const void *K, const void *V, const 
   void *scr = nullptr;
   if (csmkv::noalloc_scratch(&scr) != 0) return CSMKV_EHIP;
   char *w = static_cast<char *>(scr);
-  csmkv::DecArgs a;
+  csmkv::DecArgs a = {};
   a.q = static_cast<const char *>(q);
   a.K = static_cast<const char *>(K);
   a.V = static_cast<const char *>(V);

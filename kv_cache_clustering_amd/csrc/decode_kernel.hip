@@ -699,7 +699,16 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
 // the partials against a running maximum (rescaling its sums when the maximum grows), four
 // independent items per step, so a slice of up to 4 items per group needs one round trip to
 // memory; the item groups are then merged through LDS against their common maximum and divided.
-template <int G, int D>
+// One element of the storage type as fp32.
+template <typename T>
+__device__ __forceinline__ float as_f32(const T *p) {
+  if constexpr (__is_same(T, __bf16))
+    return __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
+  else
+    return (float)*p;
+}
+
+template <typename T, int G, int D>
 __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
   constexpr int PW = part_width<D>();
   constexpr int CPH = D / 4;               // 4-element columns per head
@@ -707,11 +716,43 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
   constexpr int IG = kCombThreads / COLS;  // item groups
   __shared__ __attribute__((aligned(16))) float s_acc[IG][G][D];
   __shared__ float s_l[IG][G], s_m[IG][G];
+  __shared__ float s_zn[G];  // fused append: the new token's base-2 logit for each head
   const int64_t z = blockIdx.x;
   const int t = threadIdx.x;
   const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
   const float NEG_INF = -__builtin_inff();
   const int i0 = a.item_off[z], i1 = a.item_off[z + 1];
+  // Fused append: the slice appends the token (if its length is below cap) and attends over the
+  // appended length, which must lie within max_len (else the error word is set and the output is
+  // zeros, as a separate append and attention would give).  The split kernel covered the rows
+  // before the token; the token enters here as one more partial with degree 1.
+  // The length is read by one thread and handed on through LDS, so that every read of it
+  // precedes (across the barrier below) the thread's update of it at the end.
+  __shared__ int s_len;
+  const bool fuse = a.k_new != nullptr;
+  auto appends = [&](int s) { return s >= 0 && (int64_t)s < a.cap; };
+  auto attends = [&](int s) {
+    const int s_att = appends(s) ? s + 1 : s;
+    return s_att >= 0 && s_att <= a.max_len && (int64_t)s_att <= a.cap;
+  };
+  if (fuse) {
+    if (t == 0) {
+      const int s = a.lens_app[z];
+      s_len = s;
+      if (!(appends(s) && attends(s))) atomicExch(a.err, kDeviceError);
+    }
+    const int w = t >> 6, l = t & 63;
+    if (w < G) {  // wave w: head w's q . k_new, in fp32 (exact products of the storage type)
+      const T *qh = reinterpret_cast<const T *>(a.q) + (g * a.H_q + kvh * G + w) * (int64_t)D;
+      const T *kn = reinterpret_cast<const T *>(a.k_new) + z * D;
+      float x = 0.f;
+#pragma unroll
+      for (int e = l; e < D; e += 64) x = fmaf(as_f32(qh + e), as_f32(kn + e), x);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+      if (l == 0) s_zn[w] = x * a.scale_log2;  // + log2(1)
+    }
+  }
   // one pass: a running maximum per thread, the sums rescaled when it grows
   const int col = t % COLS, grp = t / COLS, h = col / CPH, e4 = (col % CPH) * 4;
   float M = NEG_INF, acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
@@ -763,11 +804,16 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
     s_m[grp][h] = M;
   }
   __syncthreads();
+  const int s_old = fuse ? s_len : 0;
+  const bool app = fuse && appends(s_old), att_ok = !fuse || attends(s_old);
+  const bool extra = app && att_ok;  // the appended token enters the merge
   for (int i = t; i < G * D; i += kCombThreads) {
     const int hh = i / D, d = i % D;
     float Mx = NEG_INF;
 #pragma unroll
     for (int q = 0; q < IG; ++q) Mx = fmaxf(Mx, s_m[q][hh]);
+    const float zn = extra ? s_zn[hh] : NEG_INF;
+    Mx = fmaxf(Mx, zn);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int q = 0; q < IG; ++q) {
@@ -776,7 +822,25 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
       num = fmaf(wq, s_acc[q][hh][d], num);
       den = fmaf(wq, s_l[q][hh], den);
     }
-    a.O[(g * a.H_q + kvh * G + hh) * (int64_t)D + d] = den > 0.f ? num / den : 0.f;
+    if (extra) {
+      const float wn = __builtin_amdgcn_exp2f(zn - Mx);
+      num = fmaf(wn, as_f32(reinterpret_cast<const T *>(a.v_new) + z * D + d), num);
+      den += wn;
+    }
+    a.O[(g * a.H_q + kvh * G + hh) * (int64_t)D + d] =
+        (fuse && !att_ok) ? 0.f : den > 0.f ? num / den : 0.f;
+  }
+  if (app) {  // the token into the cache (nothing in this call reads those rows again)
+    constexpr int RB = D * (int)sizeof(T);
+    const int64_t row = z * a.cap + s_old;
+    for (int off = t * 16; off < RB; off += kCombThreads * 16) {
+      st16(a.K_app + row * RB + off, ld16(a.k_new + z * RB + off));
+      st16(a.V_app + row * RB + off, ld16(a.v_new + z * RB + off));
+    }
+    if (t == 0) {
+      a.N_app[row] = 1;
+      a.lens_app[z] = s_old + 1;
+    }
   }
 }
 
@@ -798,17 +862,24 @@ static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
                         : launch_dec_t<T, D, false>(a, G, grid, st);
 }
 
-template <int D>
-static int launch_combine(const DecArgs &a, int G, hipStream_t st) {
+template <typename T, int D>
+static int launch_combine_t(const DecArgs &a, int G, hipStream_t st) {
   const dim3 cg((uint32_t)a.num_slices), ct(kCombThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((dec_combine<1, D>), cg, ct, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((dec_combine<2, D>), cg, ct, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((dec_combine<4, D>), cg, ct, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_combine<8, D>), cg, ct, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((dec_combine<T, 1, D>), cg, ct, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((dec_combine<T, 2, D>), cg, ct, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((dec_combine<T, 4, D>), cg, ct, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((dec_combine<T, 8, D>), cg, ct, 0, st, a); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();
+}
+
+template <int D>
+static int launch_combine(const DecArgs &a, int dtype, int G, hipStream_t st) {
+  return dtype == kDtypeF32 ? launch_combine_t<float, D>(a, G, st)
+         : dtype == kDtypeF16 ? launch_combine_t<_Float16, D>(a, G, st)
+                              : launch_combine_t<__bf16, D>(a, G, st);
 }
 
 template <int D>
@@ -859,7 +930,7 @@ int launch_decode_table(const DecArgs &args, int dtype, int d, int G, int64_t ma
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
   if (rc) return rc;
-  return d == 64 ? launch_combine<64>(a, G, st) : launch_combine<128>(a, G, st);
+  return d == 64 ? launch_combine<64>(a, dtype, G, st) : launch_combine<128>(a, dtype, G, st);
 }
 
 int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_items, hipStream_t st) {
@@ -877,7 +948,7 @@ int launch_decode(const DecArgs &args, int dtype, int d, int G, int64_t max_item
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kMaxSplitGroups));
   int rc = d == 64 ? launch_split<64>(a, dtype, G, grid, st) : launch_split<128>(a, dtype, G, grid, st);
   if (rc) return rc;
-  return d == 64 ? launch_combine<64>(a, G, st) : launch_combine<128>(a, G, st);
+  return d == 64 ? launch_combine<64>(a, dtype, G, st) : launch_combine<128>(a, dtype, G, st);
 }
 
 // ------------------------------------------------------------------ append

@@ -47,6 +47,13 @@ struct DecArgs {
   int32_t *item_zp;   // [items][4] (slice, first token, end token, 0) of every work item
   int32_t inline_items;  // 1: the split and combine kernels derive the items from lens
   float *part;        // [items][G][4 + d] (max, sum, 0, 0, o) partials
+  // Fused append (kv_append_decode_attn_logn), null for plain decode: the token k_new, v_new
+  // ([num_slices][d]) each slice appends before it attends.  The split kernel reads the rows
+  // before it; the combine kernel merges the token as one more partial and then writes it into
+  // the cache through K_app, V_app, N_app, lens_app (the same buffers as K, V, N, lens).
+  const char *k_new, *v_new;
+  char *K_app, *V_app;
+  int32_t *N_app, *lens_app;
 };
 
 struct AppArgs {

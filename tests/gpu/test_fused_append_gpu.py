@@ -1,0 +1,114 @@
+"""kv_append_decode_attn_logn (one decode step of Algorithm 1 in one call) against kv_append
+followed by decode_attn_logn, and against the oracle's attention over the appended cache.
+
+Chelsea review, section 三, Algorithm 1: each decode step appends k, v with degree 1, then attends
+with O = Softmax(q K^T / sqrt(d) + log N) V.  The fused call merges the new token as one more
+partial, so its output matches the two calls up to the order of fp32 sums; the cache it leaves
+and the error word must match them exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from tests import parity
+from tests.gpu.conftest import host_cache
+
+pytestmark = pytest.mark.gpu
+
+# The fused call and the two calls differ only in the order of fp32 sums (the new token merged
+# as its own partial instead of inside the last work item): a few fp32 ulps of outputs of order
+# one, far below the bar against the oracle (2e-4 for 16-bit storage, 2e-5 for fp32).
+TWO_CALLS = 1e-5
+
+
+def _oracle_all(q, K, V, N, lens, H_q, H_kv):
+    return oatt.decode_attn_logn(parity.to_f64(q), parity.to_f64(K), parity.to_f64(V),
+                                 N.numpy().astype(np.int64), lens.numpy(), H_q, H_kv)
+
+
+def _both(lib, dev, K, V, N, L, q, kn, vn, H_q, H_kv, max_len):
+    """The two-call step and the fused step on copies of the same cache."""
+    ref = [t.to(dev).clone() for t in (K, V, N, L)]
+    fus = [t.to(dev).clone() for t in (K, V, N, L)]
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws_r = lib.new_workspace(lib.decode_workspace_bytes(ref[0], H_q, H_kv, max_len=max_len), dev)
+    lib.kv_append(*ref, kn, vn, err)
+    O_r = lib.decode_attn_logn(q, *ref, H_q, H_kv, max_len=max_len, workspace=ws_r)
+    O_f, ws_f = lib.kv_append_decode_attn_logn(q, *fus, H_q, H_kv, kn, vn, max_len=max_len)
+    err_r = lib.OK if lib.read_error(err) == lib.OK and lib.read_error(ws_r) == lib.OK else lib.EDEVICE
+    return ref, fus, O_r, O_f, err_r, lib.read_error(ws_f)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("d,H_q,H_kv", [(128, 8, 2), (64, 4, 4), (128, 16, 2), (128, 4, 4)])
+def test_fused_step_matches_append_then_attend(lib, dev, dtype, d, H_q, H_kv):
+    """Ragged lengths with an empty slice (the output is the new value), a slice one row below
+    its capacity (filled by the step) and a full one (not appended: the error word is set, and its
+    attention covers its current rows)."""
+    groups, cap = 3, 2600
+    S = groups * H_kv
+    rng = np.random.default_rng(d + H_q * 3 + H_kv)
+    lens = [int(x) for x in rng.choice([1, 2, 511, 512, 513, 1500, 2047], size=S)]
+    lens[0], lens[1], lens[2] = 2599, 2600, 0
+    K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=d + H_q, degrees=True)
+    gen = torch.Generator().manual_seed(H_q + d)
+    q = torch.randn((groups, H_q, d), generator=gen).to(dtype).to(dev)
+    kn = torch.randn((S, d), generator=gen).to(dtype).to(dev)
+    vn = torch.randn((S, d), generator=gen).to(dtype).to(dev)
+    ref, fus, O_r, O_f, err_r, err_f = _both(lib, dev, K, V, N, L, q, kn, vn, H_q, H_kv, cap)
+    for a, b in zip(ref, fus):
+        assert torch.equal(a, b)
+    assert int(fus[3][0]) == 2600 and int(fus[3][1]) == 2600 and int(fus[3][2]) == 1
+    assert err_r == lib.EDEVICE and err_f == lib.EDEVICE  # the full slice
+    diff = float((O_f - O_r).abs().max())
+    G = H_q // H_kv
+    g1, h1 = divmod(1, H_kv)  # the full slice attends over its current rows, as the two calls
+    assert float((O_f[g1, h1 * G:(h1 + 1) * G] - O_r[g1, h1 * G:(h1 + 1) * G]).abs().max()) < TWO_CALLS
+    o_new = vn[2].float().cpu()  # one row: the attention returns its value
+    for h in range(G):
+        assert torch.allclose(O_f[2 // H_kv, (2 % H_kv) * G + h].cpu(), o_new, atol=1e-6)
+    ref_o = _oracle_all(q.cpu(), *(t.cpu() for t in fus), H_q, H_kv)
+    err_o = float(np.abs(O_f.cpu().double().numpy() - ref_o).max())
+    print(dtype, d, H_q, H_kv, "fused vs two calls", diff, "vs oracle", err_o)
+    assert diff < TWO_CALLS
+    assert err_o < (2e-5 if dtype == torch.float32 else 2e-4)
+
+
+def test_fused_step_length_bound(lib, dev):
+    """A slice whose appended length exceeds max_len: appended, its output zeros and the error
+    word set, as with the two calls; the other slices unaffected."""
+    H_q, H_kv, groups, cap = 8, 2, 2, 700
+    S = groups * H_kv
+    lens = [600, 599, 100, 0]
+    K, V, N, L = host_cache(S, cap, lens, seed=5, degrees=True)
+    gen = torch.Generator().manual_seed(9)
+    q = torch.randn((groups, H_q, 128), generator=gen).to(torch.bfloat16).to(dev)
+    kn = torch.randn((S, 128), generator=gen).to(torch.bfloat16).to(dev)
+    vn = torch.randn((S, 128), generator=gen).to(torch.bfloat16).to(dev)
+    ref, fus, O_r, O_f, err_r, err_f = _both(lib, dev, K, V, N, L, q, kn, vn, H_q, H_kv, 600)
+    for a, b in zip(ref, fus):
+        assert torch.equal(a, b)
+    assert err_r == lib.EDEVICE and err_f == lib.EDEVICE
+    assert torch.all(O_f[0, :4] == 0) and torch.all(O_r[0, :4] == 0)  # slice 0 reached 601
+    assert float((O_f - O_r).abs().max()) < TWO_CALLS
+    assert float(O_f[0, 4:].abs().max()) > 0
+
+
+def test_fused_step_many_slices_plan_kernel(lib, dev):
+    """More slices than the in-kernel plan takes (the plan kernel lays the items out): the same
+    agreement with the two calls."""
+    H_q, H_kv = 1, 1
+    S, cap = 1040, 80
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(0, 79, size=S)]
+    K, V, N, L = host_cache(S, cap, lens, seed=7, degrees=True)
+    gen = torch.Generator().manual_seed(13)
+    q = torch.randn((S, H_q, 128), generator=gen).to(torch.bfloat16).to(dev)
+    kn = torch.randn((S, 128), generator=gen).to(torch.bfloat16).to(dev)
+    vn = torch.randn((S, 128), generator=gen).to(torch.bfloat16).to(dev)
+    ref, fus, O_r, O_f, err_r, err_f = _both(lib, dev, K, V, N, L, q, kn, vn, H_q, H_kv, cap)
+    for a, b in zip(ref, fus):
+        assert torch.equal(a, b)
+    assert err_r == lib.OK and err_f == lib.OK
+    assert float((O_f - O_r).abs().max()) < TWO_CALLS

@@ -268,6 +268,7 @@ def main():
         layer_graph_ms.append(e0.elapsed_time(e1))
     del layer_graph
     dec_alg_now = int(Ld.cpu().numpy().sum()) * ROW_BYTES + w.groups * w.H_q * d * (2 + 4)
+    step_flows = per_layer_steps(lib, w, Kd, Vd, Nd, Ld, q_last, app_k[-1], app_v[-1], stream, dev)
 
     # auxiliary: the out-of-place round (csm_compress_into, pristine cache -> a second cache).
     # Its algorithmic bytes are the in-place round's; it also copies the sinks of every slice and
@@ -441,6 +442,7 @@ def main():
                             "hip_graph_median_us": median(layer_graph_ms) * 1e3,
                             "hip_graph_min_us": min(layer_graph_ms) * 1e3,
                             "hip_graph_GBps": dec_alg_now / (median(layer_graph_ms) * 1e-3) / 1e9},
+                        "per_layer_steps_with_append": step_flows,
                         "traffic": recorded_traffic("dec_split_bf16_g4", DEC_SOURCES)},
         "append_us": app_avg * 1e3,
         "decode_loop_wall_us_per_step": {"eager": eager_us, "hip_graph": graph_us,
@@ -460,6 +462,64 @@ def main():
         "setup_s": setup_s,
     }
     print(json.dumps(out), flush=True)
+
+
+def per_layer_steps(lib, w, Kd, Vd, Nd, Ld, q, k_new, v_new, stream, dev, reps=10, warm=3):
+    """A decode step as a model runs it, layer after layer, each layer appending its token and
+    then attending: kv_append + decode_attn_logn per layer against kv_append_decode_attn_logn per
+    layer, each flow captured in one HIP graph and replayed on its own copy of the serving cache
+    (every replay appends one token to every slice).  After the same replays the two copies must
+    hold the same cache and close outputs."""
+    import torch
+
+    hk = w.H_kv
+    n_app = warm + reps + 1
+    bound = int(Ld.max()) + n_app
+    out = {}
+    caches, outs = {}, {}
+    for flow in ("two_calls", "fused"):
+        K, V, N, L = (t.clone() for t in (Kd, Vd, Nd, Ld))
+        O = torch.empty((w.groups, w.H_q, w.d), dtype=torch.float32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        views = [(K[l * hk:(l + 1) * hk], V[l * hk:(l + 1) * hk], N[l * hk:(l + 1) * hk],
+                  L[l * hk:(l + 1) * hk], O[l:l + 1], k_new[l * hk:(l + 1) * hk],
+                  v_new[l * hk:(l + 1) * hk]) for l in range(w.layers)]
+        ws = lib.new_workspace(lib.decode_workspace_bytes(views[0][0], w.H_q, hk, max_len=bound), dev)
+
+        def step():
+            for layer, (Kl, Vl, Nl, Ll, Ol, kl, vl) in enumerate(views):
+                if flow == "two_calls":
+                    lib.kv_append(Kl, Vl, Nl, Ll, kl, vl, err)
+                    lib.decode_attn_logn(q[layer:layer + 1], Kl, Vl, Nl, Ll, w.H_q, hk, out=Ol,
+                                         max_len=bound, workspace=ws)
+                else:
+                    lib.kv_append_decode_attn_logn(q[layer:layer + 1], Kl, Vl, Nl, Ll, w.H_q, hk,
+                                                   kl, vl, out=Ol, max_len=bound, workspace=ws)
+        step()  # one eager step, then the captured steps
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        ms = []
+        for i in range(warm + reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= warm:
+                ms.append(e0.elapsed_time(e1))
+        del graph
+        assert lib.read_error(ws) == lib.OK and lib.read_error(err) == lib.OK
+        out[flow] = {"hip_graph_median_us": median(ms) * 1e3, "hip_graph_min_us": min(ms) * 1e3}
+        caches[flow], outs[flow] = (K, V, N, L), O
+    for a, b in zip(caches["two_calls"], caches["fused"]):
+        assert torch.equal(a, b)
+    out["max_abs_fused_vs_two_calls"] = float((outs["fused"] - outs["two_calls"]).abs().max())
+    out["steps_replayed"] = n_app
+    del caches, outs
+    torch.cuda.empty_cache()
+    return out
 
 
 def index_decode(lib, w, Kd, Vd, Nd, Ld, q, stream, dev, B=64, tau=8.0):

@@ -726,8 +726,11 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
   // appended length, which must lie within max_len (else the error word is set and the output is
   // zeros, as a separate append and attention would give).  The split kernel covered the rows
   // before the token; the token enters here as one more partial with degree 1.
-  // The length is read by one thread and handed on through LDS, so that every read of it
-  // precedes (across the barrier below) the thread's update of it at the end.
+  // Wave 0 alone reads the length; it loads one 16-byte segment of the token's K or V row per
+  // lane, and waves 0 .. G-1 load q_h and the token's key.  The loads are issued here and used
+  // after the partial loop (so they wait with it): wave 0 then appends the token and hands the
+  // old length to the other waves through LDS (read after the barrier below), and waves
+  // 0 .. G-1 form the token's logits.
   __shared__ int s_len;
   const bool fuse = a.k_new != nullptr;
   auto appends = [&](int s) { return s >= 0 && (int64_t)s < a.cap; };
@@ -735,22 +738,28 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
     const int s_att = appends(s) ? s + 1 : s;
     return s_att >= 0 && s_att <= a.max_len && (int64_t)s_att <= a.cap;
   };
+  constexpr int RB = D * (int)sizeof(T), SEGR = RB / 16;  // 16-byte segments of a row
+  static_assert(2 * SEGR <= 64, "one wave copies the K and V rows");
+  const int wv = t >> 6, ln = t & 63;
+  int s_ld = 0;
+  u32x4 seg = {0u, 0u, 0u, 0u};
+  float qx[D / 64], kx[D / 64];
   if (fuse) {
-    if (t == 0) {
-      const int s = a.lens_app[z];
-      s_len = s;
-      if (!(appends(s) && attends(s))) atomicExch(a.err, kDeviceError);
+    if (wv == 0) {
+      s_ld = a.lens_app[z];
+      if (ln < SEGR)
+        seg = ld16(a.k_new + z * RB + ln * 16);
+      else if (ln < 2 * SEGR)
+        seg = ld16(a.v_new + z * RB + (ln - SEGR) * 16);
     }
-    const int w = t >> 6, l = t & 63;
-    if (w < G) {  // wave w: head w's q . k_new, in fp32 (exact products of the storage type)
-      const T *qh = reinterpret_cast<const T *>(a.q) + (g * a.H_q + kvh * G + w) * (int64_t)D;
+    if (wv < G) {  // head wv's q and the token's key, elements ln + 64 e
+      const T *qh = reinterpret_cast<const T *>(a.q) + (g * a.H_q + kvh * G + wv) * (int64_t)D;
       const T *kn = reinterpret_cast<const T *>(a.k_new) + z * D;
-      float x = 0.f;
 #pragma unroll
-      for (int e = l; e < D; e += 64) x = fmaf(as_f32(qh + e), as_f32(kn + e), x);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-      if (l == 0) s_zn[w] = x * a.scale_log2;  // + log2(1)
+      for (int e = 0; e < D / 64; ++e) {
+        qx[e] = as_f32(qh + ln + 64 * e);
+        kx[e] = as_f32(kn + ln + 64 * e);
+      }
     }
   }
   // one pass: a running maximum per thread, the sums rescaled when it grows
@@ -797,6 +806,33 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
     rescale(head.x);
     add(head.x, head.y, *reinterpret_cast<const float4 *>(pp + 4 + e4));
   }
+  if (fuse) {
+    if (wv < G) {  // head wv's logit of the token, in fp32 (exact products of the storage type)
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) x = fmaf(qx[e], kx[e], x);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+      if (ln == 0) s_zn[wv] = x * a.scale_log2;  // + log2(1)
+    }
+    if (wv == 0) {  // the token into the cache (nothing in this call reads those rows again)
+      if (appends(s_ld)) {
+        const int64_t row = z * a.cap + s_ld;
+        if (ln < SEGR)
+          st16(a.K_app + row * RB + ln * 16, seg);
+        else if (ln < 2 * SEGR)
+          st16(a.V_app + row * RB + (ln - SEGR) * 16, seg);
+      }
+      if (ln == 0) {
+        s_len = s_ld;
+        if (appends(s_ld)) {
+          a.N_app[z * a.cap + s_ld] = 1;
+          a.lens_app[z] = s_ld + 1;
+        }
+        if (!(appends(s_ld) && attends(s_ld))) atomicExch(a.err, kDeviceError);
+      }
+    }
+  }
   // every column of (grp, h) saw the same maxima, so one of them records M and L
   *reinterpret_cast<float4 *>(&s_acc[grp][h][e4]) = make_float4(acc0, acc1, acc2, acc3);
   if (e4 == 0) {
@@ -829,18 +865,6 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
     }
     a.O[(g * a.H_q + kvh * G + hh) * (int64_t)D + d] =
         (fuse && !att_ok) ? 0.f : den > 0.f ? num / den : 0.f;
-  }
-  if (app) {  // the token into the cache (nothing in this call reads those rows again)
-    constexpr int RB = D * (int)sizeof(T);
-    const int64_t row = z * a.cap + s_old;
-    for (int off = t * 16; off < RB; off += kCombThreads * 16) {
-      st16(a.K_app + row * RB + off, ld16(a.k_new + z * RB + off));
-      st16(a.V_app + row * RB + off, ld16(a.v_new + z * RB + off));
-    }
-    if (t == 0) {
-      a.N_app[row] = 1;
-      a.lens_app[z] = s_old + 1;
-    }
   }
 }
 

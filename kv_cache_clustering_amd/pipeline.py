@@ -45,7 +45,6 @@ class ClusteredKVCache:
         cap = K.shape[1]
         self.ws_csm = lib.new_workspace(lib.csm_workspace_bytes(K, n1, n2, c, max_len=cap), dev)
         self.ws_dec = lib.new_workspace(lib.decode_workspace_bytes(K, H_q, H_kv, max_len=cap), dev)
-        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         groups = K.shape[0] // H_kv
         self.out = torch.empty((groups, H_q, K.shape[2]), dtype=torch.float32, device=dev)
 
@@ -80,12 +79,12 @@ class ClusteredKVCache:
     def decode_step(self, q, k_new, v_new, out=None):
         """Append, attend, then cluster if the trigger fires.  Returns (O, r or None)."""
         self.step_index += 1
-        lib.kv_append(self.K, self.V, self.N, self.lens, k_new, v_new, self.err)
         self.sched.append()
         self.outlier_len += 1
-        O = lib.decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
-                                 out=self.out if out is None else out, max_len=self.max_len,
-                                 workspace=self.ws_dec)
+        O, _ = lib.kv_append_decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q,
+                                              self.H_kv, k_new, v_new,
+                                              out=self.out if out is None else out,
+                                              max_len=self.max_len, workspace=self.ws_dec)
         r = None
         if self.sched.over_budget():
             s_before = self.sched.s
@@ -94,7 +93,7 @@ class ClusteredKVCache:
         return O, r
 
     def capture_decode(self):
-        """Capture one decode step's append + attention into a HIP graph.
+        """Capture one decode step (append + attention, one fused call) into a HIP graph.
 
         The launch bounds are fixed at the cache capacity (the kernels read the actual
         lengths on the device), so one graph serves every step.  Step inputs are read from
@@ -110,9 +109,9 @@ class ClusteredKVCache:
         torch.cuda.synchronize(dev)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            lib.kv_append(self.K, self.V, self.N, self.lens, self.k_in, self.v_in, self.err)
-            lib.decode_attn_logn(self.q_in, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
-                                 out=self.out, max_len=cap, workspace=self.ws_dec)
+            lib.kv_append_decode_attn_logn(self.q_in, self.K, self.V, self.N, self.lens, self.H_q,
+                                           self.H_kv, self.k_in, self.v_in, out=self.out,
+                                           max_len=cap, workspace=self.ws_dec)
         self.graph = graph
 
     def decode_step_graph(self, q=None, k_new=None, v_new=None):
@@ -187,14 +186,14 @@ class ClusteredKVCache:
         """decode_step with the trigger and r decided on the device: nothing on the host
         decides whether the round runs.  The host bookkeeping is advanced in closed form so
         that it keeps the same lengths.  Returns (O, r the host expects, or None)."""
-        lib.kv_append(self.K, self.V, self.N, self.lens, k_new, v_new, self.err)
         self.step_index += 1
         self.sched.append()
         self.outlier_len += 1
         bound = self.max_len  # lengths after the append, before any round
-        O = lib.decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q, self.H_kv,
-                                 out=self.out if out is None else out, max_len=bound,
-                                 workspace=self.ws_dec)
+        O, _ = lib.kv_append_decode_attn_logn(q, self.K, self.V, self.N, self.lens, self.H_q,
+                                              self.H_kv, k_new, v_new,
+                                              out=self.out if out is None else out,
+                                              max_len=bound, workspace=self.ws_dec)
         self._triggered_round(self.sched.s)  # slices that can run share this length
         r = self.sched.next_round(self.step_index) if self.sched.over_budget() else None
         return O, r
@@ -221,11 +220,10 @@ class ClusteredKVCache:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(steps):
-                lib.kv_append(self.K, self.V, self.N, self.lens, self.loop_k[i], self.loop_v[i],
-                              self.err)
-                lib.decode_attn_logn(self.loop_q[i], self.K, self.V, self.N, self.lens, self.H_q,
-                                     self.H_kv, out=self.loop_out[i], max_len=cap,
-                                     workspace=self.ws_dec)
+                lib.kv_append_decode_attn_logn(self.loop_q[i], self.K, self.V, self.N, self.lens,
+                                               self.H_q, self.H_kv, self.loop_k[i],
+                                               self.loop_v[i], out=self.loop_out[i], max_len=cap,
+                                               workspace=self.ws_dec)
                 self._triggered_round(round_bound, observe=False)
         self.loop_graph = graph
         self.loop_steps = steps
@@ -249,7 +247,7 @@ class ClusteredKVCache:
     def check_errors(self):
         """Synchronise and raise if a kernel flagged a bad length since the cache was built
         (the error words are sticky)."""
-        for word in (self.ws_csm, self.ws_dec, self.err):
+        for word in (self.ws_csm, self.ws_dec):
             rc = lib.read_error(word)
             if rc != lib.OK:
                 raise lib.CsmkvError(rc, "device")

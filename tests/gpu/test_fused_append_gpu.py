@@ -112,3 +112,46 @@ def test_fused_step_many_slices_plan_kernel(lib, dev):
         assert torch.equal(a, b)
     assert err_r == lib.OK and err_f == lib.OK
     assert float((O_f - O_r).abs().max()) < TWO_CALLS
+
+
+def test_fused_step_64k_budget_cache(lib, dev):
+    """The benchmark's cache compressed to the 20% budget on the GPU (outlier slices at 64K): one
+    fused step over all 32 layers against the two calls (cache identical, outputs within the
+    sum-order bar) and sampled heads against the oracle over the appended cache."""
+    import kvsynth
+    from kv_cache_clustering_amd.schedule import Algorithm1, round_output_length
+    w = kvsynth.workload(4)
+    c = kvsynth.make_cache(w, dev)
+    K, V, N, lens, mask = c["K"], c["V"], c["N"], c["lens"], c["mask"]
+    sched = Algorithm1(n=w.ctx, R=w.R, Gamma=w.steps)
+    s_prev = w.ctx
+    for r in sched.prefill_rounds():
+        lib.csm_compress(K, V, N, lens, w.n1, w.n2, w.c, r, mask, max_len=s_prev)
+        s_prev = round_output_length(s_prev, w.n1, w.n2, w.c, r)
+    torch.cuda.synchronize()
+    q = kvsynth.make_queries(w, dev, steps=1)[0]
+    kn, vn = c["app_k"][0], c["app_v"][0]
+    ref, fus, O_r, O_f, err_r, err_f = _both(lib, dev, K, V, N, lens, q, kn, vn, w.H_q, w.H_kv,
+                                             w.ctx + 1)
+    del c, K, V, N
+    assert err_r == lib.OK and err_f == lib.OK
+    for a, b in zip(ref, fus):
+        assert torch.equal(a, b)
+    diff = float((O_f - O_r).abs().max())
+    Kf, Vf, Nf, Lf = fus
+    maskh = mask.cpu().numpy()
+    Oh = O_f.cpu().double().numpy()
+    worst = 0.0
+    for z in [0, 77, 255] + [int(x) for x in np.nonzero(maskh)[0][:1]]:
+        g, kvh = divmod(z, w.H_kv)
+        s = int(Lf[z])
+        Kz, Vz = parity.to_f64(Kf[z, :s].cpu()), parity.to_f64(Vf[z, :s].cpu())
+        Nz = Nf[z, :s].cpu().numpy().astype(np.int64)
+        assert int(Nz.sum()) == w.ctx + 1
+        for h in range(w.G):
+            hq = kvh * w.G + h
+            o = oatt.logn_attention_one(parity.to_f64(q[g, hq].cpu()), Kz, Vz, Nz)
+            worst = max(worst, float(np.abs(Oh[g, hq] - o).max()))
+    print("fused vs two calls", diff, "vs oracle", worst)
+    assert diff < TWO_CALLS
+    assert worst < 2e-4

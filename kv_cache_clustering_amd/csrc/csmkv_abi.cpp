@@ -130,14 +130,15 @@ int csm_common(const void *K_in, const void *V_in, const int32_t *N_in, const in
 }
 
 struct DecLayout {
-  size_t item_off, item_zp, part, total;
+  size_t item_off, s_in, item_zp, part, total;
 };
 
 DecLayout dec_layout(const csmkv_cache *c, int G) {
   DecLayout L;
   const int64_t items = csmkv::dec_max_items(c->num_slices, c->max_len);
   L.item_off = kAlign;
-  L.item_zp = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
+  L.s_in = L.item_off + align_up((size_t)(c->num_slices + 1) * 4);
+  L.item_zp = L.s_in + align_up((size_t)c->num_slices * 4);
   L.part = L.item_zp + align_up((size_t)items * 16);
   L.total = L.part + align_up((size_t)items * G * (4 + c->d) * 4);
   return L;
@@ -265,6 +266,7 @@ int decode_common(const void *q, const void *K, const void *V, const int32_t *N,
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cache->d));
   a.err = reinterpret_cast<int32_t *>(w);
   a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
+  a.s_in = reinterpret_cast<int32_t *>(w + lay.s_in);
   a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
   a.part = reinterpret_cast<float *>(w + lay.part);
   if (fuse) {  // the caller passed writable cache buffers (kv_append_decode_attn_logn)
@@ -335,6 +337,7 @@ int decode_attn_logn_noalloc(const void *q, const void *K, const void *V, const 
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)cache->d));
   a.err = error_word;
   a.item_off = reinterpret_cast<int32_t *>(w + lay.item_off);
+  a.s_in = reinterpret_cast<int32_t *>(w + lay.s_in);
   a.item_zp = reinterpret_cast<int32_t *>(w + lay.item_zp);
   a.part = reinterpret_cast<float *>(w + lay.part);
   const int e = csmkv::launch_decode(a, cache->dtype, cache->d, G, items,

@@ -105,6 +105,7 @@ __global__ void __launch_bounds__(1024) dec_prep(DecArgs a) {
   for (int64_t z = z0; z < z1; ++z) {
     a.item_off[z] = run;
     const int s = a.lens[z];
+    a.s_in[z] = s;  // the length as read, for the combine kernel's fused append
     const int cnt = len_ok(a, s) ? (s + a.tsplit - 1) / a.tsplit : 0;
     for (int p = 0; p < cnt; ++p)  // (slice, first token, end token): one load in dec_split
       *reinterpret_cast<int4 *>(a.item_zp + 4 * (int64_t)(run + p)) =
@@ -486,7 +487,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     w_incl = incl;
     total = __builtin_amdgcn_readlane(incl, 63);
     if (blockIdx.x == 0 && w == 0) {  // offsets for the combine kernel; a bad length is sticky
-      if (l < S) a.item_off[l] = incl - cnt;
+      if (l < S) {
+        a.item_off[l] = incl - cnt;
+        a.s_in[l] = sl;  // the length as read, for the combine kernel's fused append
+      }
       if (l == 0) a.item_off[S] = total;
       const uint64_t badm = __ballot(!ok);
       if (l == 0 && badm != 0) atomicExch(a.err, kDeviceError);
@@ -513,7 +517,10 @@ __global__ void __launch_bounds__(kDecThreads, 2) dec_split(DecArgs a) {
     total = __builtin_amdgcn_readfirstlane(total);
     for (int z = z0; z < z1; ++z) {
       s_off[z] = run;
-      if (blockIdx.x == 0) a.item_off[z] = run;
+      if (blockIdx.x == 0) {
+        a.item_off[z] = run;
+        a.s_in[z] = a.lens[z];  // the length as read, for the combine kernel's fused append
+      }
       run += (s_len[z] + ts - 1) / ts;
     }
     if (blockIdx.x == 0 && t == 0) a.item_off[S] = total;
@@ -708,16 +715,23 @@ __device__ __forceinline__ float as_f32(const T *p) {
     return (float)*p;
 }
 
-template <typename T, int G, int D>
-__global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
+// Threads of a combine workgroup serving HPW of a slice's G heads: 256 for one head (calls over
+// few slices spread the merge over G workgroups per slice), kCombThreads for all G.
+template <int G, int HPW>
+constexpr int comb_threads() { return HPW == 1 && G > 1 ? 256 : kCombThreads; }
+
+template <typename T, int G, int D, int HPW>
+__global__ void __launch_bounds__((comb_threads<G, HPW>())) dec_combine(DecArgs a) {
+  constexpr int NT = comb_threads<G, HPW>();
   constexpr int PW = part_width<D>();
   constexpr int CPH = D / 4;               // 4-element columns per head
-  constexpr int COLS = CPH * G;            // columns over the G heads
-  constexpr int IG = kCombThreads / COLS;  // item groups
-  __shared__ __attribute__((aligned(16))) float s_acc[IG][G][D];
-  __shared__ float s_l[IG][G], s_m[IG][G];
-  __shared__ float s_zn[G];  // fused append: the new token's base-2 logit for each head
-  const int64_t z = blockIdx.x;
+  constexpr int COLS = CPH * HPW;          // columns over the workgroup's heads
+  constexpr int IG = NT / COLS;            // item groups
+  __shared__ __attribute__((aligned(16))) float s_acc[IG][HPW][D];
+  __shared__ float s_l[IG][HPW], s_m[IG][HPW];
+  __shared__ float s_zn[HPW];  // fused append: the new token's base-2 logit for each head
+  const int64_t z = blockIdx.x / (G / HPW);
+  const int hb = (int)(blockIdx.x % (G / HPW)) * HPW;  // the workgroup's first head
   const int t = threadIdx.x;
   const int64_t g = z / a.H_kv, kvh = z % a.H_kv;
   const float NEG_INF = -__builtin_inff();
@@ -725,13 +739,11 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
   // Fused append: the slice appends the token (if its length is below cap) and attends over the
   // appended length, which must lie within max_len (else the error word is set and the output is
   // zeros, as a separate append and attention would give).  The split kernel covered the rows
-  // before the token; the token enters here as one more partial with degree 1.
-  // Wave 0 alone reads the length; it loads one 16-byte segment of the token's K or V row per
-  // lane, and waves 0 .. G-1 load q_h and the token's key.  The loads are issued here and used
-  // after the partial loop (so they wait with it): wave 0 then appends the token and hands the
-  // old length to the other waves through LDS (read after the barrier below), and waves
-  // 0 .. G-1 form the token's logits.
-  __shared__ int s_len;
+  // before the token and recorded the length it read in s_in; the token enters here as one more
+  // partial with degree 1.  Loads for it are issued before the partial loop and used after it
+  // (so they wait with it): waves 0 .. HPW-1 load q_h and the token's key and form its logits;
+  // wave 0 of the slice's first workgroup loads the token's K and V rows (a 16-byte segment per
+  // lane) and appends the token to the cache.
   const bool fuse = a.k_new != nullptr;
   auto appends = [&](int s) { return s >= 0 && (int64_t)s < a.cap; };
   auto attends = [&](int s) {
@@ -740,20 +752,22 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
   };
   constexpr int RB = D * (int)sizeof(T), SEGR = RB / 16;  // 16-byte segments of a row
   static_assert(2 * SEGR <= 64, "one wave copies the K and V rows");
+  static_assert(NT / 64 >= HPW, "a wave per head for the token's logit");
   const int wv = t >> 6, ln = t & 63;
-  int s_ld = 0;
+  const int s_old = fuse ? a.s_in[z] : 0;
+  const bool appender = fuse && hb == 0 && wv == 0;
   u32x4 seg = {0u, 0u, 0u, 0u};
   float qx[D / 64], kx[D / 64];
   if (fuse) {
-    if (wv == 0) {
-      s_ld = a.lens_app[z];
+    if (appender) {
       if (ln < SEGR)
         seg = ld16(a.k_new + z * RB + ln * 16);
       else if (ln < 2 * SEGR)
         seg = ld16(a.v_new + z * RB + (ln - SEGR) * 16);
     }
-    if (wv < G) {  // head wv's q and the token's key, elements ln + 64 e
-      const T *qh = reinterpret_cast<const T *>(a.q) + (g * a.H_q + kvh * G + wv) * (int64_t)D;
+    if (wv < HPW) {  // head hb + wv's q and the token's key, elements ln + 64 e
+      const T *qh =
+          reinterpret_cast<const T *>(a.q) + (g * a.H_q + kvh * G + hb + wv) * (int64_t)D;
       const T *kn = reinterpret_cast<const T *>(a.k_new) + z * D;
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) {
@@ -763,7 +777,7 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
     }
   }
   // one pass: a running maximum per thread, the sums rescaled when it grows
-  const int col = t % COLS, grp = t / COLS, h = col / CPH, e4 = (col % CPH) * 4;
+  const int col = t % COLS, grp = t / COLS, hl = col / CPH, h = hb + hl, e4 = (col % CPH) * 4;
   float M = NEG_INF, acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f, L = 0.f;
   auto rescale = [&](float mnew) {
     if (mnew > M) {
@@ -806,8 +820,9 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
     rescale(head.x);
     add(head.x, head.y, *reinterpret_cast<const float4 *>(pp + 4 + e4));
   }
+  const bool app = fuse && appends(s_old), att_ok = !fuse || attends(s_old);
   if (fuse) {
-    if (wv < G) {  // head wv's logit of the token, in fp32 (exact products of the storage type)
+    if (wv < HPW) {  // head hb + wv's logit of the token, in fp32 (exact storage-type products)
       float x = 0.f;
 #pragma unroll
       for (int e = 0; e < D / 64; ++e) x = fmaf(qx[e], kx[e], x);
@@ -815,35 +830,32 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
       for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
       if (ln == 0) s_zn[wv] = x * a.scale_log2;  // + log2(1)
     }
-    if (wv == 0) {  // the token into the cache (nothing in this call reads those rows again)
-      if (appends(s_ld)) {
-        const int64_t row = z * a.cap + s_ld;
+    if (appender) {  // the token into the cache (nothing in this call reads those rows again)
+      if (app) {
+        const int64_t row = z * a.cap + s_old;
         if (ln < SEGR)
           st16(a.K_app + row * RB + ln * 16, seg);
         else if (ln < 2 * SEGR)
           st16(a.V_app + row * RB + (ln - SEGR) * 16, seg);
       }
       if (ln == 0) {
-        s_len = s_ld;
-        if (appends(s_ld)) {
-          a.N_app[z * a.cap + s_ld] = 1;
-          a.lens_app[z] = s_ld + 1;
+        if (app) {
+          a.N_app[z * a.cap + s_old] = 1;
+          a.lens_app[z] = s_old + 1;
         }
-        if (!(appends(s_ld) && attends(s_ld))) atomicExch(a.err, kDeviceError);
+        if (!(app && att_ok)) atomicExch(a.err, kDeviceError);
       }
     }
   }
-  // every column of (grp, h) saw the same maxima, so one of them records M and L
-  *reinterpret_cast<float4 *>(&s_acc[grp][h][e4]) = make_float4(acc0, acc1, acc2, acc3);
+  // every column of (grp, hl) saw the same maxima, so one of them records M and L
+  *reinterpret_cast<float4 *>(&s_acc[grp][hl][e4]) = make_float4(acc0, acc1, acc2, acc3);
   if (e4 == 0) {
-    s_l[grp][h] = L;
-    s_m[grp][h] = M;
+    s_l[grp][hl] = L;
+    s_m[grp][hl] = M;
   }
   __syncthreads();
-  const int s_old = fuse ? s_len : 0;
-  const bool app = fuse && appends(s_old), att_ok = !fuse || attends(s_old);
   const bool extra = app && att_ok;  // the appended token enters the merge
-  for (int i = t; i < G * D; i += kCombThreads) {
+  for (int i = t; i < HPW * D; i += NT) {
     const int hh = i / D, d = i % D;
     float Mx = NEG_INF;
 #pragma unroll
@@ -863,7 +875,7 @@ __global__ void __launch_bounds__(kCombThreads) dec_combine(DecArgs a) {
       num = fmaf(wn, as_f32(reinterpret_cast<const T *>(a.v_new) + z * D + d), num);
       den += wn;
     }
-    a.O[(g * a.H_q + kvh * G + hh) * (int64_t)D + d] =
+    a.O[(g * a.H_q + kvh * G + hb + hh) * (int64_t)D + d] =
         (fuse && !att_ok) ? 0.f : den > 0.f ? num / den : 0.f;
   }
 }
@@ -886,14 +898,29 @@ static int launch_dec_t(const DecArgs &a, int G, int grid, hipStream_t st) {
                         : launch_dec_t<T, D, false>(a, G, grid, st);
 }
 
+// Calls over at most this many slices (a layer's KV heads) merge with a workgroup per (slice,
+// head): G times the workgroups, each reading a quarter of the slice's partials at G = 4, so
+// the few slices of a per-layer call are not merged on a handful of CUs.  The result is the same
+// bit for bit (each head's merge is unchanged).
+constexpr int64_t kCombPerHeadSlices = 64;
+
+template <typename T, int G, int D>
+static void launch_combine_g(const DecArgs &a, hipStream_t st) {
+  if (G > 1 && a.num_slices <= kCombPerHeadSlices)
+    hipLaunchKernelGGL((dec_combine<T, G, D, 1>), dim3((uint32_t)(a.num_slices * G)),
+                       dim3(comb_threads<G, 1>()), 0, st, a);
+  else
+    hipLaunchKernelGGL((dec_combine<T, G, D, G>), dim3((uint32_t)a.num_slices),
+                       dim3(comb_threads<G, G>()), 0, st, a);
+}
+
 template <typename T, int D>
 static int launch_combine_t(const DecArgs &a, int G, hipStream_t st) {
-  const dim3 cg((uint32_t)a.num_slices), ct(kCombThreads);
   switch (G) {
-    case 1: hipLaunchKernelGGL((dec_combine<T, 1, D>), cg, ct, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((dec_combine<T, 2, D>), cg, ct, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((dec_combine<T, 4, D>), cg, ct, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((dec_combine<T, 8, D>), cg, ct, 0, st, a); break;
+    case 1: launch_combine_g<T, 1, D>(a, st); break;
+    case 2: launch_combine_g<T, 2, D>(a, st); break;
+    case 4: launch_combine_g<T, 4, D>(a, st); break;
+    case 8: launch_combine_g<T, 8, D>(a, st); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

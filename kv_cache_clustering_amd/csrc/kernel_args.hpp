@@ -44,6 +44,7 @@ struct DecArgs {
   float scale_log2;   // log2(e) / sqrt(d)
   int32_t *err;       // sticky device error word (set on a bad length, never cleared here)
   int32_t *item_off;  // [num_slices + 1] first work item of each slice (plan kernel only)
+  int32_t *s_in;      // [num_slices] each length as the plan read it (for the fused append)
   int32_t *item_zp;   // [items][4] (slice, first token, end token, 0) of every work item
   int32_t inline_items;  // 1: the split and combine kernels derive the items from lens
   float *part;        // [items][G][4 + d] (max, sum, 0, 0, o) partials

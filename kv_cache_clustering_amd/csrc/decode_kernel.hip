@@ -20,9 +20,11 @@
 //                 FMAs with a DPP reduction over the lanes of a row, and at G = 8 two
 //                 workgroups of four heads each.  Waves merge in LDS; each item writes one
 //                 (max, sum, 0, 0, o[d]) partial per head.
-//   dec_combine : one 1024-thread workgroup per slice merges the item partials by
-//                 log-sum-exp (a running maximum per thread over item groups in parallel,
-//                 then the groups merged against their common maximum).
+//   dec_combine : one 1024-thread workgroup per slice (per (slice, head), 256 threads, for
+//                 calls over at most 64 slices) merges the item partials by log-sum-exp (a
+//                 running maximum per thread over item groups in parallel, then the groups
+//                 merged against their common maximum); for kv_append_decode_attn_logn it also
+//                 merges the appended token as one more partial and writes it into the cache.
 #include <algorithm>
 #include <mutex>
 

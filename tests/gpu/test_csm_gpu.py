@@ -407,6 +407,36 @@ def test_seeded_sweep_of_shapes_and_parameters(lib, dev):
     parity.check_report(total)
 
 
+def test_seeded_sweep_long_slices(lib, dev):
+    """600 more seeded configurations with slices up to ~40 chunks long: chunk sizes around the
+    tile edges (127..129, 255..257, 511), sinks / recent 0..129, r in {0, 0.05, 0.1, 0.2, 0.5, 1}
+    or random, AR(1) keys of correlation 0, 0.5, 0.95 or 0.99, every format and both head dims,
+    random outlier masks; each slice compared with the oracle.  fp32 storage may use the
+    absolute floor where a merged mean cancels (counted in the report)."""
+    rng = np.random.default_rng(91)
+    dtypes = [torch.bfloat16, torch.float16, torch.float32]
+    total = parity.Report()
+    for case in range(600):
+        dtype = dtypes[case % 3]
+        d = 64 if rng.random() < 0.5 else 128
+        cmax = 256 if dtype == torch.float32 else 512
+        c = int(rng.choice([2, 3, 4, 7, 16, 33, 64, 127, 128, 129, 200, 255, 256, 257, 300, 384,
+                            511, cmax, int(rng.integers(2, cmax + 1))]))
+        c = min(c, cmax)
+        n1, n2 = int(rng.integers(0, 130)), int(rng.integers(0, 130))
+        r = float(rng.choice([0.0, 1.0, 0.5, 0.1, 0.05, 0.2, float(rng.random())]))
+        S = int(rng.integers(1, 7))
+        cap = int(rng.integers(n1 + n2 + 2, n1 + n2 + 40 * c + 400))
+        lens = [int(rng.choice([0, 1, n1 + n2, min(cap, n1 + n2 + 1), min(cap, n1 + n2 + 2), cap,
+                                int(rng.integers(0, cap + 1))])) for _ in range(S)]
+        K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=9100000 + case, degrees=True,
+                                rho=float(rng.choice([0.95, 0.5, 0.99, 0.0])))
+        mask = (rng.random(S) < 0.25).astype(np.uint8)
+        total.add(run_and_compare(lib, dev, K, V, N, L, n1, n2, c, r, mask))
+    print(total)
+    parity.check_report(total)
+
+
 def test_error_word_is_sticky_until_cleared(lib, dev):
     """A bad length flagged by one call stays visible after later clean calls on the same
     workspace (as in a loop or a graph replay of many calls) until csmkv_clear_error; the

@@ -56,7 +56,8 @@ def check_values(rep, gpu_vals, oracle_vals, storage):
     fp32 storage, fp16 steps for fp16) of the oracle's value.  Where a weighted mean
     cancels to a value far below its terms, fp32 accumulation error (about 2**-24 of the
     terms) can exceed one ulp of the tiny result; such elements pass when the absolute
-    difference is below 2**-20 and are counted in rep.abs_floor_used."""
+    difference is below 2**-20 and are counted in rep.abs_floor_used (rep.abs_floor_used_f32 for
+    fp32 storage)."""
     g = np.asarray(gpu_vals, np.float64)
     o = np.asarray(oracle_vals, np.float64)
     if g.size == 0:
@@ -76,7 +77,10 @@ def check_values(rep, gpu_vals, oracle_vals, storage):
         ulp_bf16 = np.ldexp(1.0, np.maximum(e, -125) - 8)
         bad = diff > ulp_bf16
     floor_ok = bad & (diff <= ABS_FLOOR)
-    rep.abs_floor_used += int(floor_ok.sum())
+    if storage == "f32":
+        rep.abs_floor_used_f32 += int(floor_ok.sum())
+    else:
+        rep.abs_floor_used += int(floor_ok.sum())
     hard = bad & ~floor_ok
     assert not hard.any(), ("K/V differ by more than one ulp", storage, float(diff[hard].max()))
 
@@ -99,7 +103,8 @@ class Report:
         self.followed_chunks = 0
         self.max_ulp = 0
         self.max_abs = 0.0
-        self.abs_floor_used = 0
+        self.abs_floor_used = 0      # 16-bit storage
+        self.abs_floor_used_f32 = 0  # fp32 storage (compared against one bf16 step: see check_values)
         self.slices = 0
         self.exact_match_ties = 0   # A rows whose best fp64 score is attained by >= 2 B rows
         self.exact_cut_ties = 0     # chunks whose selection cut falls inside a run of equal scores
@@ -112,13 +117,15 @@ class Report:
                 f"match_hard={self.match_hard}, sel_near={self.sel_near}, sel_hard={self.sel_hard}, "
                 f"followed={self.followed_chunks}, max_ulp={self.max_ulp}, "
                 f"max_abs={self.max_abs:.3g}, abs_floor_used={self.abs_floor_used}, "
+                f"abs_floor_used_f32={self.abs_floor_used_f32}, "
                 f"near_frac={self.near_fraction():.2e}, exact_match_ties={self.exact_match_ties}, "
                 f"exact_cut_ties={self.exact_cut_ties})")
 
     def add(self, other):
         """Accumulate another report's counts into this one."""
         for f in ("edges", "match_near", "match_hard", "sel_near", "sel_hard", "followed_chunks",
-                  "abs_floor_used", "slices", "exact_match_ties", "exact_cut_ties"):
+                  "abs_floor_used", "abs_floor_used_f32", "slices", "exact_match_ties",
+                  "exact_cut_ties"):
             setattr(self, f, getattr(self, f) + getattr(other, f))
         self.max_ulp = max(self.max_ulp, other.max_ulp)
         self.max_abs = max(self.max_abs, other.max_abs)
@@ -186,7 +193,10 @@ def compare_slice(rep, Kin, Vin, Nin, s, n1, n2, c, r, storage, gpu_best, gpu_se
 
 def check_report(rep, near_bar=1e-3, floor_allowed=False):
     """No hard mismatch, near-ties below near_bar of the A edges, and (unless the inputs are built
-    to make weighted means cancel) no merged value that needed the absolute floor."""
+    to make weighted means cancel) no 16-bit merged value that needed the absolute floor.  fp32
+    storage is held to one bf16 step of the oracle's value; where a mean of terms of order one
+    cancels to ~1e-6 or below, fp32 accumulation error alone exceeds that step, so its floor uses
+    are counted and reported (about three per million merged edges on random data), not refused."""
     assert rep.match_hard == 0 and rep.sel_hard == 0, rep
     assert rep.near_fraction() < near_bar, rep
     if not floor_allowed:

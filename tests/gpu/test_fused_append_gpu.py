@@ -155,3 +155,54 @@ def test_fused_step_64k_budget_cache(lib, dev):
     print("fused vs two calls", diff, "vs oracle", worst)
     assert diff < TWO_CALLS
     assert worst < 2e-4
+
+
+def test_seeded_sweep_fused_step(lib, dev):
+    """60 seeded random geometries: storage format, head dim, heads per group (1..8), slice counts
+    on both sides of the per-head combine limit (64 slices), ragged lengths with empty, nearly
+    full and full slices, degrees 1..1000, and length bounds that some appended slices exceed.
+    Each step against the two calls (cache and error word identical, outputs within the sum-order
+    bar) and every head against the oracle over the cache the step left."""
+    rng = np.random.default_rng(123)
+    dtypes = [torch.bfloat16, torch.float16, torch.float32]
+    worst = {dt: 0.0 for dt in dtypes}
+    worst_two = 0.0
+    for case in range(60):
+        dtype = dtypes[case % 3]
+        d = 64 if (case // 3) % 2 else 128
+        G = int(rng.choice([1, 2, 4, 8]))
+        H_kv = int(rng.choice([1, 2, 4, 8]))
+        groups = int(rng.choice([1, 2, 3, 9, 12]))
+        S = groups * H_kv
+        cap = int(rng.integers(2, 1500))
+        lens = [int(rng.choice([0, 1, cap - 1, cap, int(rng.integers(0, cap + 1))]))
+                for _ in range(S)]
+        K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=900 + case, degrees=True)
+        N[N > 0] = torch.from_numpy(rng.integers(1, 1001, size=int((N > 0).sum())).astype(np.int32))
+        gen = torch.Generator().manual_seed(1000 + case)
+        H_q = G * H_kv
+        q = torch.randn((groups, H_q, d), generator=gen).to(dtype).to(dev)
+        kn = torch.randn((S, d), generator=gen).to(dtype).to(dev)
+        vn = torch.randn((S, d), generator=gen).to(dtype).to(dev)
+        top = min(max(lens) + 1, cap)
+        max_len = top if rng.random() < 0.7 else max(1, top - 1)
+        ref, fus, O_r, O_f, err_r, err_f = _both(lib, dev, K, V, N, L, q, kn, vn, H_q, H_kv,
+                                                 max_len)
+        for a, b in zip(ref, fus):
+            assert torch.equal(a, b), case
+        full = any(x == cap for x in lens)
+        over = any(min(x + 1, cap) > max_len for x in lens)
+        assert err_f == err_r == (lib.EDEVICE if full or over else lib.OK), case
+        worst_two = max(worst_two, float((O_f - O_r).abs().max()))
+        Lf = fus[3].cpu()
+        ref_o = _oracle_all(q.cpu(), *(t.cpu() for t in fus), H_q, H_kv)
+        for z in range(S):  # slices past the length bound give zeros
+            if int(Lf[z]) > max_len:
+                g, kvh = divmod(z, H_kv)
+                ref_o[g, kvh * G:(kvh + 1) * G] = 0.0
+        err_o = float(np.abs(O_f.cpu().double().numpy() - ref_o).max())
+        worst[dtype] = max(worst[dtype], err_o)
+    print("fused vs two calls", worst_two, {str(k): v for k, v in worst.items()})
+    assert worst_two < TWO_CALLS
+    assert worst[torch.float32] < 2e-5
+    assert worst[torch.bfloat16] < 2e-4 and worst[torch.float16] < 2e-4

@@ -407,3 +407,44 @@ def test_index_and_pruned_decode_full_size_sampled(lib, dev):
             want = oatt.logn_attention_one(qs[h], K64[rows], V64[rows], N64[rows])
             assert float(np.abs(O[g, kvh * G + h].cpu().double().numpy() - want).max()) < 2e-4
         print("slice", z, "rows", s, "kept blocks", int(dev_keep.sum()), "of", ref["nleaf"])
+
+
+def test_seeded_sweep_pruned_decode(lib, dev):
+    """36 seeded random geometries: storage format, head dim, block rows 16..256, heads per group
+    (1..8), KV heads, ragged lengths (empty, one row, full, random), protected-row counts (none
+    included), key spreads and thresholds from 0.5 to +inf.  Every build and pruned call against
+    the oracle as in the tests above."""
+    rng = np.random.default_rng(2024)
+    dts = ["bf16", "f16", "f32"]
+    total_dropped = total_near = 0
+    worst = 0.0
+    for case in range(36):
+        dt = dts[case % 3]
+        d = 64 if (case // 3) % 2 else 128
+        B = int(rng.choice([16, 32, 64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        H_kv = int(rng.choice([1, 2, 4]))
+        groups = int(rng.choice([1, 2]))
+        S = groups * H_kv
+        cap = int(rng.integers(1, 3000))
+        lens = [int(rng.choice([0, 1, cap, int(rng.integers(0, cap + 1))])) for _ in range(S)]
+        n1, n2 = int(rng.choice([0, 1, 16])), int(rng.choice([0, 7, 64]))
+        spread = float(rng.choice([0.05, 0.3, 1.0]))
+        tau = float(rng.choice([0.5, 2.0, 6.0, np.inf]))
+        K, V, N, L, q = _setup(dev, dt, d, B, spread, seed=3000 + case, lens=lens, cap=cap,
+                               H_q=G * H_kv, H_kv=H_kv)
+        index = lib.new_index(K, B)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        lib.index_build(K, N, L, index, err, B)
+        assert lib.read_error(err) == lib.OK, case
+        dropped, near, differ, wf, wfull, ok = _compare_pruned(lib, K, V, N, L, q, index, tau, B,
+                                                               n1, n2, G * H_kv, H_kv)
+        assert wf < 2e-4 and ok, (case, dt, d, B, G, H_kv, lens, n1, n2, tau, wf)
+        if tau == float("inf"):
+            assert dropped == 0 and wfull < 2e-4, case
+        total_dropped += dropped
+        total_near += near
+        worst = max(worst, wf)
+    print("dropped rows", total_dropped, "near-threshold differences", total_near,
+          "worst vs oracle (device's rows)", worst)
+    assert total_dropped > 0

@@ -94,7 +94,8 @@ __global__ void csm_prep(CsmArgs a) {
   }
 }
 
-template <typename T, int NT, int D>
+// ROWS: rows per block of the copies (see copy_rows).
+template <typename T, int NT, int D, int ROWS = kMaxChunk>
 __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch, bool outl) {
   using TL = Tile<T, NT, D>;
   const int t = threadIdx.x;
@@ -105,7 +106,7 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   int32_t *Nd = a.Nout + z * a.cap_out;
   int32_t *src = a.tap_src ? a.tap_src + z * a.cap_out : nullptr;
   if (nch == 0) {  // nothing to compress: lens unchanged, copy everything out of place
-    if (!a.in_place) copy_rows<T, NT, D>(Ks, Vs, Ns, Kd, Vd, Nd, s);
+    if (!a.in_place) copy_rows<T, NT, D, ROWS>(Ks, Vs, Ns, Kd, Vd, Nd, s);
     if (src)
       for (int i = t; i < s; i += blockDim.x) src[i] = i;
     if (t == 0) a.lens_out[z] = s;
@@ -113,7 +114,7 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   }
   const int n1 = a.n1, n2 = a.n2, c = a.c;
   __shared__ int s_stuck;
-  if (!a.in_place) copy_rows<T, NT, D>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
+  if (!a.in_place) copy_rows<T, NT, D, ROWS>(Ks, Vs, Ns, Kd, Vd, Nd, n1);
   if (t == 0) s_stuck = 0;
   if (a.in_place && !outl && t == 0) {
     // the recent rows land in [s_new - n2, s_new): wait for chunks whose sources overlap it
@@ -131,7 +132,7 @@ __device__ void tail_unit(const CsmArgs &a, int64_t z, int s, int s_new, int nch
   __syncthreads();
   if (s_stuck) return;
   const int64_t so = (int64_t)(s - n2), dof = (int64_t)(s_new - n2);
-  copy_rows<T, NT, D>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
+  copy_rows<T, NT, D, ROWS>(Ks + so * TL::ROWB, Vs + so * TL::ROWB, Ns + so, Kd + dof * TL::ROWB,
                Vd + dof * TL::ROWB, Nd + dof, n2);
   if (src) {
     for (int i = t; i < n1; i += blockDim.x) src[i] = i;
@@ -517,6 +518,449 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   }
 }
 
+// MFMA step for 16-bit keys: acc += B rows (32 x 16, from LDS) . A rows^T (16 x 32, registers).
+__device__ __forceinline__ f32x16 mfma16(u32x4 b, u32x4 a, f32x16 acc, __bf16 *) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b),
+                                                 __builtin_bit_cast(bf16x8, a), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma16(u32x4 b, u32x4 a, f32x16 acc, _Float16 *) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, b),
+                                                __builtin_bit_cast(f16x8, a), acc, 0, 0, 0);
+}
+
+// One unit of the round for chunks of up to 512 rows when at most a quarter of the rows merge
+// (r <= 1/2), on 256 threads with the LDS of two (d = 128) or three (d = 64) workgroups per CU.
+// The steps and every decision and rounding are those of csm_round_body; what differs is where
+// the rows live.  The A keys go from memory straight into MFMA operand registers (wave w holds
+// A groups 2w and 2w + 1, lane (col, h) segments 2k + h of its A row, as the LDS tile feeds them
+// in csm_round_body), only the B keys are staged in LDS, and the values stay in registers.  At
+// output, unmerged A keys and values are stored from registers; the rows that take part in a
+// merge go through the B-key tile: a target keeps its B slot, and since at most a quarter of a
+// chunk's rows are sources there are at least as many B rows that are not targets as there are
+// sources, so the j-th source (ascending A) takes the j-th such slot once that row has been
+// written out.
+template <typename T, int D>
+__device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
+  constexpr int NT = 256, CMAX = kMaxChunkWide, NA = CMAX / 2, NW = NT / 64;
+  constexpr int ROWB = D * (int)sizeof(T), SEGS = ROWB / 16, KS = D / 16, SWM = SEGS - 1;
+  constexpr int RPI = NT / SEGS;    // rows per block-wide load (16 lanes a row at d = 128)
+  constexpr int NLB = NA / RPI;     // loads per thread for the B rows
+  constexpr int NLV = CMAX / RPI;   // loads per thread for every row
+  constexpr int EPS = 16 / (int)sizeof(T);
+  static_assert(sizeof(T) == 2 && (D == 64 || D == 128) && NA == NT, "16-bit, d = 64 or 128");
+  struct SimPart {
+    uint64_t key[NA];  // rank keys, 0 = no edge
+    float invB[NA];    // 1 / max(|k_b|, eps)
+  };
+  struct OutPart {
+    int32_t list[NA];  // sources of every target, by target, ascending A
+    int32_t tgt[NA];   // merge targets (B indices)
+    int32_t src[NA];   // tile row holding each source A row
+    int32_t fre[NA];   // B rows that are not targets, ascending
+  };
+  struct __attribute__((aligned(16))) Smem {
+    char tile[NA * ROWB];
+    union {
+      SimPart s;
+      OutPart o;
+    } u1;
+    union {
+      int32_t cntw[NW][NA];  // per-wave same-target counts
+      int32_t slot[CMAX];    // output row of every kept row
+    } u2;
+    int32_t n[CMAX];
+    int32_t best[NA], sel[NA], cnt[NA], wsum[NA], off[NA];
+    int32_t misc[1 + 5 * NW];
+  };
+  __shared__ Smem sm;
+  auto swzb = [](int b, int seg) { return b * ROWB + ((seg ^ (b & SWM)) << 4); };
+
+  const int t = threadIdx.x;
+  const int64_t z = blockIdx.x / (uint32_t)a.units;
+  const double r = a.s_r[z];
+  if (r < 0.0) return;
+  const int s = a.s_in[z];
+  if (s < 0) return;
+  const bool outl = a.mask != nullptr && a.mask[z] != 0;
+  if (outl && a.in_place) return;
+  if (t == 0) sm.misc[0] = (int32_t)atomicAdd(a.ticket + z, 1u);
+  __syncthreads();
+  const int u = sm.misc[0];
+  const int n1 = a.n1, n2 = a.n2, c = a.c;
+  const int m_full = merge_count_dev(r, c);
+  const int M = s - n1 - n2;
+  const int nch = M >= 2 ? (M + c - 1) / c : 0;
+  const int s_new = a.s_out[z];
+  if (u == a.units - 1) {
+    tail_unit<T, NT, D, 128>(a, z, s, s_new, nch, outl);  // 128-row blocks: fewer live registers
+    return;
+  }
+  if (u >= nch) return;
+
+  const int j = u;
+  const int start = n1 + j * c;
+  const int L = min(c, M - j * c);
+  const bool copy_only = outl;
+  const int m = copy_only ? 0 : merge_count_dev(r, L);
+  const int nA = (L + 1) / 2, nB = L / 2;
+  const int base = copy_only ? start : n1 + j * (c - m_full);
+  const int nout = L - m;
+  T *tsel = nullptr;
+  const char *Ksrc = a.Kin + (z * a.cap_in + start) * (int64_t)ROWB;
+  const char *Vsrc = a.Vin + (z * a.cap_in + start) * (int64_t)ROWB;
+  const int w = t >> 6, l = t & 63, col = l & 31, h = l >> 5;
+  const int sg = t % SEGS, rb = t / SEGS;
+
+  // 1. loads: A keys into operand registers, B keys into the tile (+ their norms), degrees,
+  //    then the values.  A keys use cached loads: each 128-byte line is read by four of a
+  //    lane's loads, issued back to back.
+  // range-checked buffers over the chunk's L rows: rows past them read as zeros
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Ksrc), 0, L * ROWB, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Vsrc), 0, L * ROWB, kBufWord3);
+  u32x4 areg[2][KS];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int voff = 2 * (32 * (2 * w + gi) + col) * ROWB + h * 16;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      areg[gi][kk] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + kk * 32, 0, 0));
+  }
+  {
+    u32x4 breg[NLB];
+    const int voff = (2 * rb + 1) * ROWB + sg * 16;
+#pragma unroll
+    for (int i = 0; i < NLB; ++i)
+      breg[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 2 * RPI * ROWB * i, 2));
+    const int32_t *Nsrc = a.Nin + z * a.cap_in + start;
+    const int32_t nv0 = t < L ? Nsrc[t] : 0, nv1 = t + NT < L ? Nsrc[t + NT] : 0;
+    // RPI is a multiple of SEGS, so B rows rb + RPI i share rb's swizzle: one base address
+    char *trow = sm.tile + swzb(rb, sg);
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+      *reinterpret_cast<u32x4 *>(trow + i * RPI * ROWB) = breg[i];
+      const float ss = lanes_sum<SEGS>(seg_sumsq(breg[i], tsel));
+      if (sg == 0) sm.u1.s.invB[rb + RPI * i] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    }
+    sm.n[t] = nv0;
+    sm.n[t + NT] = nv1;
+  }
+  // A norms, summed in the order of the 16-lane tree of the B norms: segment pairs (2k, 2k+1)
+  // first (one from each half-wave), then pairs of pairs
+  float ia[2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    float p[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const float x = seg_sumsq(areg[gi][kk], tsel);
+      p[kk] = x + __shfl_xor(x, 32);
+    }
+    float ss;
+    if constexpr (KS == 8)
+      ss = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    else
+      ss = (p[0] + p[1]) + (p[2] + p[3]);
+    ia[gi] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+  }
+  __syncthreads();
+
+  // 2. similarity and arg-max over B (ascending B, strict >, lowest index on ties); both A
+  //    groups of the wave against one B tile at a time (one operand read, two MFMA chains)
+  if (!copy_only && nB > 0) {
+    float best[2] = {-__builtin_inff(), -__builtin_inff()};
+    int bidx[2] = {0, 0};
+#pragma unroll 1
+    for (int bt = 0; bt < NA / 32; ++bt) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[0][q] = acc[1][q] = 0.f;
+      const char *brow = sm.tile + bt * 32 * ROWB;  // rows bt 32 + col share col's swizzle
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const u32x4 braw = *reinterpret_cast<const u32x4 *>(brow + swzb(col, 2 * kk + h));
+        acc[0] = mfma16(braw, areg[0][kk], acc[0], tsel);
+        acc[1] = mfma16(braw, areg[1][kk], acc[1], tsel);
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int b0 = bt * 32 + 8 * g4 + 4 * h;
+        const float4 ib = *reinterpret_cast<const float4 *>(&sm.u1.s.invB[b0]);
+        const float ibv[4] = {ib.x, ib.y, ib.z, ib.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            float sc = (acc[gi][4 * g4 + i] * ibv[i]) * ia[gi];
+            sc = (b0 + i < nB) ? sc : -__builtin_inff();
+            const bool up = sc > best[gi];
+            best[gi] = up ? sc : best[gi];
+            bidx[gi] = up ? b0 + i : bidx[gi];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int aidx = 32 * (2 * w + gi) + col;
+      const float ob = __shfl_xor(best[gi], 32);
+      const int oi = __shfl_xor(bidx[gi], 32);
+      if (ob > best[gi] || (ob == best[gi] && oi < bidx[gi])) {
+        best[gi] = ob;
+        bidx[gi] = oi;
+      }
+      if (h == 0) {
+        sm.best[aidx] = aidx < nA ? bidx[gi] : -1;
+        sm.u1.s.key[aidx] = aidx < nA ? rank_key(best[gi], aidx) : 0ull;
+      }
+    }
+  } else {
+    sm.best[t] = -1;
+    sm.u1.s.key[t] = 0ull;
+  }
+  // the values, in flight through the rank and list steps
+  u32x4 vreg[NLV];
+  {
+    const int voff = rb * ROWB + sg * 16;
+#pragma unroll
+    for (int i = 0; i < NLV; ++i)
+      vreg[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, RPI * ROWB * i, 2));
+  }
+  __syncthreads();
+
+  // 3. top-m selection: rank of each A edge = number of larger unique keys
+  {
+    const uint64_t my = sm.u1.s.key[t];
+    int rank = 0;
+#pragma unroll 8
+    for (int q = 0; q < NA; q += 2) {
+      const uint64_t k0 = sm.u1.s.key[q], k1 = sm.u1.s.key[q + 1];
+      rank += (k0 > my) + (k1 > my);
+    }
+    sm.sel[t] = (t < nA && m > 0 && nB > 0) ? (rank < m) : 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) sm.u2.cntw[ww][t] = 0;
+    sm.wsum[t] = t < nB ? sm.n[2 * t + 1] : 0;
+  }
+  __syncthreads();
+
+  // 4. source lists (ballots over the 8 target-index bits), kept rows, targets, free B rows
+  const bool sa = sm.sel[t] != 0;
+  int my_pos = 0, my_b = -1;
+  {
+    const int b = sa ? sm.best[t] : 0;
+    uint64_t eq = __ballot(sa);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t mb = __ballot(sa && ((b >> bit) & 1));
+      eq &= ((b >> bit) & 1) ? mb : ~mb;
+    }
+    if (sa) {
+      my_b = b;
+      my_pos = lanes_below(eq);
+      if (my_pos == 0) sm.u2.cntw[w][b] = __popcll(eq);
+      atomicAdd(&sm.wsum[b], sm.n[2 * t]);
+    }
+  }
+  const bool keep0 = t < L && ((t & 1) || !sm.sel[t >> 1]);
+  const bool keep1 = t + NT < L && (((t + NT) & 1) || !sm.sel[(t + NT) >> 1]);
+  const uint64_t bal0 = __ballot(keep0), bal1 = __ballot(keep1);
+  if (l == 0) {
+    sm.misc[1 + w] = __popcll(bal0);
+    sm.misc[1 + NW + w] = __popcll(bal1);
+  }
+  __syncthreads();
+  if (t < 64) {  // per-target counts and their exclusive scan (NA / 64 targets per lane)
+    constexpr int TPL = NA / 64;
+    int cn[TPL], tot = 0;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      int cc = 0;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) cc += sm.u2.cntw[ww][TPL * t + k];
+      cn[k] = cc;
+      tot += cc;
+    }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (t >= o) incl += y;
+    }
+    int ex = incl - tot;
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      sm.off[TPL * t + k] = ex;
+      sm.cnt[TPL * t + k] = cn[k];
+      ex += cn[k];
+    }
+  }
+  __syncthreads();
+  if (my_b >= 0) {
+    int before = 0;  // same-target sources of the lower waves come first
+    for (int ww = 0; ww < w; ++ww) before += sm.u2.cntw[ww][my_b];
+    sm.u1.o.list[sm.off[my_b] + before + my_pos] = t;
+  }
+  const bool is_tgt = t < nB && sm.cnt[t] > 0;
+  const bool is_free = t < nB && sm.cnt[t] == 0;
+  const uint64_t btg = __ballot(is_tgt), bfr = __ballot(is_free), bsr = __ballot(sa);
+  if (l == 0) {
+    sm.misc[1 + 2 * NW + w] = __popcll(btg);
+    sm.misc[1 + 3 * NW + w] = __popcll(bfr);
+    sm.misc[1 + 4 * NW + w] = __popcll(bsr);
+  }
+  if (a.in_place) {
+    // every load of this chunk has landed before its "source consumed" flag rises; only then
+    // does it wait for the lower chunks whose sources its destination rows
+    // [base, base + nout) overlap (chunks lo..j)
+    wait_vm_loads();
+    __syncthreads();
+    if (t == 0) {
+      __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
+      bool ok = true;
+      for (int i = lo; i <= hi && ok; ++i) ok = wait_flag(a.flags + z * a.units + i);
+      if (!ok) {  // a wait that did not end: report it and leave the chunk's rows unwritten
+        atomicExch(a.err, kDeviceError);
+        sm.misc[0] = -1;
+      }
+    }
+  }
+  __syncthreads();
+  if (sm.misc[0] == -1) return;
+  int slot0 = 0, slot1 = 0, srank = 0, ntgt = 0;
+  {
+    int o0 = 0, o1 = 0, ot = 0, of = 0, tot0 = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const bool lower = ww < w;
+      tot0 += sm.misc[1 + ww];
+      ntgt += sm.misc[1 + 2 * NW + ww];
+      o0 += lower ? sm.misc[1 + ww] : 0;
+      o1 += lower ? sm.misc[1 + NW + ww] : 0;
+      ot += lower ? sm.misc[1 + 2 * NW + ww] : 0;
+      of += lower ? sm.misc[1 + 3 * NW + ww] : 0;
+      srank += lower ? sm.misc[1 + 4 * NW + ww] : 0;
+    }
+    slot0 = o0 + lanes_below(bal0);
+    slot1 = tot0 + o1 + lanes_below(bal1);
+    srank += lanes_below(bsr);
+    if (keep0) sm.u2.slot[t] = slot0;
+    if (keep1) sm.u2.slot[t + NT] = slot1;
+    if (is_tgt) sm.u1.o.tgt[ot + lanes_below(btg)] = t;
+    if (is_free) sm.u1.o.fre[of + lanes_below(bfr)] = t;
+  }
+  __syncthreads();
+  if (sa) sm.u1.o.src[t] = sm.u1.o.fre[srank];
+  if (a.tap_best != nullptr) {
+    const int64_t o = (z * a.units + j) * NA + t;
+    a.tap_best[o] = (t < nA && !copy_only) ? sm.best[t] : -1;
+    a.tap_sel[o] = (uint8_t)sm.sel[t];
+  }
+  if (a.tap_src != nullptr) {
+    int32_t *ts = a.tap_src + z * a.cap_out + base;
+    if (keep0) ts[slot0] = start + t;
+    if (keep1) ts[slot1] = start + t + NT;
+  }
+  __syncthreads();
+
+  // 5. keys: B rows that are not targets from the tile, unmerged A rows from the registers;
+  //    then the sources into the freed B rows and the merged rows
+  //    (N_b k_b + sum N_a k_a) * (1 / W) in fp32, sources in ascending A order
+  // output rows [0, nout) of the chunk's destination, as range-checked buffers
+  const __amdgpu_buffer_rsrc_t rko = __builtin_amdgcn_make_buffer_rsrc(
+      wave_uniform(a.Kout + (z * a.cap_out + base) * (int64_t)ROWB), 0, nout * ROWB, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rvo = __builtin_amdgcn_make_buffer_rsrc(
+      wave_uniform(a.Vout + (z * a.cap_out + base) * (int64_t)ROWB), 0, nout * ROWB, kBufWord3);
+  auto store_row_seg = [](const __amdgpu_buffer_rsrc_t &rs, u32x4 v, int off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 2);  // non-temporal
+  };
+  auto merge_rows = [&](const __amdgpu_buffer_rsrc_t &dst) {
+    for (int idx = rb; idx < ntgt; idx += RPI) {
+      const int b = sm.u1.o.tgt[idx];
+      float accv[EPS], tmp[EPS];
+      seg_unpack(*reinterpret_cast<const u32x4 *>(sm.tile + swzb(b, sg)), tmp, tsel);
+      const float nb = (float)sm.n[2 * b + 1];
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) accv[e] = nb * tmp[e];
+      const int q0 = sm.off[b], q1 = q0 + sm.cnt[b];
+      for (int q = q0; q < q1; ++q) {
+        const int aa = sm.u1.o.list[q];
+        const float wa = (float)sm.n[2 * aa];
+        seg_unpack(*reinterpret_cast<const u32x4 *>(sm.tile + swzb(sm.u1.o.src[aa], sg)), tmp,
+                   tsel);
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) accv[e] = fmaf(wa, tmp[e], accv[e]);
+      }
+      const float inv = __builtin_amdgcn_rcpf((float)sm.wsum[b]);  // v_rcp_f32, 1 ulp
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) accv[e] *= inv;
+      store_row_seg(dst, seg_pack(accv, tsel), sm.u2.slot[2 * b + 1] * ROWB + sg * 16);
+    }
+  };
+  {
+    const char *trow = sm.tile + swzb(rb, sg);
+#pragma unroll
+    for (int i = 0; i < NLB; ++i) {
+      const int b = rb + RPI * i;
+      if (b < nB && sm.cnt[b] == 0)
+        store_row_seg(rko, *reinterpret_cast<const u32x4 *>(trow + i * RPI * ROWB),
+                      sm.u2.slot[2 * b + 1] * ROWB + sg * 16);
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int aidx = 32 * (2 * w + gi) + col;
+    if (aidx < nA && !sm.sel[aidx]) {
+      const int off = sm.u2.slot[2 * aidx] * ROWB + h * 16;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) store_row_seg(rko, areg[gi][kk], off + kk * 32);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int aidx = 32 * (2 * w + gi) + col;
+    if (aidx < nA && sm.sel[aidx]) {
+      const int fs = sm.u1.o.src[aidx];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        *reinterpret_cast<u32x4 *>(sm.tile + swzb(fs, 2 * kk + h)) = areg[gi][kk];
+    }
+  }
+  __syncthreads();
+  merge_rows(rko);
+  __syncthreads();
+
+  // 6. values: rows that take part in a merge into the tile as the keys were, the others
+  //    straight from the registers; then the merged rows; then N
+#pragma unroll
+  for (int i = 0; i < NLV; ++i) {
+    const int rr = rb + RPI * i;
+    if (rr < L) {
+      const int hb = rr >> 1;
+      int trow = -1;
+      if (rr & 1) trow = sm.cnt[hb] > 0 ? hb : -1;
+      else trow = sm.sel[hb] ? sm.u1.o.src[hb] : -1;
+      if (trow >= 0)
+        *reinterpret_cast<u32x4 *>(sm.tile + swzb(trow, sg)) = vreg[i];
+      else
+        store_row_seg(rvo, vreg[i], sm.u2.slot[rr] * ROWB + sg * 16);
+    }
+  }
+  __syncthreads();
+  merge_rows(rvo);
+  int32_t *Nd = a.Nout + z * a.cap_out + base;
+  if (keep0) Nd[slot0] = ((t & 1) && sm.cnt[t >> 1] > 0) ? sm.wsum[t >> 1] : sm.n[t];
+  if (keep1) Nd[slot1] = (((t + NT) & 1) && sm.cnt[(t + NT) >> 1] > 0) ? sm.wsum[(t + NT) >> 1]
+                                                                        : sm.n[t + NT];
+}
+
 // Head dim 128.  bf16 / fp16: 512 threads and 78 KB of LDS per workgroup, two workgroups
 // (four waves per SIMD) per CU.  fp32: the 128 KB key tile allows one workgroup per CU.
 constexpr int kWideThreads = 512;
@@ -557,6 +1001,25 @@ __global__ void __launch_bounds__(kBigThreads, 1) csm_round_bf16_d64_c512(CsmArg
 __global__ void __launch_bounds__(kBigThreads, 1) csm_round_f16_d64_c512(CsmArgs a) {
   csm_round_body<_Float16, kBigThreads, 64, kMaxChunkWide>(a);
 }
+// Chunks up to 512 rows at r <= 1/2, A keys and values in registers: 256 threads; d = 128 takes
+// 79 KB of LDS and at most 256 registers a lane (two workgroups per CU), d = 64 three per CU.
+constexpr int kRegsThreads = 256;
+__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(2)))
+csm_round_bf16_c512_regs(CsmArgs a) {
+  csm_round_wide_body<__bf16, 128>(a);
+}
+__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(2)))
+csm_round_f16_c512_regs(CsmArgs a) {
+  csm_round_wide_body<_Float16, 128>(a);
+}
+__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(3)))
+csm_round_bf16_d64_c512_regs(CsmArgs a) {
+  csm_round_wide_body<__bf16, 64>(a);
+}
+__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(3)))
+csm_round_f16_d64_c512_regs(CsmArgs a) {
+  csm_round_wide_body<_Float16, 64>(a);
+}
 
 // Host-side launcher used by the C ABI (d is 64 or 128; c <= 512, and c <= 256 for fp32).
 // Returns 0 or a hipError_t value.
@@ -571,7 +1034,16 @@ int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
   const bool f32 = dtype == kDtypeF32, f16 = dtype == kDtypeF16;
   if (args.c > kMaxChunk) {
     if (f32) return (int)hipErrorInvalidValue;  // rejected by the C ABI before this point
-    if (d == 64) {
+    if (args.r <= 0.5) {  // args.r bounds every slice's r, annealed r included
+      const dim3 regs(kRegsThreads);
+      if (d == 64) {
+        if (f16) hipLaunchKernelGGL(csm_round_f16_d64_c512_regs, grid, regs, 0, stream, args);
+        else hipLaunchKernelGGL(csm_round_bf16_d64_c512_regs, grid, regs, 0, stream, args);
+      } else {
+        if (f16) hipLaunchKernelGGL(csm_round_f16_c512_regs, grid, regs, 0, stream, args);
+        else hipLaunchKernelGGL(csm_round_bf16_c512_regs, grid, regs, 0, stream, args);
+      }
+    } else if (d == 64) {
       if (f16) hipLaunchKernelGGL(csm_round_f16_d64_c512, grid, big, 0, stream, args);
       else hipLaunchKernelGGL(csm_round_bf16_d64_c512, grid, big, 0, stream, args);
     } else {

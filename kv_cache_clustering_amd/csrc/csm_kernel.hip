@@ -547,6 +547,13 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
   constexpr int NLB = NA / RPI;     // loads per thread for the B rows
   constexpr int NLV = CMAX / RPI;   // loads per thread for every row
   constexpr int EPS = 16 / (int)sizeof(T);
+  // Value loads issued before the similarity (the rest right after it): all of them at d = 64;
+  // at d = 128 all of them would not fit beside the A keys and the MFMA accumulators.
+  constexpr int VE = D == 64 ? NLV : NLV / 2;
+  // Where the "source consumed" flag rises, once every load of the chunk has landed: after the
+  // similarity (0), after the rank (1, when values were still loading during the similarity) or
+  // just before the chunk waits for lower flags (2).
+  constexpr int FLAG_AT = VE == NLV ? 0 : 1;
   static_assert(sizeof(T) == 2 && (D == 64 || D == 128) && NA == NT, "16-bit, d = 64 or 128");
   struct SimPart {
     uint64_t key[NA];  // rank keys, 0 = no edge
@@ -666,6 +673,12 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
       ss = (p[0] + p[1]) + (p[2] + p[3]);
     ia[gi] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
   }
+  u32x4 vreg[NLV];
+  const int voffv = rb * ROWB + sg * 16;
+#pragma unroll
+  for (int i = 0; i < VE; ++i)
+    vreg[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voffv, RPI * ROWB * i, 2));
   __syncthreads();
 
   // 2. similarity and arg-max over B (ascending B, strict >, lowest index on ties); both A
@@ -721,16 +734,16 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
     sm.best[t] = -1;
     sm.u1.s.key[t] = 0ull;
   }
-  // the values, in flight through the rank and list steps
-  u32x4 vreg[NLV];
-  {
-    const int voff = rb * ROWB + sg * 16;
+  // the remaining values, in flight through the rank and list steps
 #pragma unroll
-    for (int i = 0; i < NLV; ++i)
-      vreg[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, RPI * ROWB * i, 2));
-  }
+  for (int i = VE; i < NLV; ++i)
+    vreg[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voffv, RPI * ROWB * i, 2));
+  // in place: every load of this chunk has landed before its "source consumed" flag rises
+  if (FLAG_AT == 0 && a.in_place) wait_vm_loads();
   __syncthreads();
+  if (FLAG_AT == 0 && a.in_place && t == 0)
+    __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 3. top-m selection: rank of each A edge = number of larger unique keys
   {
@@ -746,7 +759,10 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
     for (int ww = 0; ww < NW; ++ww) sm.u2.cntw[ww][t] = 0;
     sm.wsum[t] = t < nB ? sm.n[2 * t + 1] : 0;
   }
+  if (FLAG_AT == 1 && a.in_place) wait_vm_loads();
   __syncthreads();
+  if (FLAG_AT == 1 && a.in_place && t == 0)
+    __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 4. source lists (ballots over the 8 target-index bits), kept rows, targets, free B rows
   const bool sa = sm.sel[t] != 0;
@@ -814,14 +830,16 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
     sm.misc[1 + 4 * NW + w] = __popcll(bsr);
   }
   if (a.in_place) {
-    // every load of this chunk has landed before its "source consumed" flag rises; only then
-    // does it wait for the lower chunks whose sources its destination rows
-    // [base, base + nout) overlap (chunks lo..j)
-    wait_vm_loads();
-    __syncthreads();
+    // the flag rises (if it has not yet) before the chunk waits for the lower chunks whose
+    // sources its destination rows [base, base + nout) overlap (chunks lo..j)
+    if (FLAG_AT == 2) {
+      wait_vm_loads();
+      __syncthreads();
+    }
     if (t == 0) {
-      __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      if (FLAG_AT == 2)
+        __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
       bool ok = true;
       for (int i = lo; i <= hi && ok; ++i) ok = wait_flag(a.flags + z * a.units + i);

@@ -528,9 +528,9 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 b, u32x4 a, f32x16 acc, _Float16 
                                                 __builtin_bit_cast(f16x8, a), acc, 0, 0, 0);
 }
 
-// One unit of the round for chunks of up to 512 rows when at most a quarter of the rows merge
-// (r <= 1/2), on 256 threads with the LDS of two (d = 128) or three (d = 64) workgroups per CU.
-// The steps and every decision and rounding are those of csm_round_body; what differs is where
+// One unit of the round for chunks of up to CMAX rows when at most a quarter of the rows merge
+// (r <= 1/2), one thread per A row (256 threads for chunks of up to 512 rows, with the LDS of two
+// workgroups per CU at d = 128 and three at d = 64).  The steps and every decision and rounding are those of csm_round_body; what differs is where
 // the rows live.  The A keys go from memory straight into MFMA operand registers (wave w holds
 // A groups 2w and 2w + 1, lane (col, h) segments 2k + h of its A row, as the LDS tile feeds them
 // in csm_round_body), only the B keys are staged in LDS, and the values stay in registers.  At
@@ -539,9 +539,9 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 b, u32x4 a, f32x16 acc, _Float16 
 // chunk's rows are sources there are at least as many B rows that are not targets as there are
 // sources, so the j-th source (ascending A) takes the j-th such slot once that row has been
 // written out.
-template <typename T, int D>
-__device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
-  constexpr int NT = 256, CMAX = kMaxChunkWide, NA = CMAX / 2, NW = NT / 64;
+template <typename T, int D, int CMAX>
+__device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
+  constexpr int NA = CMAX / 2, NT = NA, NW = NT / 64;
   constexpr int ROWB = D * (int)sizeof(T), SEGS = ROWB / 16, KS = D / 16, SWM = SEGS - 1;
   constexpr int RPI = NT / SEGS;    // rows per block-wide load (16 lanes a row at d = 128)
   constexpr int NLB = NA / RPI;     // loads per thread for the B rows
@@ -554,7 +554,9 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
   // similarity (0), after the rank (1, when values were still loading during the similarity) or
   // just before the chunk waits for lower flags (2).
   constexpr int FLAG_AT = VE == NLV ? 0 : 1;
-  static_assert(sizeof(T) == 2 && (D == 64 || D == 128) && NA == NT, "16-bit, d = 64 or 128");
+  static_assert(sizeof(T) == 2 && (D == 64 || D == 128), "16-bit storage, d = 64 or 128");
+  static_assert(CMAX == kMaxChunk || CMAX == kMaxChunkWide, "chunk capacity 256 or 512");
+  static_assert(NA % 64 == 0 && NA <= 256, "whole waves of A rows; 8-bit target indices");
   struct SimPart {
     uint64_t key[NA];  // rank keys, 0 = no edge
     float invB[NA];    // 1 / max(|k_b|, eps)
@@ -581,6 +583,14 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
   };
   __shared__ Smem sm;
   auto swzb = [](int b, int seg) { return b * ROWB + ((seg ^ (b & SWM)) << 4); };
+  // LDS offset of this thread's segment of B row rb + RPI i: the swizzle repeats every PER values
+  // of i, so PER base addresses serve them all
+  static_assert(RPI % SEGS == 0 || SEGS % RPI == 0, "swizzle period");
+  constexpr int PER = RPI >= SEGS ? 1 : SEGS / RPI;
+  const int rb0 = threadIdx.x / SEGS, sg0 = threadIdx.x % SEGS;
+  auto bslot = [=](int i) {
+    return swzb(rb0 + RPI * (i % PER), sg0) + (i - i % PER) * RPI * ROWB;
+  };
 
   const int t = threadIdx.x;
   const int64_t z = blockIdx.x / (uint32_t)a.units;
@@ -644,11 +654,9 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 2 * RPI * ROWB * i, 2));
     const int32_t *Nsrc = a.Nin + z * a.cap_in + start;
     const int32_t nv0 = t < L ? Nsrc[t] : 0, nv1 = t + NT < L ? Nsrc[t + NT] : 0;
-    // RPI is a multiple of SEGS, so B rows rb + RPI i share rb's swizzle: one base address
-    char *trow = sm.tile + swzb(rb, sg);
 #pragma unroll
     for (int i = 0; i < NLB; ++i) {
-      *reinterpret_cast<u32x4 *>(trow + i * RPI * ROWB) = breg[i];
+      *reinterpret_cast<u32x4 *>(sm.tile + bslot(i)) = breg[i];
       const float ss = lanes_sum<SEGS>(seg_sumsq(breg[i], tsel));
       if (sg == 0) sm.u1.s.invB[rb + RPI * i] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
     }
@@ -921,15 +929,12 @@ __device__ __forceinline__ void csm_round_wide_body(const CsmArgs &a) {
       store_row_seg(dst, seg_pack(accv, tsel), sm.u2.slot[2 * b + 1] * ROWB + sg * 16);
     }
   };
-  {
-    const char *trow = sm.tile + swzb(rb, sg);
 #pragma unroll
-    for (int i = 0; i < NLB; ++i) {
-      const int b = rb + RPI * i;
-      if (b < nB && sm.cnt[b] == 0)
-        store_row_seg(rko, *reinterpret_cast<const u32x4 *>(trow + i * RPI * ROWB),
-                      sm.u2.slot[2 * b + 1] * ROWB + sg * 16);
-    }
+  for (int i = 0; i < NLB; ++i) {
+    const int b = rb + RPI * i;
+    if (b < nB && sm.cnt[b] == 0)
+      store_row_seg(rko, *reinterpret_cast<const u32x4 *>(sm.tile + bslot(i)),
+                    sm.u2.slot[2 * b + 1] * ROWB + sg * 16);
   }
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
@@ -1019,25 +1024,20 @@ __global__ void __launch_bounds__(kBigThreads, 1) csm_round_bf16_d64_c512(CsmArg
 __global__ void __launch_bounds__(kBigThreads, 1) csm_round_f16_d64_c512(CsmArgs a) {
   csm_round_body<_Float16, kBigThreads, 64, kMaxChunkWide>(a);
 }
-// Chunks up to 512 rows at r <= 1/2, A keys and values in registers: 256 threads; d = 128 takes
-// 79 KB of LDS and at most 256 registers a lane (two workgroups per CU), d = 64 three per CU.
-constexpr int kRegsThreads = 256;
-__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(2)))
-csm_round_bf16_c512_regs(CsmArgs a) {
-  csm_round_wide_body<__bf16, 128>(a);
-}
-__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(2)))
-csm_round_f16_c512_regs(CsmArgs a) {
-  csm_round_wide_body<_Float16, 128>(a);
-}
-__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(3)))
-csm_round_bf16_d64_c512_regs(CsmArgs a) {
-  csm_round_wide_body<__bf16, 64>(a);
-}
-__global__ void __launch_bounds__(kRegsThreads) __attribute__((amdgpu_waves_per_eu(3)))
-csm_round_f16_d64_c512_regs(CsmArgs a) {
-  csm_round_wide_body<_Float16, 64>(a);
-}
+// Chunks up to 512 rows at r <= 1/2, 16-bit storage: A keys and values in registers, one thread
+// per A row (256).  d = 128: 79 KB of LDS and up to 256 registers a lane, two workgroups per CU;
+// d = 64: 47 KB, three per CU.  (For chunks up to 256 rows the same body on 128 threads, four
+// workgroups per CU at d = 128, is no faster than csm_round_body's two 512-thread workgroups.)
+#define CSMKV_REGS_KERNEL(NAME, T, D, CMAX, WPE)                                             \
+  __global__ void __launch_bounds__(CMAX / 2) __attribute__((amdgpu_waves_per_eu(WPE)))     \
+  NAME(CsmArgs a) {                                                                          \
+    csm_round_regs_body<T, D, CMAX>(a);                                                      \
+  }
+CSMKV_REGS_KERNEL(csm_round_bf16_c512_regs, __bf16, 128, kMaxChunkWide, 2)
+CSMKV_REGS_KERNEL(csm_round_f16_c512_regs, _Float16, 128, kMaxChunkWide, 2)
+CSMKV_REGS_KERNEL(csm_round_bf16_d64_c512_regs, __bf16, 64, kMaxChunkWide, 3)
+CSMKV_REGS_KERNEL(csm_round_f16_d64_c512_regs, _Float16, 64, kMaxChunkWide, 3)
+#undef CSMKV_REGS_KERNEL
 
 // Host-side launcher used by the C ABI (d is 64 or 128; c <= 512, and c <= 256 for fp32).
 // Returns 0 or a hipError_t value.
@@ -1053,7 +1053,7 @@ int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
   if (args.c > kMaxChunk) {
     if (f32) return (int)hipErrorInvalidValue;  // rejected by the C ABI before this point
     if (args.r <= 0.5) {  // args.r bounds every slice's r, annealed r included
-      const dim3 regs(kRegsThreads);
+      const dim3 regs(kMaxChunkWide / 2);
       if (d == 64) {
         if (f16) hipLaunchKernelGGL(csm_round_f16_d64_c512_regs, grid, regs, 0, stream, args);
         else hipLaunchKernelGGL(csm_round_bf16_d64_c512_regs, grid, regs, 0, stream, args);

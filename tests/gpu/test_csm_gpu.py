@@ -331,6 +331,46 @@ def test_wide_chunks(lib, dev, dtype, d, c, r, n1, n2):
     parity.check_report(rep)
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)])
+@pytest.mark.parametrize("c", [512, 300, 260])
+def test_wide_chunks_distinct_targets_fill_every_free_b_row(lib, dev, dtype, d, c):
+    """The tightest case of the r <= 1/2 wide-chunk kernel: rows stored as pairs (an A row and a
+    slightly perturbed copy of it just after, each pair far from the others), so every merged A
+    row has its own partner as target.  At r = 1/2 a chunk merges m = floor(L/4) rows into m
+    distinct targets, which leaves exactly nB - m >= m B rows that are not targets for the m
+    sources; lengths give full chunks (L divisible by 4 or not) and ragged last chunks."""
+    rng = np.random.default_rng(c + d)
+    lens = [4 * c, 3 * c + 7, 2 * c + 2, c + c // 2 + 1, 5, 0]
+    cap = max(lens)
+    S = len(lens)
+    K = np.zeros((S, cap, d), np.float32)
+    V = rng.standard_normal((S, cap, d)).astype(np.float32)
+    N = np.zeros((S, cap), np.int32)
+    for z, s in enumerate(lens):
+        npair = (s + 1) // 2
+        A = rng.standard_normal((npair, d))
+        eps = 0.01 + 0.3 * rng.random(npair)  # distinct perturbations: well-separated scores
+        B = A + eps[:, None] * rng.standard_normal((npair, d))
+        rows = np.empty((2 * npair, d))
+        rows[0::2], rows[1::2] = A, B
+        K[z, :s] = rows[:s]
+        N[z, :s] = rng.integers(1, 5, s)
+    K, V, N = torch.from_numpy(K).to(dtype), torch.from_numpy(V).to(dtype), torch.from_numpy(N)
+    L = torch.tensor(lens, dtype=torch.int32)
+    # the input is the tight case: in slice 0 every chunk's m sources have m distinct targets
+    # and the chunk has exactly 2m B rows
+    from oracle import csm as ocsm
+    taps = ocsm.csm_round_slice(parity.to_f64(K[0]), parity.to_f64(V[0]), N[0].numpy().astype(np.int64),
+                                lens[0], 0, 0, c, 0.5, _storage(K))[4]
+    for tp in taps["chunks"]:
+        sel = np.asarray(tp["selected"], bool)
+        assert len(set(np.asarray(tp["best_b"])[sel])) == tp["m"] and tp["S"].shape[1] == 2 * tp["m"]
+    rep = run_and_compare(lib, dev, K, V, N, L, 0, 0, c, 0.5)
+    print(rep)
+    parity.check_report(rep)
+    assert rep.edges > 0
+
+
 def test_wide_chunks_in_place_equals_out_of_place(lib, dev):
     S, cap = 6, 5000
     lens = [4999, 5000, 17, 1500, 0, 592]

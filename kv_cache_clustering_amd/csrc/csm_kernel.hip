@@ -149,6 +149,54 @@ __device__ __forceinline__ uint64_t rank_key(float score, int aidx) {
   return ((uint64_t)ord << 8) | (uint64_t)(255 - aidx);
 }
 
+// One chunk unit of a slice, as the workgroup's ticket assigns it.
+struct ChunkUnit {
+  int64_t z;       // slice
+  int j;           // chunk of the slice
+  int start, L;    // first source row, rows in the chunk
+  int m, nA, nB;   // merges, A rows, B rows
+  int base, nout;  // first output row, output rows
+  bool copy_only;  // outlier slice out of place: its rows move unchanged
+};
+
+// Starts a workgroup of the round: a slice that does not run this call (r < 0: trigger not met,
+// outlier in place, or a bad length with the error word already set) is left as it is, one load
+// deciding it; otherwise the workgroup takes a ticket from its slice's counter (slot: one int of
+// LDS), runs the slice's tail unit if the ticket names it, and returns true with cu filled in when
+// the ticket names a chunk.  ROWS: rows per block of the tail unit's copies.
+template <typename T, int NT, int D, int ROWS>
+__device__ __forceinline__ bool take_unit(const CsmArgs &a, int32_t *slot, ChunkUnit &cu) {
+  const int64_t z = blockIdx.x / (uint32_t)a.units;
+  const double r = a.s_r[z];
+  if (r < 0.0) return false;
+  const int s = a.s_in[z];
+  if (s < 0) return false;
+  const bool outl = a.mask != nullptr && a.mask[z] != 0;
+  if (outl && a.in_place) return false;
+  if (threadIdx.x == 0) *slot = (int32_t)atomicAdd(a.ticket + z, 1u);
+  __syncthreads();
+  const int u = *slot;
+  const int n1 = a.n1, n2 = a.n2, c = a.c;
+  const int M = s - n1 - n2;
+  const int nch = M >= 2 ? (M + c - 1) / c : 0;
+  if (u == a.units - 1) {
+    tail_unit<T, NT, D, ROWS>(a, z, s, a.s_out[z], nch, outl);
+    return false;
+  }
+  if (u >= nch) return false;
+  cu.z = z;
+  cu.j = u;
+  cu.start = n1 + u * c;
+  cu.L = min(c, M - u * c);
+  cu.copy_only = outl;
+  cu.m = outl ? 0 : merge_count_dev(r, cu.L);
+  cu.nA = (cu.L + 1) / 2;
+  cu.nB = cu.L / 2;
+  cu.base = outl ? cu.start : n1 + u * (c - merge_count_dev(r, c));
+  cu.nout = cu.L - cu.m;
+  return true;
+}
+
 // One unit of the round.  T: storage type; NT: threads; D: head dim; CMAX: chunk capacity
 // (256: A and B up to 128 rows; 512: up to 256).  NA = CMAX / 2 A rows; the A x B tile is
 // split over the waves as AG = NA / 32 column groups times NT / 64 / AG B parts.
@@ -182,39 +230,12 @@ __device__ __forceinline__ void csm_round_body(const CsmArgs &a) {
   __shared__ int32_t s_misc[1 + NW];
 
   const int t = threadIdx.x;
-  const int64_t z = blockIdx.x / (uint32_t)a.units;
-  // r < 0: the slice does not run this call (trigger not met, outlier in place, or a bad length
-  // with the error word already set) and is left as it is; one load decides it
-  const double r = a.s_r[z];
-  if (r < 0.0) return;
-  const int s = a.s_in[z];
-  if (s < 0) return;
-  const bool outl = a.mask != nullptr && a.mask[z] != 0;
-  if (outl && a.in_place) return;
-  if (t == 0) s_misc[0] = (int32_t)atomicAdd(a.ticket + z, 1u);
-  __syncthreads();
-  const int u = s_misc[0];
-  const int n1 = a.n1, n2 = a.n2, c = a.c;
-  const int m_full = merge_count_dev(r, c);
-  const int M = s - n1 - n2;
-  const int nch = M >= 2 ? (M + c - 1) / c : 0;
-  const int s_new = a.s_out[z];
-
-  if (u == a.units - 1) {
-    tail_unit<T, NT, D>(a, z, s, s_new, nch, outl);
-    return;
-  }
-  if (u >= nch) return;
-
-  // ---------------------------------------------------------------- chunk unit
-  const int j = u;
-  const int start = n1 + j * c;
-  const int L = min(c, M - j * c);
-  const bool copy_only = outl;  // outlier slice, out of place: rows move unchanged
-  const int m = copy_only ? 0 : merge_count_dev(r, L);
-  const int nA = (L + 1) / 2, nB = L / 2;
-  const int base = copy_only ? start : n1 + j * (c - m_full);
-  const int nout = L - m;
+  ChunkUnit cu;
+  if (!take_unit<T, NT, D, kMaxChunk>(a, &s_misc[0], cu)) return;
+  const int64_t z = cu.z;
+  const int j = cu.j, start = cu.start, L = cu.L, m = cu.m, nA = cu.nA, nB = cu.nB;
+  const int base = cu.base, nout = cu.nout, n1 = a.n1, c = a.c;
+  const bool copy_only = cu.copy_only;
   T *tsel = nullptr;
 
   const char *Ksrc = a.Kin + (z * a.cap_in + start) * (int64_t)ROWB;
@@ -593,35 +614,13 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   };
 
   const int t = threadIdx.x;
-  const int64_t z = blockIdx.x / (uint32_t)a.units;
-  const double r = a.s_r[z];
-  if (r < 0.0) return;
-  const int s = a.s_in[z];
-  if (s < 0) return;
-  const bool outl = a.mask != nullptr && a.mask[z] != 0;
-  if (outl && a.in_place) return;
-  if (t == 0) sm.misc[0] = (int32_t)atomicAdd(a.ticket + z, 1u);
-  __syncthreads();
-  const int u = sm.misc[0];
-  const int n1 = a.n1, n2 = a.n2, c = a.c;
-  const int m_full = merge_count_dev(r, c);
-  const int M = s - n1 - n2;
-  const int nch = M >= 2 ? (M + c - 1) / c : 0;
-  const int s_new = a.s_out[z];
-  if (u == a.units - 1) {
-    tail_unit<T, NT, D, 128>(a, z, s, s_new, nch, outl);  // 128-row blocks: fewer live registers
-    return;
-  }
-  if (u >= nch) return;
-
-  const int j = u;
-  const int start = n1 + j * c;
-  const int L = min(c, M - j * c);
-  const bool copy_only = outl;
-  const int m = copy_only ? 0 : merge_count_dev(r, L);
-  const int nA = (L + 1) / 2, nB = L / 2;
-  const int base = copy_only ? start : n1 + j * (c - m_full);
-  const int nout = L - m;
+  ChunkUnit cu;
+  // 128-row blocks in the tail unit's copies: fewer live registers
+  if (!take_unit<T, NT, D, 128>(a, &sm.misc[0], cu)) return;
+  const int64_t z = cu.z;
+  const int j = cu.j, start = cu.start, L = cu.L, m = cu.m, nA = cu.nA, nB = cu.nB;
+  const int base = cu.base, nout = cu.nout, n1 = a.n1, c = a.c;
+  const bool copy_only = cu.copy_only;
   T *tsel = nullptr;
   const char *Ksrc = a.Kin + (z * a.cap_in + start) * (int64_t)ROWB;
   const char *Vsrc = a.Vin + (z * a.cap_in + start) * (int64_t)ROWB;

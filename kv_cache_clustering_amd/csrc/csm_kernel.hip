@@ -560,9 +560,11 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 b, u32x4 a, f32x16 acc, _Float16 
 // chunk's rows are sources there are at least as many B rows that are not targets as there are
 // sources, so the j-th source (ascending A) takes the j-th such slot once that row has been
 // written out.
-template <typename T, int D, int CMAX>
+template <typename T, int D, int CMAX, int NT>
 __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
-  constexpr int NA = CMAX / 2, NT = NA, NW = NT / 64;
+  constexpr int NA = CMAX / 2, NW = NT / 64;
+  constexpr int GPW = NA / 32 / NW;  // A groups of 32 rows per wave
+  static_assert(NT == NA || NT == 2 * NA, "one or two threads per A row");
   constexpr int ROWB = D * (int)sizeof(T), SEGS = ROWB / 16, KS = D / 16, SWM = SEGS - 1;
   constexpr int RPI = NT / SEGS;    // rows per block-wide load (16 lanes a row at d = 128)
   constexpr int NLB = NA / RPI;     // loads per thread for the B rows
@@ -570,7 +572,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   constexpr int EPS = 16 / (int)sizeof(T);
   // Value loads issued before the similarity (the rest right after it): all of them at d = 64;
   // at d = 128 all of them would not fit beside the A keys and the MFMA accumulators.
-  constexpr int VE = D == 64 ? NLV : NLV / 2;
+  constexpr int VE = (D == 64 || GPW == 1) ? NLV : NLV / 2;
   // Where the "source consumed" flag rises, once every load of the chunk has landed: after the
   // similarity (0), after the rank (1, when values were still loading during the similarity) or
   // just before the chunk waits for lower flags (2).
@@ -635,10 +637,10 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
       __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Ksrc), 0, L * ROWB, kBufWord3);
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc(wave_uniform(Vsrc), 0, L * ROWB, kBufWord3);
-  u32x4 areg[2][KS];
+  u32x4 areg[GPW][KS];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int voff = 2 * (32 * (2 * w + gi) + col) * ROWB + h * 16;
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int voff = 2 * (32 * (GPW * w + gi) + col) * ROWB + h * 16;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
       areg[gi][kk] = __builtin_bit_cast(
@@ -660,13 +662,13 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
       if (sg == 0) sm.u1.s.invB[rb + RPI * i] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
     }
     sm.n[t] = nv0;
-    sm.n[t + NT] = nv1;
+    if (t + NT < CMAX) sm.n[t + NT] = nv1;
   }
   // A norms, summed in the order of the 16-lane tree of the B norms: segment pairs (2k, 2k+1)
   // first (one from each half-wave), then pairs of pairs
-  float ia[2];
+  float ia[GPW];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < GPW; ++gi) {
     float p[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -691,19 +693,26 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   // 2. similarity and arg-max over B (ascending B, strict >, lowest index on ties); both A
   //    groups of the wave against one B tile at a time (one operand read, two MFMA chains)
   if (!copy_only && nB > 0) {
-    float best[2] = {-__builtin_inff(), -__builtin_inff()};
-    int bidx[2] = {0, 0};
+    float best[GPW];
+    int bidx[GPW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      best[gi] = -__builtin_inff();
+      bidx[gi] = 0;
+    }
 #pragma unroll 1
     for (int bt = 0; bt < NA / 32; ++bt) {
-      f32x16 acc[2];
+      f32x16 acc[GPW];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[0][q] = acc[1][q] = 0.f;
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[gi][q] = 0.f;
       const char *brow = sm.tile + bt * 32 * ROWB;  // rows bt 32 + col share col's swizzle
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const u32x4 braw = *reinterpret_cast<const u32x4 *>(brow + swzb(col, 2 * kk + h));
-        acc[0] = mfma16(braw, areg[0][kk], acc[0], tsel);
-        acc[1] = mfma16(braw, areg[1][kk], acc[1], tsel);
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) acc[gi] = mfma16(braw, areg[gi][kk], acc[gi], tsel);
       }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -713,7 +722,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi) {
+          for (int gi = 0; gi < GPW; ++gi) {
             float sc = (acc[gi][4 * g4 + i] * ibv[i]) * ia[gi];
             sc = (b0 + i < nB) ? sc : -__builtin_inff();
             const bool up = sc > best[gi];
@@ -724,8 +733,8 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
       }
     }
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int aidx = 32 * (2 * w + gi) + col;
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int aidx = 32 * (GPW * w + gi) + col;
       const float ob = __shfl_xor(best[gi], 32);
       const int oi = __shfl_xor(bidx[gi], 32);
       if (ob > best[gi] || (ob == best[gi] && oi < bidx[gi])) {
@@ -737,7 +746,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
         sm.u1.s.key[aidx] = aidx < nA ? rank_key(best[gi], aidx) : 0ull;
       }
     }
-  } else {
+  } else if (t < NA) {
     sm.best[t] = -1;
     sm.u1.s.key[t] = 0ull;
   }
@@ -753,7 +762,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
     __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 3. top-m selection: rank of each A edge = number of larger unique keys
-  {
+  if (t < NA) {
     const uint64_t my = sm.u1.s.key[t];
     int rank = 0;
 #pragma unroll 8
@@ -772,7 +781,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
     __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 4. source lists (ballots over the 8 target-index bits), kept rows, targets, free B rows
-  const bool sa = sm.sel[t] != 0;
+  const bool sa = t < NA && sm.sel[t] != 0;
   int my_pos = 0, my_b = -1;
   {
     const int b = sa ? sm.best[t] : 0;
@@ -882,7 +891,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   }
   __syncthreads();
   if (sa) sm.u1.o.src[t] = sm.u1.o.fre[srank];
-  if (a.tap_best != nullptr) {
+  if (a.tap_best != nullptr && t < NA) {
     const int64_t o = (z * a.units + j) * NA + t;
     a.tap_best[o] = (t < nA && !copy_only) ? sm.best[t] : -1;
     a.tap_sel[o] = (uint8_t)sm.sel[t];
@@ -936,8 +945,8 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
                     sm.u2.slot[2 * b + 1] * ROWB + sg * 16);
   }
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int aidx = 32 * (2 * w + gi) + col;
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int aidx = 32 * (GPW * w + gi) + col;
     if (aidx < nA && !sm.sel[aidx]) {
       const int off = sm.u2.slot[2 * aidx] * ROWB + h * 16;
 #pragma unroll
@@ -946,8 +955,8 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int aidx = 32 * (2 * w + gi) + col;
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int aidx = 32 * (GPW * w + gi) + col;
     if (aidx < nA && sm.sel[aidx]) {
       const int fs = sm.u1.o.src[aidx];
 #pragma unroll
@@ -1027,15 +1036,18 @@ __global__ void __launch_bounds__(kBigThreads, 1) csm_round_f16_d64_c512(CsmArgs
 // per A row (256).  d = 128: 79 KB of LDS and up to 256 registers a lane, two workgroups per CU;
 // d = 64: 47 KB, three per CU.  (For chunks up to 256 rows the same body on 128 threads, four
 // workgroups per CU at d = 128, is no faster than csm_round_body's two 512-thread workgroups.)
-#define CSMKV_REGS_KERNEL(NAME, T, D, CMAX, WPE)                                             \
-  __global__ void __launch_bounds__(CMAX / 2) __attribute__((amdgpu_waves_per_eu(WPE)))     \
+constexpr int kRegsThreads = 256;
+#define CSMKV_REGS_KERNEL(NAME, T, D, CMAX, NT, WPE)                                         \
+  __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))           \
   NAME(CsmArgs a) {                                                                          \
-    csm_round_regs_body<T, D, CMAX>(a);                                                      \
+    csm_round_regs_body<T, D, CMAX, NT>(a);                                                  \
   }
-CSMKV_REGS_KERNEL(csm_round_bf16_c512_regs, __bf16, 128, kMaxChunkWide, 2)
-CSMKV_REGS_KERNEL(csm_round_f16_c512_regs, _Float16, 128, kMaxChunkWide, 2)
-CSMKV_REGS_KERNEL(csm_round_bf16_d64_c512_regs, __bf16, 64, kMaxChunkWide, 3)
-CSMKV_REGS_KERNEL(csm_round_f16_d64_c512_regs, _Float16, 64, kMaxChunkWide, 3)
+CSMKV_REGS_KERNEL(csm_round_bf16_c512_regs, __bf16, 128, kMaxChunkWide, 256, 2)
+CSMKV_REGS_KERNEL(csm_round_f16_c512_regs, _Float16, 128, kMaxChunkWide, 256, 2)
+CSMKV_REGS_KERNEL(csm_round_bf16_d64_c512_regs, __bf16, 64, kMaxChunkWide, 256, 3)
+CSMKV_REGS_KERNEL(csm_round_f16_d64_c512_regs, _Float16, 64, kMaxChunkWide, 256, 3)
+CSMKV_REGS_KERNEL(csm_round_bf16_regs, __bf16, 128, kMaxChunk, 256, 3)
+CSMKV_REGS_KERNEL(csm_round_f16_regs, _Float16, 128, kMaxChunk, 256, 3)
 #undef CSMKV_REGS_KERNEL
 
 // Host-side launcher used by the C ABI (d is 64 or 128; c <= 512, and c <= 256 for fp32).
@@ -1052,7 +1064,7 @@ int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
   if (args.c > kMaxChunk) {
     if (f32) return (int)hipErrorInvalidValue;  // rejected by the C ABI before this point
     if (args.r <= 0.5) {  // args.r bounds every slice's r, annealed r included
-      const dim3 regs(kMaxChunkWide / 2);
+      const dim3 regs(kRegsThreads);
       if (d == 64) {
         if (f16) hipLaunchKernelGGL(csm_round_f16_d64_c512_regs, grid, regs, 0, stream, args);
         else hipLaunchKernelGGL(csm_round_bf16_d64_c512_regs, grid, regs, 0, stream, args);
@@ -1067,6 +1079,10 @@ int launch_csm(const CsmArgs &args, int dtype, int d, hipStream_t stream) {
       if (f16) hipLaunchKernelGGL(csm_round_f16_c512, grid, big, 0, stream, args);
       else hipLaunchKernelGGL(csm_round_bf16_c512, grid, big, 0, stream, args);
     }
+  } else if (!f32 && d == 128 && args.r <= 0.5) {
+    const dim3 regs(kRegsThreads);
+    if (f16) hipLaunchKernelGGL(csm_round_f16_regs, grid, regs, 0, stream, args);
+    else hipLaunchKernelGGL(csm_round_bf16_regs, grid, regs, 0, stream, args);
   } else if (d == 64) {
     if (f32) hipLaunchKernelGGL(csm_round_f32_d64, grid, wide, 0, stream, args);
     else if (f16) hipLaunchKernelGGL(csm_round_f16_d64, grid, wide, 0, stream, args);

@@ -451,10 +451,10 @@ def main():
                                          "device_trigger_steps": tsteps,
                                          "device_trigger_rounds_fired": trig_rounds},
         "hbm_copy_GBps": copy_gbps,
-        "roofline": {"bound": "hbm", "kernel": "csm_round_bf16 (csm_compress, in place)",
+        "roofline": {"bound": "hbm", "kernel": "csm_round_bf16_regs (csm_compress, in place)",
                      "achieved": csm_gbps, "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": csm_gbps / PEAK_GBPS,
-                     "traffic": recorded_traffic("csm_round_bf16", CSM_SOURCES)},
+                     "traffic": recorded_traffic("csm_round_bf16_regs", CSM_SOURCES)},
         "cpu_offload": offload,
         "hierarchical_index": hier,
         "cpu_baseline": cpu,

@@ -949,8 +949,11 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
     const int aidx = 32 * (GPW * w + gi) + col;
     if (aidx < nA && !sm.sel[aidx]) {
       const int off = sm.u2.slot[2 * aidx] * ROWB + h * 16;
+      // cached stores: a lane writes 16 of every 32 bytes of its row, and its partner lane the
+      // rest; the lines stay in L2 until both halves are in, so each reaches memory once
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) store_row_seg(rko, areg[gi][kk], off + kk * 32);
+      for (int kk = 0; kk < KS; ++kk)
+        __builtin_amdgcn_raw_buffer_store_b128(areg[gi][kk], rko, off + kk * 32, 0, 0);
     }
   }
   __syncthreads();

@@ -13,7 +13,9 @@
 //                records each slice's input and output length, resets the per-slice
 //                ticket counters and clears the per-chunk "source consumed" flags.
 //   csm_round  : one workgroup per unit (512 threads for chunks of up to 256 rows, 256 for
-//                fp32 storage at d = 128, 1024 for chunks of up to 512 rows); units are (slice,
+//                fp32 storage at d = 128, 1024 for chunks of up to 512 rows; at r <= 1/2 with
+//                16-bit storage the register-resident kernels, 256 threads for chunks of up to
+//                256 rows at d = 128 and for chunks of up to 512 rows); units are (slice,
 //                chunk) pairs plus one "tail" unit per slice that moves the recent rows and
 //                writes lens.  A workgroup's slice comes from its block index (a slice that does
 //                not run exits at once, touching no counter); its unit within the slice is a
@@ -31,8 +33,9 @@
 //
 // Per chunk (A = even offsets, B = odd; up to 128 of each for c <= 256, 256 for c <= 512; head
 // dim d = 64 or 128):
-//   keys -> LDS tile (swizzled rows), reciprocal fp32 norms from the same registers; values
-//   stay in registers;
+//   keys -> LDS tile (swizzled rows; the register-resident kernels stage only the B keys and
+//   load the A keys into MFMA operand registers), reciprocal fp32 norms from the same
+//   registers; values stay in registers;
 //   S^T = B_keys . A_keys^T on MFMA (16-bit: v_mfma_f32_32x32x16_bf16 / _f16, fp32:
 //   v_mfma_f32_32x32x2_f32): the waves split the tile into 32-column A groups times B parts;
 //   cosine = (dot * fl(1/max(|b|,1e-12))) * fl(1/max(|a|,1e-12)) in fp32, branch-free arg-max
@@ -550,20 +553,22 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 b, u32x4 a, f32x16 acc, _Float16 
 }
 
 // One unit of the round for chunks of up to CMAX rows when at most a quarter of the rows merge
-// (r <= 1/2), one thread per A row (256 threads for chunks of up to 512 rows, with the LDS of two
-// workgroups per CU at d = 128 and three at d = 64).  The steps and every decision and rounding are those of csm_round_body; what differs is where
-// the rows live.  The A keys go from memory straight into MFMA operand registers (wave w holds
-// A groups 2w and 2w + 1, lane (col, h) segments 2k + h of its A row, as the LDS tile feeds them
-// in csm_round_body), only the B keys are staged in LDS, and the values stay in registers.  At
-// output, unmerged A keys and values are stored from registers; the rows that take part in a
-// merge go through the B-key tile: a target keeps its B slot, and since at most a quarter of a
-// chunk's rows are sources there are at least as many B rows that are not targets as there are
-// sources, so the j-th source (ascending A) takes the j-th such slot once that row has been
-// written out.
+// (r <= 1/2), on NT threads: one per A row (256 for chunks of up to 512 rows: two workgroups per
+// CU at d = 128, three at d = 64) or two (256 for chunks of up to 256 rows: three workgroups per
+// CU at d = 128).  The steps and every decision and rounding are those of csm_round_body; what
+// differs is where the rows live.  The A keys go from memory straight into MFMA operand
+// registers (wave w holds A groups GPW w .. GPW w + GPW - 1, lane (col, h) segments 2k + h of its
+// A row, as the LDS tile feeds them in csm_round_body), only the B keys are staged in LDS, and
+// the values stay in registers.  At output, unmerged A keys and values are stored from
+// registers; the rows that take part in a merge go through the B-key tile: a target keeps its B
+// slot, and since at most a quarter of a chunk's rows are sources there are at least as many B
+// rows that are not targets as there are sources, so the j-th source (ascending A) takes the
+// j-th such slot once that row has been written out.
 template <typename T, int D, int CMAX, int NT>
 __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   constexpr int NA = CMAX / 2, NW = NT / 64;
   constexpr int GPW = NA / 32 / NW;  // A groups of 32 rows per wave
+  constexpr int LW = NA / 64;        // waves that hold the A rows in the list step
   static_assert(NT == NA || NT == 2 * NA, "one or two threads per A row");
   constexpr int ROWB = D * (int)sizeof(T), SEGS = ROWB / 16, KS = D / 16, SWM = SEGS - 1;
   constexpr int RPI = NT / SEGS;    // rows per block-wide load (16 lanes a row at d = 128)
@@ -597,7 +602,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
       OutPart o;
     } u1;
     union {
-      int32_t cntw[NW][NA];  // per-wave same-target counts
+      int32_t cntw[LW][NA];  // same-target counts of each wave that holds A rows
       int32_t slot[CMAX];    // output row of every kept row
     } u2;
     int32_t n[CMAX];
@@ -772,7 +777,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
     }
     sm.sel[t] = (t < nA && m > 0 && nB > 0) ? (rank < m) : 0;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) sm.u2.cntw[ww][t] = 0;
+    for (int ww = 0; ww < LW; ++ww) sm.u2.cntw[ww][t] = 0;
     sm.wsum[t] = t < nB ? sm.n[2 * t + 1] : 0;
   }
   if (FLAG_AT == 1 && a.in_place) wait_vm_loads();
@@ -813,7 +818,7 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
     for (int k = 0; k < TPL; ++k) {
       int cc = 0;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) cc += sm.u2.cntw[ww][TPL * t + k];
+      for (int ww = 0; ww < LW; ++ww) cc += sm.u2.cntw[ww][TPL * t + k];
       cn[k] = cc;
       tot += cc;
     }

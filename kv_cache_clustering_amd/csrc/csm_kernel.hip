@@ -579,8 +579,8 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   // at d = 128 all of them would not fit beside the A keys and the MFMA accumulators.
   constexpr int VE = (D == 64 || GPW == 1) ? NLV : NLV / 2;
   // Where the "source consumed" flag rises, once every load of the chunk has landed: after the
-  // similarity (0), after the rank (1, when values were still loading during the similarity) or
-  // just before the chunk waits for lower flags (2).
+  // similarity (0), or after the rank (1) when values were still loading during the similarity.
+  // Either way it rises before the chunk waits for any other chunk's flag.
   constexpr int FLAG_AT = VE == NLV ? 0 : 1;
   static_assert(sizeof(T) == 2 && (D == 64 || D == 128), "16-bit storage, d = 64 or 128");
   static_assert(CMAX == kMaxChunk || CMAX == kMaxChunkWide, "chunk capacity 256 or 512");
@@ -850,24 +850,14 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
     sm.misc[1 + 3 * NW + w] = __popcll(bfr);
     sm.misc[1 + 4 * NW + w] = __popcll(bsr);
   }
-  if (a.in_place) {
-    // the flag rises (if it has not yet) before the chunk waits for the lower chunks whose
-    // sources its destination rows [base, base + nout) overlap (chunks lo..j)
-    if (FLAG_AT == 2) {
-      wait_vm_loads();
-      __syncthreads();
-    }
-    if (t == 0) {
-      if (FLAG_AT == 2)
-        __hip_atomic_store(a.flags + z * a.units + j, 1, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
-      bool ok = true;
-      for (int i = lo; i <= hi && ok; ++i) ok = wait_flag(a.flags + z * a.units + i);
-      if (!ok) {  // a wait that did not end: report it and leave the chunk's rows unwritten
-        atomicExch(a.err, kDeviceError);
-        sm.misc[0] = -1;
-      }
+  if (a.in_place && t == 0) {
+    // destination rows [base, base + nout) overlap the sources of chunks lo..j
+    const int lo = (base - n1) / c, hi = min(j - 1, (base + nout - 1 - n1) / c);
+    bool ok = true;
+    for (int i = lo; i <= hi && ok; ++i) ok = wait_flag(a.flags + z * a.units + i);
+    if (!ok) {  // a wait that did not end: report it and leave the chunk's rows unwritten
+      atomicExch(a.err, kDeviceError);
+      sm.misc[0] = -1;
     }
   }
   __syncthreads();

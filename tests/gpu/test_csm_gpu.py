@@ -477,6 +477,32 @@ def test_seeded_sweep_long_slices(lib, dev):
     parity.check_report(total)
 
 
+def test_seeded_sweep_r_up_to_half(lib, dev):
+    """1200 seeded configurations at r <= 1/2 (the rounds the register-resident kernels run, at
+    every chunk size up to 512 for bf16 and fp16 and both head dims): sinks / recent 0..69,
+    slices up to ~12 chunks with ragged lengths, AR(1) keys of correlation 0 to 0.99, random
+    outlier masks; each slice compared with the oracle."""
+    rng = np.random.default_rng(555)
+    total = parity.Report()
+    for case in range(1200):
+        dtype = [torch.bfloat16, torch.float16][case % 2]
+        d = 64 if rng.random() < 0.4 else 128
+        c = int(rng.choice([2, 3, 4, 5, 8, 31, 64, 100, 127, 128, 129, 200, 255, 256, 257, 300, 384,
+                            500, 511, 512, int(rng.integers(2, 513))]))
+        n1, n2 = int(rng.integers(0, 70)), int(rng.integers(0, 70))
+        r = float(rng.choice([0.5, 0.5, 0.25, 0.1, 0.0, 0.49, float(rng.random() * 0.5)]))
+        S = int(rng.integers(1, 6))
+        cap = int(rng.integers(n1 + n2 + 2, n1 + n2 + 12 * c + 300))
+        lens = [int(rng.choice([0, 1, n1 + n2, n1 + n2 + 1, cap, int(rng.integers(0, cap + 1))]))
+                for _ in range(S)]
+        K, V, N, L = host_cache(S, cap, lens, d=d, dtype=dtype, seed=700000 + case, degrees=True,
+                                rho=float(rng.choice([0.95, 0.5, 0.99, 0.0])))
+        mask = (rng.random(S) < 0.2).astype(np.uint8)
+        total.add(run_and_compare(lib, dev, K, V, N, L, n1, n2, c, r, mask))
+    print(total)
+    parity.check_report(total)
+
+
 def test_error_word_is_sticky_until_cleared(lib, dev):
     """A bad length flagged by one call stays visible after later clean calls on the same
     workspace (as in a loop or a graph replay of many calls) until csmkv_clear_error; the

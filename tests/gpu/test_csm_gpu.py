@@ -332,9 +332,9 @@ def test_wide_chunks(lib, dev, dtype, d, c, r, n1, n2):
 
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float16, 64)])
-@pytest.mark.parametrize("c", [512, 300, 260])
-def test_wide_chunks_distinct_targets_fill_every_free_b_row(lib, dev, dtype, d, c):
-    """The tightest case of the r <= 1/2 wide-chunk kernel: rows stored as pairs (an A row and a
+@pytest.mark.parametrize("c", [512, 300, 260, 256, 100])
+def test_distinct_targets_fill_every_free_b_row(lib, dev, dtype, d, c):
+    """The tightest case of the r <= 1/2 register-resident kernels: rows stored as pairs (an A row and a
     slightly perturbed copy of it just after, each pair far from the others), so every merged A
     row has its own partner as target.  At r = 1/2 a chunk merges m = floor(L/4) rows into m
     distinct targets, which leaves exactly nB - m >= m B rows that are not targets for the m

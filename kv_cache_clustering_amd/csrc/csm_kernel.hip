@@ -575,8 +575,9 @@ __device__ __forceinline__ void csm_round_regs_body(const CsmArgs &a) {
   constexpr int NLB = NA / RPI;     // loads per thread for the B rows
   constexpr int NLV = CMAX / RPI;   // loads per thread for every row
   constexpr int EPS = 16 / (int)sizeof(T);
-  // Value loads issued before the similarity (the rest right after it): all of them at d = 64;
-  // at d = 128 all of them would not fit beside the A keys and the MFMA accumulators.
+  // Value loads issued before the similarity (the rest right after it): all of them at d = 64 or
+  // with one A group per wave; with two groups per wave at d = 128 only half fit beside the A
+  // keys and the MFMA accumulators.
   constexpr int VE = (D == 64 || GPW == 1) ? NLV : NLV / 2;
   // Where the "source consumed" flag rises, once every load of the chunk has landed: after the
   // similarity (0), or after the rank (1) when values were still loading during the similarity.

@@ -321,7 +321,8 @@ LENS_WIDE = [4100, 1111, 81, 600, 2000, 0, 3001, 4100]
                                        (511, 0.1, 16, 64)])
 def test_wide_chunks(lib, dev, dtype, d, c, r, n1, n2):
     """Chunks of up to 512 rows: 256 x 256 similarity tile, ranks over 256 candidates, 8-bit
-    target ballots, 512-row compaction, 1024-thread workgroups."""
+    target ballots, 512-row compaction; r = 1 runs the 1024-thread kernel, the other rows the
+    register-resident one (c = 300 at r = 0.77 the 1024-thread kernel too)."""
     K, V, N, lens = host_cache(len(LENS_WIDE), 4100, LENS_WIDE, d=d, dtype=dtype,
                                seed=c + d + (dtype == torch.float16), degrees=True)
     mask = np.zeros(len(LENS_WIDE), np.uint8)
